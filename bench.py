@@ -1,0 +1,218 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused exact-attention hot path on one MI355X.
+
+One step = the whole path over one batch: the forward (fa_fwd: O and LSE)
+followed by the backward's three stages (fa_bwd_preprocess, fa_bwd_main,
+fa_bwd_dq_convert: dQ, dK, dV), at B=2, H=16, N=8192, D=128, causal, bf16,
+on seeded synthetic N(0,1) inputs already resident in device memory.
+
+FLOPs per step follow the usual attention convention: forward 4*B*H*N^2*D,
+halved for causal; backward 2.5x the forward.  Every launch is bracketed by
+HIP events on the stream it runs on, so per-kernel averages are measured live.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+METRIC = "attention fwd/bwd TFLOPS + % bf16 MFMA peak, B2 H16 N8K D128 causal"
+KERNEL_SOURCES = {
+    "fwd_kernel": ["exact_attention_98_amd/csrc/fwd_kernel.hip",
+                   "exact_attention_98_amd/csrc/common.hpp"],
+    "bwd_main_kernel": ["exact_attention_98_amd/csrc/bwd_kernels.hip",
+                        "exact_attention_98_amd/csrc/common.hpp"],
+}
+
+
+def log(msg: str):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_digest(kernel: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def load_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256") != source_digest(kernel):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, n_heads: int):
+    """The fp64 oracle, as it stands, on the first n_heads (batch 0) of the workload."""
+    import oracle
+    import synth
+    q, k, v, do = synth.generate(1, n_heads, n_heads, w.N, w.D, seed=0, with_dout=True)
+    t0 = time.perf_counter()
+    oracle.attention_fwd(q, k, v, w.causal, w.scale)
+    oracle.attention_bwd(q, k, v, do, w.causal, w.scale)
+    dt = time.perf_counter() - t0
+    flops = (w.flops_fwd() + w.flops_bwd()) * n_heads / (w.B * w.Hq)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"fp64 forward+backward of {n_heads} of the {w.B * w.Hq} (batch, head) "
+                      f"slices (N={w.N}, D={w.D}, causal), {dt:.1f} s wall"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--deterministic", action="store_true",
+                    help="fixed-order dQ accumulation in the backward")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=4)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this path runs on a single MI355X with no cross-GPU communication)",
+              file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    import torch
+    import exact_attention_98_amd as fa
+    import synth
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    fa.load()
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS["bwd_d128"]  # B2 H16 N8192 D128 causal, with dO
+    B, Hq, Hkv, N, D = w.B, w.Hq, w.Hkv, w.N, w.D
+    log(f"generating inputs B{B} H{Hq} N{N} D{D} causal (seed 0)")
+    q, k, v, do = (t.to(dev) for t in synth.generate_workload(w))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    det = 1 if args.deterministic else 0
+    ws_bytes = fa.fa_bwd_workspace_size(B, Hq, Hkv, N, D, det)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    P = dict(q=q.data_ptr(), k=k.data_ptr(), v=v.data_ptr(), o=o.data_ptr(), lse=lse.data_ptr(),
+             do=do.data_ptr(), dq=dq.data_ptr(), dk=dk.data_ptr(), dv=dv.data_ptr(),
+             ws=ws.data_ptr())
+
+    def check(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what}: {fa.fa_strerror(rc)}")
+
+    names = ["fwd_kernel", "bwd_pre_kernel", "bwd_main_kernel", "bwd_dq_convert_kernel"]
+
+    def step(ev):
+        ev[0].record(stream)
+        check(fa.fa_fwd(P["q"], P["k"], P["v"], P["o"], P["lse"], B, Hq, Hkv, N, D, 1, w.scale, sh),
+              "fa_fwd")
+        ev[1].record(stream)
+        check(fa.fa_bwd_preprocess(P["o"], P["do"], B, Hq, Hkv, N, D, P["ws"], ws_bytes, det, sh),
+              "fa_bwd_preprocess")
+        ev[2].record(stream)
+        check(fa.fa_bwd_main(P["q"], P["k"], P["v"], P["lse"], P["do"], P["dk"], P["dv"], B, Hq,
+                             Hkv, N, D, 1, w.scale, P["ws"], ws_bytes, det, sh), "fa_bwd_main")
+        ev[3].record(stream)
+        check(fa.fa_bwd_dq_convert(P["dq"], B, Hq, Hkv, N, D, w.scale, P["ws"], ws_bytes, det, sh),
+              "fa_bwd_dq_convert")
+        ev[4].record(stream)
+
+    def events():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step(events())
+    torch.cuda.synchronize()
+
+    log(f"timing {args.steps} steps")
+    evs = [events() for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    per_kernel = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps
+                  for j, n in enumerate(names)}
+    for n, t in per_kernel.items():
+        log(f"  {n}: {t * 1e3:.1f} us/launch")
+
+    f_fwd, f_bwd = w.flops_fwd(), w.flops_bwd()
+    value = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
+    fwd_tf = f_fwd / (per_kernel["fwd_kernel"] * 1e-3) / 1e12
+    bwd_ms = per_kernel["bwd_pre_kernel"] + per_kernel["bwd_main_kernel"] + \
+        per_kernel["bwd_dq_convert_kernel"]
+    bwd_tf = f_bwd / (bwd_ms * 1e-3) / 1e12
+
+    # Dominant kernel and its roofline (bf16 MFMA bound: attention is a dense contraction).
+    algo_flops = {"fwd_kernel": f_fwd, "bwd_main_kernel": f_bwd}
+    dom = max(algo_flops, key=lambda n: per_kernel[n])
+    achieved = algo_flops[dom] / (per_kernel[dom] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": load_traffic(dom),
+                "avg_launch_us": round(per_kernel[dom] * 1e3, 1)}
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 Q, K, V, dO)",
+        "config": {"workload": "attention forward+backward, B2 Hq16 Hkv16 N8192 D128 causal",
+                   "B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "D": D, "causal": True,
+                   "dq_accumulation": "deterministic" if det else "atomic",
+                   "flops_per_step": f_fwd + f_bwd},
+        "roofline": roofline,
+        "fwd": {"tflops": round(fwd_tf, 1), "frac_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
+                "us": round(per_kernel["fwd_kernel"] * 1e3, 1)},
+        "bwd": {"tflops": round(bwd_tf, 1), "frac_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
+                "us": round(bwd_ms * 1e3, 1),
+                "kernels_us": {n: round(per_kernel[n] * 1e3, 1)
+                               for n in names[1:]}},
+        "host_wall_ms_per_step": round(wall / args.steps * 1e3, 4),
+    }
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on {args.cpu_heads} heads")
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,197 @@
+"""Python binding of libfa.so, the gfx950 fused exact-attention library.
+
+The functions ``fa_fwd``, ``fa_fwd_ex``, ``fa_bwd``, ``fa_bwd_workspace_size``
+and ``fa_strerror`` call the C ABI of ``include/fa.h`` one-to-one (device
+pointers as ints, sizes as ints, a HIP stream handle as an int).  ``forward``
+and ``backward`` are thin conveniences over them for torch tensors: they check
+dtype, device, shape and contiguity, allocate outputs and the workspace with
+torch, and pass the current stream.  All arithmetic runs in the library's HIP
+kernels; there is no other implementation here and no fallback: if the
+library is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_workspace_size", "fa_bwd_preprocess",
+           "fa_bwd_main", "fa_bwd_dq_convert", "fa_strerror", "forward", "backward", "FaError",
+           "library_path", "load"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libfa.so")
+_lib = None
+
+FA_OK = 0
+FA_ERR_INVALID = -1
+FA_ERR_UNSUPPORTED = -2
+FA_ERR_ALIGN = -3
+FA_ERR_WORKSPACE = -4
+FA_ERR_HIP = -5
+FA_ERR_TOO_LARGE = -6
+
+EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_workspace_size", "fa_bwd_preprocess",
+            "fa_bwd_main", "fa_bwd_dq_convert", "fa_strerror")
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {fa_strerror(status)} ({status})")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libfa.so (built in-tree by ``exact_attention_98_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                           "`python -m exact_attention_98_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, ci, cf, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp]
+    lib.fa_fwd.restype = ci
+    lib.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, vp]
+    lib.fa_fwd_ex.restype = ci
+    lib.fa_bwd_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci]
+    lib.fa_bwd_workspace_size.restype = sz
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp, sz,
+                           ci, vp]
+    lib.fa_bwd.restype = ci
+    lib.fa_bwd_preprocess.argtypes = [vp, vp, ci, ci, ci, ci, ci, vp, sz, ci, vp]
+    lib.fa_bwd_preprocess.restype = ci
+    lib.fa_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp, sz, ci,
+                                vp]
+    lib.fa_bwd_main.restype = ci
+    lib.fa_bwd_dq_convert.argtypes = [vp, ci, ci, ci, ci, ci, cf, vp, sz, ci, vp]
+    lib.fa_bwd_dq_convert.restype = ci
+    lib.fa_strerror.argtypes = [ci]
+    lib.fa_strerror.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+# ----------------------------------------------------------------- raw C ABI
+def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, D, causal, scale, stream) -> int:
+    return load().fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, D, int(causal), float(scale), stream)
+
+
+def fa_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, N, D, causal, scale, exp_poly_quarters, stream) -> int:
+    return load().fa_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, N, D, int(causal), float(scale),
+                            int(exp_poly_quarters), stream)
+
+
+def fa_bwd_workspace_size(B, Hq, Hkv, N, D, deterministic) -> int:
+    return int(load().fa_bwd_workspace_size(B, Hq, Hkv, N, D, int(deterministic)))
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, D, causal, scale, workspace,
+           workspace_bytes, deterministic, stream) -> int:
+    return load().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, D, int(causal),
+                         float(scale), workspace, workspace_bytes, int(deterministic), stream)
+
+
+def fa_bwd_preprocess(o, dout, B, Hq, Hkv, N, D, workspace, workspace_bytes, deterministic,
+                      stream) -> int:
+    return load().fa_bwd_preprocess(o, dout, B, Hq, Hkv, N, D, workspace, workspace_bytes,
+                                     int(deterministic), stream)
+
+
+def fa_bwd_main(q, k, v, lse, dout, dk, dv, B, Hq, Hkv, N, D, causal, scale, workspace,
+                workspace_bytes, deterministic, stream) -> int:
+    return load().fa_bwd_main(q, k, v, lse, dout, dk, dv, B, Hq, Hkv, N, D, int(causal),
+                              float(scale), workspace, workspace_bytes, int(deterministic), stream)
+
+
+def fa_bwd_dq_convert(dq, B, Hq, Hkv, N, D, scale, workspace, workspace_bytes, deterministic,
+                      stream) -> int:
+    return load().fa_bwd_dq_convert(dq, B, Hq, Hkv, N, D, float(scale), workspace,
+                                    workspace_bytes, int(deterministic), stream)
+
+
+def fa_strerror(status: int) -> str:
+    return load().fa_strerror(int(status)).decode()
+
+
+# ------------------------------------------------------- torch conveniences
+def _check(name, t, dtype, shape):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _stream_handle(device):
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def forward(q, k, v, causal: bool, scale: float, *, exp_poly_quarters: int | None = None,
+            out=None, lse=None):
+    """O (bf16) and LSE (fp32) for q [B,Hq,N,D], k/v [B,Hkv,N,D] bf16 device tensors."""
+    import torch
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, D]")
+    B, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    _check("q", q, torch.bfloat16, (B, Hq, N, D))
+    _check("k", k, torch.bfloat16, (B, Hkv, N, D))
+    _check("v", v, torch.bfloat16, (B, Hkv, N, D))
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _check("out", out, torch.bfloat16, (B, Hq, N, D))
+    _check("lse", lse, torch.float32, (B, Hq, N))
+    stream = _stream_handle(q.device)
+    if exp_poly_quarters is None:
+        rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B,
+                    Hq, Hkv, N, D, causal, scale, stream)
+    else:
+        rc = fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                       B, Hq, Hkv, N, D, causal, scale, exp_poly_quarters, stream)
+    if rc != FA_OK:
+        raise FaError(rc, "fa_fwd")
+    return out, lse
+
+
+def backward(q, k, v, o, lse, dout, causal: bool, scale: float, *, deterministic: bool = False,
+             workspace=None, dq=None, dk=None, dv=None):
+    """dQ, dK, dV (bf16) for the forward's inputs/outputs and dO."""
+    import torch
+    B, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    for name, t, shp in (("q", q, (B, Hq, N, D)), ("k", k, (B, Hkv, N, D)),
+                         ("v", v, (B, Hkv, N, D)), ("o", o, (B, Hq, N, D)),
+                         ("dout", dout, (B, Hq, N, D))):
+        _check(name, t, torch.bfloat16, shp)
+    _check("lse", lse, torch.float32, (B, Hq, N))
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    ws_bytes = fa_bwd_workspace_size(B, Hq, Hkv, N, D, deterministic)
+    if ws_bytes == 0:
+        raise FaError(FA_ERR_INVALID, "fa_bwd_workspace_size")
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    if workspace.numel() < ws_bytes:
+        raise FaError(FA_ERR_WORKSPACE, "fa_bwd")
+    rc = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, N, D,
+                causal, scale, workspace.data_ptr(), workspace.numel(), deterministic,
+                _stream_handle(q.device))
+    if rc != FA_OK:
+        raise FaError(rc, "fa_bwd")
+    return dq, dk, dv

@@ -1,0 +1,198 @@
+// C ABI of the attention library: argument checks, workspace sizing and
+// dispatch to the gfx950 kernels.  Every check runs before any launch, the
+// library allocates and synchronizes nothing, and no exception crosses the
+// boundary.
+#include <math.h>
+#include <stdint.h>
+
+#include <initializer_list>
+
+#include "../../include/fa.h"
+#include "kernels.hpp"
+
+namespace {
+
+// Share of exponentials given to the FMA polynomial by fa_fwd.
+constexpr int kDefaultPolyQuarters = 0;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+// Shape checks shared by forward and backward.
+int check_shape(int B, int Hq, int Hkv, int N, int D, float scale) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || D < 1) return FA_ERR_INVALID;
+  if (Hq % Hkv != 0) return FA_ERR_INVALID;
+  if (!isfinite(scale)) return FA_ERR_INVALID;
+  if (!(scale > 0.f)) return FA_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+  const uint64_t elems = (uint64_t)B * (uint64_t)Hq * (uint64_t)N * (uint64_t)D;
+  if (elems >= (1ull << 31)) return FA_ERR_TOO_LARGE;
+  return FA_OK;
+}
+
+int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+             int Hkv, int N, int D, int causal, float scale, int poly_quarters, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID;
+  int rc = check_shape(B, Hq, Hkv, N, D, scale);
+  if (rc != FA_OK) return rc;
+  if (poly_quarters < 0 || poly_quarters > 2) return FA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  const size_t qbytes = (size_t)B * Hq * N * D * 2, kvbytes = (size_t)B * Hkv * N * D * 2;
+  const size_t lbytes = (size_t)B * Hq * N * 4;
+  if (overlaps(o, qbytes, q, qbytes) || overlaps(o, qbytes, k, kvbytes) ||
+      overlaps(o, qbytes, v, kvbytes) || overlaps(lse, lbytes, o, qbytes) ||
+      overlaps(lse, lbytes, q, qbytes) || overlaps(lse, lbytes, k, kvbytes) ||
+      overlaps(lse, lbytes, v, kvbytes))
+    return FA_ERR_INVALID;
+  fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, D, causal ? 1 : 0, scale, poly_quarters};
+  hipError_t e = fa::launch_fwd(a, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+           int Hkv, int N, int D, int causal, float scale, void* stream) {
+  return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, N, D, causal, scale, kDefaultPolyQuarters, stream);
+}
+
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+              int Hkv, int N, int D, int causal, float scale, int exp_poly_quarters,
+              void* stream) {
+  return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, N, D, causal, scale, exp_poly_quarters, stream);
+}
+
+size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int D, int deterministic) {
+  if (check_shape(B, Hq, Hkv, N, D, 1.0f) != FA_OK) return 0;
+  return fa::bwd_layout(B, Hq, N, D, deterministic ? 1 : 0).total;
+}
+
+}  // extern "C"
+
+namespace {
+
+struct Buf {
+  const void* p;
+  size_t bytes;
+};
+
+// Checks shared by the backward entry points: shape, scale, workspace size
+// and alignment, pointer alignment, and that no written buffer overlaps any
+// other buffer of the call.
+int check_bwd(int B, int Hq, int Hkv, int N, int D, float scale, const void* workspace,
+              size_t workspace_bytes, int deterministic, std::initializer_list<Buf> reads,
+              std::initializer_list<Buf> writes) {
+  for (const Buf& b : reads)
+    if (!b.p) return FA_ERR_INVALID;
+  for (const Buf& b : writes)
+    if (!b.p) return FA_ERR_INVALID;
+  int rc = check_shape(B, Hq, Hkv, N, D, scale);
+  if (rc != FA_OK) return rc;
+  for (const Buf& b : reads)
+    if (!aligned16(b.p)) return FA_ERR_ALIGN;
+  for (const Buf& b : writes)
+    if (!aligned16(b.p)) return FA_ERR_ALIGN;
+  const fa::BwdLayout lay = fa::bwd_layout(B, Hq, N, D, deterministic ? 1 : 0);
+  if (!workspace || workspace_bytes < lay.total) return FA_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & 255u) != 0) return FA_ERR_ALIGN;
+  const Buf ws{workspace, lay.total};
+  const Buf* wb = writes.begin();
+  const size_t nw = writes.size();
+  for (size_t i = 0; i < nw; ++i) {
+    for (const Buf& r : reads)
+      if (overlaps(wb[i].p, wb[i].bytes, r.p, r.bytes)) return FA_ERR_INVALID;
+    for (size_t j = 0; j < nw; ++j)
+      if (j != i && overlaps(wb[i].p, wb[i].bytes, wb[j].p, wb[j].bytes)) return FA_ERR_INVALID;
+    if (overlaps(wb[i].p, wb[i].bytes, ws.p, ws.bytes)) return FA_ERR_INVALID;
+  }
+  for (const Buf& r : reads)
+    if (overlaps(r.p, r.bytes, ws.p, ws.bytes)) return FA_ERR_INVALID;
+  return FA_OK;
+}
+
+fa::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N,
+                     int D, int causal, float scale, void* workspace, int deterministic) {
+  return fa::BwdArgs{q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, D, causal ? 1 : 0, scale,
+                     deterministic ? 1 : 0, workspace};
+}
+
+size_t qbytes(int B, int Hq, int N, int D) { return (size_t)B * Hq * N * D * 2; }
+size_t lbytes(int B, int Hq, int N) { return (size_t)B * Hq * N * 4; }
+
+}  // namespace
+
+extern "C" {
+
+int fa_bwd_preprocess(const void* o, const void* dout, int B, int Hq, int Hkv, int N, int D,
+                      void* workspace, size_t workspace_bytes, int deterministic, void* stream) {
+  const size_t qb = qbytes(B, Hq, N, D);
+  int rc = check_bwd(B, Hq, Hkv, N, D, 1.0f, workspace, workspace_bytes, deterministic,
+                     {{o, qb}, {dout, qb}}, {});
+  if (rc != FA_OK) return rc;
+  const fa::BwdArgs a = bwd_args(nullptr, nullptr, nullptr, o, nullptr, dout, nullptr, nullptr,
+                                 nullptr, B, Hq, Hkv, N, D, 0, 1.0f, workspace, deterministic);
+  return fa::launch_bwd_preprocess(a, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_bwd_main(const void* q, const void* k, const void* v, const float* lse, const void* dout,
+                void* dk, void* dv, int B, int Hq, int Hkv, int N, int D, int causal, float scale,
+                void* workspace, size_t workspace_bytes, int deterministic, void* stream) {
+  const size_t qb = qbytes(B, Hq, N, D), kb = qbytes(B, Hkv, N, D), lb = lbytes(B, Hq, N);
+  int rc = check_bwd(B, Hq, Hkv, N, D, scale, workspace, workspace_bytes, deterministic,
+                     {{q, qb}, {k, kb}, {v, kb}, {lse, lb}, {dout, qb}}, {{dk, kb}, {dv, kb}});
+  if (rc != FA_OK) return rc;
+  const fa::BwdArgs a = bwd_args(q, k, v, nullptr, lse, dout, nullptr, dk, dv, B, Hq, Hkv, N, D,
+                                 causal, scale, workspace, deterministic);
+  return fa::launch_bwd_main(a, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_bwd_dq_convert(void* dq, int B, int Hq, int Hkv, int N, int D, float scale,
+                      void* workspace, size_t workspace_bytes, int deterministic, void* stream) {
+  int rc = check_bwd(B, Hq, Hkv, N, D, scale, workspace, workspace_bytes, deterministic, {},
+                     {{dq, qbytes(B, Hq, N, D)}});
+  if (rc != FA_OK) return rc;
+  const fa::BwdArgs a = bwd_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, dq, nullptr,
+                                 nullptr, B, Hq, Hkv, N, D, 0, scale, workspace, deterministic);
+  return fa::launch_bwd_dq_convert(a, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N, int D,
+           int causal, float scale, void* workspace, size_t workspace_bytes, int deterministic,
+           void* stream) {
+  const size_t qb = qbytes(B, Hq, N, D), kb = qbytes(B, Hkv, N, D), lb = lbytes(B, Hq, N);
+  int rc = check_bwd(B, Hq, Hkv, N, D, scale, workspace, workspace_bytes, deterministic,
+                     {{q, qb}, {k, kb}, {v, kb}, {o, qb}, {lse, lb}, {dout, qb}},
+                     {{dq, qb}, {dk, kb}, {dv, kb}});
+  if (rc != FA_OK) return rc;
+  const fa::BwdArgs a = bwd_args(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, D, causal,
+                                 scale, workspace, deterministic);
+  hipStream_t s = (hipStream_t)stream;
+  if (fa::launch_bwd_preprocess(a, s) != hipSuccess) return FA_ERR_HIP;
+  if (fa::launch_bwd_main(a, s) != hipSuccess) return FA_ERR_HIP;
+  if (fa::launch_bwd_dq_convert(a, s) != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
+}
+
+const char* fa_strerror(int status) {
+  switch (status) {
+    case FA_OK: return "success";
+    case FA_ERR_INVALID: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FA_ERR_ALIGN: return "pointer not aligned (16 bytes; workspace 256 bytes)";
+    case FA_ERR_WORKSPACE: return "workspace missing or too small";
+    case FA_ERR_HIP: return "HIP runtime error at launch";
+    case FA_ERR_TOO_LARGE: return "tensor too large (2^31 elements or more)";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,64 @@
+// Internal launch interface between the C ABI (fa_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, Hq, Hkv, N, D;
+  int causal;
+  float scale;
+  int poly_quarters;
+};
+
+// Kernel-side parameters of the forward (passed by value).
+struct FwdParams {
+  int BH;     // B * Hq
+  int Hq;
+  int G;      // Hq / Hkv
+  int N;
+  int nqb;    // query tiles per head
+  float c;    // scale * log2(e)
+};
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, Hq, Hkv, N, D;
+  int causal;
+  float scale;
+  int deterministic;
+  void* workspace;
+};
+
+// Workspace layout of the backward (offsets in bytes, 256-byte aligned).
+struct BwdLayout {
+  size_t dq_acc;    // fp32 [B][Hq][N][D]
+  size_t delta;     // fp32 [B][Hq][N]
+  size_t counters;  // int32 [B][Hq][query tiles] (deterministic only)
+  size_t total;
+};
+
+BwdLayout bwd_layout(int B, int Hq, int N, int D, int deterministic);
+// The three backward stages; each reads only the BwdArgs fields it needs.
+hipError_t launch_bwd_preprocess(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_dq_convert(const BwdArgs& a, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,138 @@
+/*
+ * fa.h -- C ABI of the fused exact-attention library for AMD Instinct MI355X (gfx950).
+ *
+ * The library computes O = softmax(scale * Q K^T) V and its gradients without
+ * ever forming the N x N score matrix: Q tiles stay resident while K/V tiles
+ * stream past them, with a running row max and row sum (online softmax).
+ * Passages followed:
+ *   - tiling and online softmax: "FlashAttention-4 算法解析" (zeeklog), section 4,
+ *     the tiled forward pseudocode;
+ *   - exp2 with the scale folded into log2(e), conditional rescale with
+ *     tau = log2(256) = 8 and one final correction, optional cubic-polynomial
+ *     exp2 after a 2^n / fraction split: hotelren FlashAttention-4 summary,
+ *     sections 3.2 and 3.3; danialwang explainer, section 04 (巧招一, 巧招二);
+ *   - backward recomputing P and forming dV, dP, dS, dK, dQ, with atomic dQ
+ *     accumulation or a fixed-order deterministic mode: hotelren summary,
+ *     sections 4.1-4.2; danialwang explainer, sections 05-06;
+ *   - query heads sharing one K/V head (multi-query / grouped): hotdry
+ *     article, kernel-fusion section.
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are contiguous, layout [B][H][N][D] with D innermost.  q, o, dout
+ *     and dq have Hq heads; k, v, dk and dv have Hkv heads; Hq % Hkv == 0 and
+ *     query head h reads K/V head h / (Hq / Hkv).
+ *   - q, k, v, o, dout, dq, dk, dv are bfloat16; lse is float32 [B][Hq][N].
+ *   - LSE is the natural log of sum_j exp(scale * q_i . k_j) over the keys row
+ *     i may attend to.
+ *   - causal != 0 masks key j for query i when j > i (queries and keys share
+ *     the same length N and start at position 0).
+ *   - Every pointer is a device pointer (HIP), 16-byte aligned.
+ *   - stream is a hipStream_t passed as void*; NULL means the null stream.
+ *   - Ownership: the caller allocates and frees every buffer, workspace
+ *     included.  The library never allocates device memory, never frees and
+ *     never synchronizes: each call only enqueues kernels on `stream` and
+ *     returns.  Outputs are valid once that stream's work has completed.
+ *   - Errors: every argument check runs before any launch, so a call that
+ *     returns an error has launched nothing.  No exception crosses the ABI.
+ *   - Supported now: D in {64, 128}; N >= 1; B, Hq, Hkv >= 1; B*Hq*N*D below
+ *     2^31 elements per tensor.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_INVALID = -1,     /* null pointer, non-positive size, Hq % Hkv != 0, non-finite or non-positive scale, aliasing */
+    FA_ERR_UNSUPPORTED = -2, /* valid request this build does not handle (e.g. D not in {64,128}) */
+    FA_ERR_ALIGN = -3,       /* a pointer is not 16-byte aligned */
+    FA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than fa_bwd_workspace_size() */
+    FA_ERR_HIP = -5,         /* the HIP runtime reported an error at launch */
+    FA_ERR_TOO_LARGE = -6    /* a tensor exceeds 2^31 elements */
+} fa_status;
+
+/*
+ * Forward pass.
+ *   q [B][Hq][N][D], k/v [B][Hkv][N][D] (bf16, read)
+ *   o [B][Hq][N][D] (bf16, written), lse [B][Hq][N] (fp32, written)
+ *   scale: the softmax scale (typically 1/sqrt(D)), finite and > 0.
+ * o must not overlap q, k or v.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int Hq, int Hkv, int N, int D, int causal, float scale, void* stream);
+
+/*
+ * Forward pass with the exp2 split exposed: exp_poly_quarters in {0, 1, 2}
+ * is the share (in quarters) of exponentials evaluated with the FMA-only
+ * cubic polynomial after the 2^n / fraction split instead of the hardware
+ * v_exp_f32 (hotelren summary, section 3.2, mixed execution).  fa_fwd uses
+ * the library's default share.  Same arguments and errors as fa_fwd, plus
+ * FA_ERR_INVALID for a share outside {0, 1, 2}.
+ */
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int Hq, int Hkv, int N, int D, int causal, float scale,
+              int exp_poly_quarters, void* stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for this problem (fp32 dQ
+ * accumulator, per-row Delta = rowsum(dO * O), and for deterministic mode the
+ * per-query-tile order counters).  Returns 0 for invalid sizes.
+ */
+size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int D, int deterministic);
+
+/*
+ * Backward pass.  Recomputes P from q, k and lse (never stored by the
+ * forward), then forms dV = P^T dO, dP = dO V^T, dS = P o (dP - Delta),
+ * dK = scale dS^T Q and dQ = scale dS K.
+ *   q, k, v, o, lse: exactly as given to / returned by fa_fwd (read)
+ *   dout [B][Hq][N][D] (bf16, read)
+ *   dq [B][Hq][N][D], dk/dv [B][Hkv][N][D] (bf16, written)
+ *   workspace: device memory of at least fa_bwd_workspace_size() bytes,
+ *     256-byte aligned, owned by the caller; its contents on entry do not
+ *     matter and are scratch afterwards.  Two calls in flight at once must
+ *     not share a workspace.
+ *   deterministic = 0: dQ contributions are added with fp32 atomics (no
+ *     run-to-run bitwise guarantee).  deterministic = 1: they are added in a
+ *     fixed order, so dq, dk and dv are bit-identical across calls with the
+ *     same inputs on the same device.
+ * With Hq != Hkv, dk and dv sum over the query heads that share a K/V head.
+ * dq, dk, dv must not overlap any input.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv,
+           int B, int Hq, int Hkv, int N, int D, int causal, float scale,
+           void* workspace, size_t workspace_bytes, int deterministic, void* stream);
+
+/*
+ * The three stages fa_bwd runs, exported so that a caller can schedule or
+ * time them separately.  Called in this order on one stream with the same
+ * problem and workspace, they are exactly fa_bwd.  Arguments have the
+ * meaning given for fa_bwd; each stage checks the arguments it uses and
+ * returns the same codes.
+ *   fa_bwd_preprocess: Delta_i = rowsum(dO * O) into the workspace, and
+ *     clears the workspace's fp32 dQ accumulator (and order counters).
+ *   fa_bwd_main: recomputes P tile by tile and forms dK, dV (written to dk,
+ *     dv) and the unscaled dQ sums (accumulated in the workspace).
+ *   fa_bwd_dq_convert: dq = bf16(scale * accumulated dQ).
+ */
+int fa_bwd_preprocess(const void* o, const void* dout, int B, int Hq, int Hkv, int N, int D,
+                      void* workspace, size_t workspace_bytes, int deterministic, void* stream);
+int fa_bwd_main(const void* q, const void* k, const void* v, const float* lse, const void* dout,
+                void* dk, void* dv, int B, int Hq, int Hkv, int N, int D, int causal, float scale,
+                void* workspace, size_t workspace_bytes, int deterministic, void* stream);
+int fa_bwd_dq_convert(void* dq, int B, int Hq, int Hkv, int N, int D, float scale,
+                      void* workspace, size_t workspace_bytes, int deterministic, void* stream);
+
+/* Static text for a status code. */
+const char* fa_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

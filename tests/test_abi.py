@@ -1,0 +1,116 @@
+"""The C ABI: library loads, exports every declared entry point, and rejects bad
+arguments before launching anything.  No GPU is used: every call here fails an
+argument check, which runs before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_attention_98_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = fa.load()
+    names = _declared()
+    assert set(names) == set(fa.EXPORTED)
+    for name in names:
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_strerror():
+    assert fa.fa_strerror(0) == "success"
+    for code in range(-6, 0):
+        assert fa.fa_strerror(code) != "unknown status"
+    assert fa.fa_strerror(-99) == "unknown status"
+
+
+# Fake, well-separated, 256-byte aligned device addresses: never dereferenced,
+# because each call below fails a host-side check first.
+Q, K, V, O, L, DO, DQ, DK, DV, WS = [(i + 1) << 36 for i in range(10)]
+
+
+def fwd(**kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, B=1, Hq=2, Hkv=1, N=64, D=128, causal=1, scale=0.1,
+             stream=None)
+    a.update(kw)
+    return fa.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["N"],
+                     a["D"], a["causal"], a["scale"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), fa.FA_ERR_INVALID), (dict(lse=None), fa.FA_ERR_INVALID),
+    (dict(B=0), fa.FA_ERR_INVALID), (dict(N=0), fa.FA_ERR_INVALID), (dict(N=-5), fa.FA_ERR_INVALID),
+    (dict(Hq=3, Hkv=2), fa.FA_ERR_INVALID), (dict(Hkv=0), fa.FA_ERR_INVALID),
+    (dict(D=96), fa.FA_ERR_UNSUPPORTED), (dict(D=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(D=0), fa.FA_ERR_INVALID),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID), (dict(scale=float("inf")), fa.FA_ERR_INVALID),
+    (dict(scale=-1.0), fa.FA_ERR_UNSUPPORTED),
+    (dict(q=Q + 2), fa.FA_ERR_ALIGN), (dict(o=O + 8), fa.FA_ERR_ALIGN),
+    (dict(o=Q), fa.FA_ERR_INVALID), (dict(lse=O + 64), fa.FA_ERR_INVALID),
+    (dict(B=1 << 10, Hq=1 << 10, Hkv=1 << 10, N=1 << 10, D=128), fa.FA_ERR_TOO_LARGE),
+])
+def test_fwd_rejects(kw, code):
+    assert fwd(**kw) == code
+
+
+def test_fwd_ex_rejects_bad_share():
+    assert fa.fa_fwd_ex(Q, K, V, O, L, 1, 1, 1, 64, 64, 0, 0.125, 3, None) == fa.FA_ERR_INVALID
+    assert fa.fa_fwd_ex(Q, K, V, O, L, 1, 1, 1, 64, 64, 0, 0.125, -1, None) == fa.FA_ERR_INVALID
+
+
+def test_workspace_size():
+    B, H, N, D = 2, 16, 8192, 128
+    s0 = fa.fa_bwd_workspace_size(B, H, H, N, D, 0)
+    s1 = fa.fa_bwd_workspace_size(B, H, H, N, D, 1)
+    assert s0 >= B * H * N * D * 4 + B * H * N * 4
+    assert s1 > s0
+    assert s0 % 256 == 0 and s1 % 256 == 0
+    assert fa.fa_bwd_workspace_size(0, H, H, N, D, 0) == 0
+    assert fa.fa_bwd_workspace_size(B, H, H, N, 80, 0) == 0
+
+
+def bwd(**kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, dout=DO, dq=DQ, dk=DK, dv=DV, B=1, Hq=2, Hkv=2, N=100,
+             D=64, causal=1, scale=0.125, ws=WS, wsb=1 << 30, det=0, stream=None)
+    a.update(kw)
+    return fa.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dout"], a["dq"], a["dk"],
+                     a["dv"], a["B"], a["Hq"], a["Hkv"], a["N"], a["D"], a["causal"], a["scale"],
+                     a["ws"], a["wsb"], a["det"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dout=None), fa.FA_ERR_INVALID), (dict(dv=None), fa.FA_ERR_INVALID),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE), (dict(wsb=1024), fa.FA_ERR_WORKSPACE),
+    (dict(ws=WS + 16), fa.FA_ERR_ALIGN), (dict(dk=DK + 4), fa.FA_ERR_ALIGN),
+    (dict(D=32), fa.FA_ERR_UNSUPPORTED), (dict(Hq=4, Hkv=3), fa.FA_ERR_INVALID),
+    (dict(dq=Q), fa.FA_ERR_INVALID), (dict(dk=DV), fa.FA_ERR_INVALID),
+    (dict(ws=DQ), fa.FA_ERR_INVALID), (dict(scale=float("nan")), fa.FA_ERR_INVALID),
+])
+def test_bwd_rejects(kw, code):
+    assert bwd(**kw) == code
+
+
+def test_bwd_stages_reject():
+    ws = 1 << 30
+    assert fa.fa_bwd_preprocess(None, DO, 1, 2, 2, 64, 64, WS, ws, 0, None) == fa.FA_ERR_INVALID
+    assert fa.fa_bwd_preprocess(O, DO, 1, 2, 2, 64, 64, WS, 16, 0, None) == fa.FA_ERR_WORKSPACE
+    assert fa.fa_bwd_preprocess(O, DO + 8, 1, 2, 2, 64, 64, WS, ws, 0, None) == fa.FA_ERR_ALIGN
+    assert fa.fa_bwd_main(Q, K, V, L, DO, DK, DV, 1, 2, 2, 64, 96, 1, 0.1, WS, ws, 0, None) == \
+        fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_bwd_main(Q, K, V, L, DO, DK, DK, 1, 2, 2, 64, 64, 1, 0.1, WS, ws, 0, None) == \
+        fa.FA_ERR_INVALID
+    assert fa.fa_bwd_main(Q, K, V, L, DO, K, DV, 1, 2, 2, 64, 64, 1, 0.1, WS, ws, 0, None) == \
+        fa.FA_ERR_INVALID
+    assert fa.fa_bwd_dq_convert(WS, 1, 2, 2, 64, 64, 0.1, WS, ws, 0, None) == fa.FA_ERR_INVALID
+    assert fa.fa_bwd_dq_convert(DQ + 2, 1, 2, 2, 64, 64, 0.1, WS, ws, 0, None) == fa.FA_ERR_ALIGN
