@@ -133,11 +133,11 @@ def main() -> int:
         check(fa.fa_fwd(P["q"], P["k"], P["v"], P["o"], P["lse"], B, Hq, Hkv, N, D, 1, w.scale, sh),
               "fa_fwd")
         ev[1].record(stream)
-        check(fa.fa_bwd_preprocess(P["o"], P["do"], B, Hq, Hkv, N, D, P["ws"], ws_bytes, det, sh),
-              "fa_bwd_preprocess")
+        check(fa.fa_bwd_preprocess(P["o"], P["do"], P["lse"], B, Hq, Hkv, N, D, P["ws"], ws_bytes,
+                                   det, sh), "fa_bwd_preprocess")
         ev[2].record(stream)
-        check(fa.fa_bwd_main(P["q"], P["k"], P["v"], P["lse"], P["do"], P["dk"], P["dv"], B, Hq,
-                             Hkv, N, D, 1, w.scale, P["ws"], ws_bytes, det, sh), "fa_bwd_main")
+        check(fa.fa_bwd_main(P["q"], P["k"], P["v"], P["do"], P["dk"], P["dv"], B, Hq, Hkv, N, D,
+                             1, w.scale, P["ws"], ws_bytes, det, sh), "fa_bwd_main")
         ev[3].record(stream)
         check(fa.fa_bwd_dq_convert(P["dq"], B, Hq, Hkv, N, D, w.scale, P["ws"], ws_bytes, det, sh),
               "fa_bwd_dq_convert")

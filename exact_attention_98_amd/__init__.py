@@ -63,10 +63,9 @@ def load():
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp, sz,
                            ci, vp]
     lib.fa_bwd.restype = ci
-    lib.fa_bwd_preprocess.argtypes = [vp, vp, ci, ci, ci, ci, ci, vp, sz, ci, vp]
+    lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, vp, sz, ci, vp]
     lib.fa_bwd_preprocess.restype = ci
-    lib.fa_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp, sz, ci,
-                                vp]
+    lib.fa_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp, sz, ci, vp]
     lib.fa_bwd_main.restype = ci
     lib.fa_bwd_dq_convert.argtypes = [vp, ci, ci, ci, ci, ci, cf, vp, sz, ci, vp]
     lib.fa_bwd_dq_convert.restype = ci
@@ -96,16 +95,16 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, D, causal, scale, w
                          float(scale), workspace, workspace_bytes, int(deterministic), stream)
 
 
-def fa_bwd_preprocess(o, dout, B, Hq, Hkv, N, D, workspace, workspace_bytes, deterministic,
+def fa_bwd_preprocess(o, dout, lse, B, Hq, Hkv, N, D, workspace, workspace_bytes, deterministic,
                       stream) -> int:
-    return load().fa_bwd_preprocess(o, dout, B, Hq, Hkv, N, D, workspace, workspace_bytes,
+    return load().fa_bwd_preprocess(o, dout, lse, B, Hq, Hkv, N, D, workspace, workspace_bytes,
                                      int(deterministic), stream)
 
 
-def fa_bwd_main(q, k, v, lse, dout, dk, dv, B, Hq, Hkv, N, D, causal, scale, workspace,
+def fa_bwd_main(q, k, v, dout, dk, dv, B, Hq, Hkv, N, D, causal, scale, workspace,
                 workspace_bytes, deterministic, stream) -> int:
-    return load().fa_bwd_main(q, k, v, lse, dout, dk, dv, B, Hq, Hkv, N, D, int(causal),
-                              float(scale), workspace, workspace_bytes, int(deterministic), stream)
+    return load().fa_bwd_main(q, k, v, dout, dk, dv, B, Hq, Hkv, N, D, int(causal), float(scale),
+                              workspace, workspace_bytes, int(deterministic), stream)
 
 
 def fa_bwd_dq_convert(dq, B, Hq, Hkv, N, D, scale, workspace, workspace_bytes, deterministic,

@@ -34,6 +34,9 @@ def hipcc() -> str:
 def compile_flags() -> list:
     return [
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-I", CSRC, "-I", INCLUDE,
+        # The kernels produce no NaNs; without this every fmax first
+        # canonicalizes its inputs.
+        "-fno-honor-nans",
         # No packed fp32 (v_pk_*_f32) code generation.
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wno-unused-command-line-argument",

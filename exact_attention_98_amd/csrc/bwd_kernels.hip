@@ -2,7 +2,7 @@
 //
 // The backward recomputes P from Q, K and the forward's LSE instead of
 // storing it (hotdry article, kernel-fusion section) and runs five bf16 MFMA
-// products per K/V tile and query tile (hotelren summary, sections 4.1-4.2):
+// products per K/V tile and query step (hotelren summary, sections 4.1-4.2):
 //   S  = Q K^T              P  = exp2(S c - LSE log2 e)
 //   dP = dO V^T             dS = P o (dP - Delta),  Delta_i = dO_i . O_i
 //   dV += P^T dO            dK += dS^T Q            dQ += dS K
@@ -15,10 +15,15 @@
 // of P^T dO and dS^T Q (a C-layout tile read as an A operand is its own
 // transpose), which is the "compute the transposed form so the result is the
 // next product's operand" idea of the danialwang explainer (section 05).  The
-// B operands of those two products need 8 queries of one d per lane, so Q and
-// dO are also written to LDS transposed, with queries permuted inside each
-// group of 16 to match the accumulator's row order.  dQ contracts over keys,
-// so dS takes one trip through LDS.
+// B operands of those two products need 8 queries of one d per lane; they are
+// read from the row-major Q and dO tiles with ds_read_b64_tr_b16.  dQ
+// contracts over keys, so dS^T takes one trip through LDS and is read back
+// with the same transposing read.
+//
+// Pipeline: Q, dO, LSE*log2e and Delta of query step i+1 are copied from HBM
+// straight into LDS (buffer_load ... lds) while step i computes; the dQ
+// product of step i runs during step i+1, after the one barrier per step that
+// publishes step i's dS^T.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -27,19 +32,9 @@ namespace {
 
 constexpr int kBwdBN = 128;    // keys per workgroup (32 per wave)
 constexpr int kBwdWaves = 4;
-constexpr int kMaxSpin = 1 << 18;  // bound on a deterministic-order wait
+constexpr int kMaxSpin = 1 << 20;  // bound on a deterministic-order wait
 
-__device__ __forceinline__ int pos16(int kl) {
-  return (kl & 3) | ((kl >> 3) & 1) << 2 | ((kl >> 2) & 1) << 3;
-}
-// 16-byte chunk swizzle of a transposed Q / dO row holding RCH chunks
-// (RCH = QS / 8): distinct chunks for 8 consecutive d (MFMA reads) and
-// for d stepping by 8 (staging writes); always < RCH.
-template <int RCH>
-__device__ __forceinline__ int tswz(int d) {
-  if constexpr (RCH >= 8) return (d ^ (d >> 3)) & 7;
-  else return ((d >> 1) ^ (d >> 3)) & (RCH - 1);
-}
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 
 struct BwdParams {
   int B, Hq, G, N;
@@ -49,15 +44,19 @@ struct BwdParams {
   float scale;
   float* dq_acc;   // fp32 [B][Hq][N][D]
   float* delta;    // fp32 [B][Hq][N]
-  int* counters;   // int32 [B][Hq][nqs] (deterministic only)
+  float* lse2;     // fp32 [B][Hq][N]
+  int* counters;   // int32 [B][Hq][nqs][waves] (deterministic only)
+  int* give_up;    // int32: set once a wait has timed out (deterministic only)
 };
 
 // ---------------------------------------------------------------------------
-// Preprocess: Delta_i = sum_d dO[i,d] O[i,d] (fp32), zero the dQ accumulator
-// and the order counters.  A row of D bf16 is read by D/8 lanes (16 B each).
+// Preprocess: Delta_i = sum_d dO[i,d] O[i,d] (fp32), LSE_i * log2(e), and
+// zero the dQ accumulator and the order counters.  A row of D bf16 is read by
+// D/8 lanes (16 B each).
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict__ O,
                                                       const uint16_t* __restrict__ dO,
+                                                      const float* __restrict__ LSE,
                                                       BwdParams p, int rows, int ncount) {
   constexpr int LPR = D / 8;                 // lanes per row
   constexpr int RPB = 256 / LPR;             // rows per block
@@ -79,9 +78,13 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
   }
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (row < rows && c == 0) p.delta[row] = acc;
+  if (row < rows && c == 0) {
+    p.delta[row] = acc;
+    p.lse2[row] = LSE[row] * kLog2e;
+  }
   const int gid = blockIdx.x * 256 + tid;
   if (p.counters && gid < ncount) p.counters[gid] = 0;
+  if (p.give_up && gid == 0) *p.give_up = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -93,22 +96,24 @@ template <int D, bool CAUSAL, bool DET>
 __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-    const float* __restrict__ LSE, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
-    BwdParams p) {
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, BwdParams p) {
   constexpr int BN = kBwdBN;
+  constexpr int RB = D * 2;           // bytes per Q/dO/K/V row
+  constexpr int KCH = D / 8;          // 16-byte chunks per row
   constexpr int QS = 4096 / D;        // queries per step
   constexpr int NQB = QS / 32;        // 32-query blocks per step
   constexpr int ND = D / 32;          // 32-wide d blocks
-  constexpr int KCH = D / 8;          // 16-byte chunks per row
+  constexpr int TB = QS * RB;         // bytes of one Q (or dO) step tile
+  constexpr int NLD = TB / 1024 / kBwdWaves;  // 1 KiB direct loads per wave per tensor
+  constexpr int DSB = BN * QS * 2;    // bytes of one dS^T buffer [key][query]
+  constexpr int DSRB = QS * 2;        // bytes per dS^T row
   static_assert(NQB * ND == kBwdWaves, "one dQ output block per wave");
+  static_assert(NLD >= 1, "step tile too small");
 
-  __shared__ __attribute__((aligned(16))) uint16_t q_s[QS * D];    // row-major, swizzled
-  __shared__ __attribute__((aligned(16))) uint16_t do_s[QS * D];
-  __shared__ __attribute__((aligned(16))) uint16_t qt_s[D * QS];   // transposed, permuted
-  __shared__ __attribute__((aligned(16))) uint16_t dot_s[D * QS];
-  __shared__ __attribute__((aligned(16))) uint16_t ds_s[QS * BN];  // dS [query][key], swizzled
-  __shared__ __attribute__((aligned(16))) float lse_s[QS];
-  __shared__ __attribute__((aligned(16))) float dlt_s[QS];
+  // Per stage: Q tile, dO tile, 256 B of LSE*log2e, 256 B of Delta.
+  constexpr int STAGE = 2 * TB + 512;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE + 2 * DSB];
+  char* const ds_buf = smem + 2 * STAGE;
 
   const int Hkv = p.Hq / p.G;
   const int wg = blockIdx.x;
@@ -117,40 +122,40 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
   const int b = bhk / Hkv, hk = bhk % Hkv;
   const int k0 = kb * BN;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
   const int n = lane & 31, h = lane >> 5;
-  const int kw = k0 + 32 * wave;     // this wave's first key
+  const int kw = k0 + 32 * wave;     // this wave's first key (uniform)
   const int key = kw + n;            // key this lane carries as MFMA column
 
-  const size_t kv_head = ((size_t)b * Hkv + hk) * (size_t)p.N * D;
-  const uint16_t* __restrict__ Kh = K + kv_head;
-  const uint16_t* __restrict__ Vh = V + kv_head;
+  const size_t head_elems = (size_t)p.N * D;
+  const uint32_t head_bytes = (uint32_t)(head_elems * 2);
+  const size_t kv_head = ((size_t)b * Hkv + hk) * head_elems;
+  const rsrc_t kr = make_rsrc_uniform(K + kv_head, head_bytes);
+  const rsrc_t vr = make_rsrc_uniform(V + kv_head, head_bytes);
 
-  // Resident B operands for S = Q K^T and dP = dO V^T (k = d).
+  // Resident B operands for S = Q K^T and dP = dO V^T (k = d); keys past N
+  // read as zero.
   bf16x8 kB[D / 16], vB[D / 16];
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) {
-    u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
-    if (key < p.N) {
-      a = *(const u32x4*)(Kh + (size_t)key * D + 16 * t + 8 * h);
-      c = *(const u32x4*)(Vh + (size_t)key * D + 16 * t + 8 * h);
-    }
-    kB[t] = as_bf16x8(a);
-    vB[t] = as_bf16x8(c);
+    kB[t] = as_bf16x8(buf_load16(kr, (uint32_t)(key * RB + 32 * t + 16 * h)));
+    vB[t] = as_bf16x8(buf_load16(vr, (uint32_t)(key * RB + 32 * t + 16 * h)));
   }
-  // Resident B operand for this wave's dQ block (k = keys of the tile):
-  // lane (d, h) holds K[k0 + 16t + 8h + i][d] for i < 8.
+  // Resident B operand of this wave's dQ block (k = the tile's 128 keys):
+  // lane (d, h) holds K[k0 + 16t + 8(i/4) + 4h + i%4][d] in slot i, matching
+  // the transposing read of dS^T.
   const int dq_qb = wave / ND, dq_db = wave % ND;
   bf16x8 kT[BN / 16];
   {
     const int d = 32 * dq_db + n;
+    const uint16_t* Kh = K + kv_head;
 #pragma unroll
     for (int t = 0; t < BN / 16; ++t) {
       u32x4 w;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int r0 = k0 + 16 * t + 8 * h + 2 * j;
+        const int r0 = k0 + 16 * t + 8 * (j >> 1) + 4 * h + 2 * (j & 1);
         const uint32_t lo = (r0 < p.N) ? Kh[(size_t)r0 * D + d] : 0u;
         const uint32_t hi = (r0 + 1 < p.N) ? Kh[(size_t)(r0 + 1) * D + d] : 0u;
         w[j] = lo | (hi << 16);
@@ -168,200 +173,233 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
       dv_acc[i][r] = 0.f;
     }
 
-  // Staging roles: threads 0..127 load Q, 128..255 load dO; each owns 4 rows
-  // (queries 4g..4g+3 of the step) of one 16-byte d chunk.
-  const int st_half = tid >> 7;            // 0: Q, 1: dO
-  const int st_t = tid & 127;
-  const int st_c = st_t % KCH, st_g = st_t / KCH;
-  static_assert((QS / 4) * KCH == 128, "128 staging threads per tensor");
-
-  // First query step that meets this key tile (causal), else 0.
-  const int qs_first = CAUSAL ? (k0 / QS) : 0;
-
-  for (int g = 0; g < p.G; ++g) {
-    const int hq = hk * p.G + g;
-    const size_t q_head = ((size_t)b * p.Hq + hq) * (size_t)p.N;
-    const uint16_t* __restrict__ src = (st_half ? dO : Q) + q_head * D;
-    const float* __restrict__ lse_h = LSE + q_head;
-    const float* __restrict__ dlt_h = p.delta + q_head;
-    float* __restrict__ dq_h = p.dq_acc + q_head * D;
-
-    for (int qs = p.nqs - 1; qs >= qs_first; --qs) {
-      const int q0 = qs * QS;
-      // ---- stage Q / dO (row-major and transposed), LSE*log2e and Delta ----
-      u32x4 rows[4];
+  // ---- per-lane LDS offsets ------------------------------------------------
+  // Direct loads: load s of this wave fills chunks g = (s*4 + wave)*64 + lane
+  // of a step tile (row g / KCH, physical chunk g % KCH holds logical chunk
+  // (g % KCH) ^ f(row)).
+  uint32_t ld_off[NLD];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int qr = q0 + 4 * st_g + j;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (qr < p.N) v = *(const u32x4*)(src + (size_t)qr * D + st_c * 8);
-        rows[j] = v;
+  for (int s = 0; s < NLD; ++s) {
+    const int g = (s * kBwdWaves + wave) * 64 + lane;
+    const int row = g / KCH, pc = g % KCH;
+    ld_off[s] = (uint32_t)(row * RB + ((pc ^ swz(row)) * 16));
+  }
+  // Row-major A operand (Q of S, dO of dP): row 32 qb + n, logical chunk 2t+h.
+  uint32_t a_off[D / 16];
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) a_off[t] = (uint32_t)(n * RB + (((2 * t + h) ^ swz(n)) * 16));
+  // Transposing B-operand reads of Q / dO (queries 32 qb + 16 u + 8 rd + 4 h +
+  // 0..3 of column d = 32 db + n): lane j of 16-lane group gq points at row
+  // 4 h + j/4 and d = 32 db + 16 (gq & 1) + 4 (j & 3).
+  const int tj = lane & 15, gq = lane >> 4;
+  uint32_t tr_off[ND];
+  {
+    const int row = 4 * h + (tj >> 2);
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+      const int c = 4 * db + 2 * (gq & 1) + ((tj & 3) >> 1);
+      tr_off[db] = (uint32_t)(row * RB + ((c ^ swz(row)) * 16) + (tj & 1) * 8);
+    }
+  }
+  // dS^T [key][query] (rows of DSRB bytes).  Chunk swizzle for 4 consecutive
+  // rows read at two adjacent chunks: fd(r) keeps those 8 chunks on distinct
+  // banks for both 64-byte and 128-byte rows.
+  auto fd = [](int r) { return QS == 32 ? (((r >> 1) & 1) << 1) : swz(r); };
+  // Writer: lane (key 32 wave + n) stores 4 consecutive queries 32 qb + 8 g + 4 h.
+  // Reader (A operand of dQ): lane j of group gq points at key row
+  // 16 t + 8 rd + 4 h + j/4 and query 32 dq_qb + 16 (gq & 1) + 4 (j & 3).
+  uint32_t dsr_off;
+  {
+    const int row = 4 * h + (tj >> 2);
+    const int col = 32 * dq_qb + 16 * (gq & 1) + 4 * (tj & 3);
+    dsr_off = (uint32_t)(row * DSRB + (((col >> 3) ^ fd(row)) * 16) + ((col >> 2) & 1) * 8);
+  }
+  const int ds_wrow = 32 * wave + n;
+
+  // ---- step schedule -------------------------------------------------------
+  // Linear step index i covers (head g, query step qs) with qs descending.
+  const int qs_first = CAUSAL ? (k0 / QS) : 0;
+  const int per_head = max(p.nqs - qs_first, 0);
+  const int nsteps = p.G * per_head;
+  auto step_head = [&](int i) { return hk * p.G + i / per_head; };
+  auto step_qs = [&](int i) { return p.nqs - 1 - (i % per_head); };
+
+  auto issue_step = [&](int i, int stage) {
+    const int hq = step_head(i);
+    const int q0 = step_qs(i) * QS;
+    const size_t qh = ((size_t)b * p.Hq + hq) * head_elems;
+    const uint32_t base = (uint32_t)q0 * RB;
+    const uint32_t left = head_bytes > base ? head_bytes - base : 0u;
+    const rsrc_t qrr = make_rsrc_uniform((const char*)(Q + qh) + base, left);
+    const rsrc_t dor = make_rsrc_uniform((const char*)(dO + qh) + base, left);
+    char* st = smem + stage * STAGE;
+#pragma unroll
+    for (int s = 0; s < NLD; ++s) {
+      lds_dma16(qrr, (lds_void*)(st + (s * kBwdWaves + wave) * 1024), ld_off[s]);
+      lds_dma16(dor, (lds_void*)(st + TB + (s * kBwdWaves + wave) * 1024), ld_off[s]);
+    }
+    const size_t rh = ((size_t)b * p.Hq + hq) * p.N + q0;
+    const uint32_t rleft = (uint32_t)max(p.N - q0, 0) * 4u;
+    if (wave == 0) lds_dma4(make_rsrc_uniform(p.lse2 + rh, rleft), (lds_void*)(st + 2 * TB), lane * 4);
+    if (wave == 1)
+      lds_dma4(make_rsrc_uniform(p.delta + rh, rleft), (lds_void*)(st + 2 * TB + 256), lane * 4);
+  };
+
+  // dQ block of step i (dS^T of that step in ds buffer i & 1).
+  auto dq_step = [&](int i) {
+    const int hq = step_head(i);
+    const int q0 = step_qs(i) * QS;
+    const char* dsb = ds_buf + (i & 1) * DSB;
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int t = 0; t < BN / 16; ++t) {
+      const char* base = dsb + (16 * t) * DSRB + dsr_off;
+      const u32x2 lo = lds_read_tr16((const lds_void*)base);
+      const u32x2 hi = lds_read_tr16((const lds_void*)(base + 8 * DSRB));
+      const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+      acc = mfma32(as_bf16x8(a), kT[t], acc);
+    }
+    // acc register r: query q0 + 32 dq_qb + 8(r/4) + 4h + r%4, d = 32 dq_db + n.
+    const size_t qh = ((size_t)b * p.Hq + hq) * p.N;
+    float* dqh = p.dq_acc + qh * D;
+    const int qrow0 = q0 + 32 * dq_qb + 4 * h;
+    const int d = 32 * dq_db + n;
+    if (!DET) {
+      const rsrc_t dqr = make_rsrc_uniform(dqh, (uint32_t)(head_elems * 4));
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        buf_atomic_add(dqr, (uint32_t)(((qrow0 + 8 * (r >> 2) + (r & 3)) * D + d) * 4), acc[r]);
+    } else {
+      // Fixed order: the key tiles add into this (query step, d block) in
+      // ascending tile order.  The wave waits (bounded) for its turn, adds
+      // with coherent loads and stores, then publishes the next turn.
+      int* cnt = p.counters + (((size_t)b * p.Hq + hq) * p.nqs + step_qs(i)) * kBwdWaves + wave;
+      // A wait that runs past kMaxSpin polls sets give_up, after which no
+      // wave of the call waits again and the remaining adds are atomic (still
+      // correct, no longer ordered), so a call ends in bounded time.
+      bool late = false;
+      int spins = 0;
+      while (__hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != kb) {
+        if (spins >= kMaxSpin ||
+            __hip_atomic_load(p.give_up, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+          late = true;
+          if (lane == 0) __hip_atomic_store(p.give_up, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        ++spins;
       }
-      float lv = 0.f;
-      if (tid < QS) {
-        const int qr = q0 + tid;
-        lv = (qr < p.N) ? lse_h[qr] * kLog2e : __builtin_inff();
-      } else if (tid >= 128 && tid < 128 + QS) {
-        const int qr = q0 + tid - 128;
-        lv = (qr < p.N) ? dlt_h[qr] : 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qg = qrow0 + 8 * (r >> 2) + (r & 3);
+        if (qg < p.N) {
+          float* ptr = dqh + (size_t)qg * D + d;
+          if (late) {
+            atomicAdd(ptr, acc[r]);
+          } else {
+            const float old = __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(ptr, old + acc[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
       }
-      __syncthreads();  // previous step finished reading every LDS buffer
-      {
-        uint16_t* rm = st_half ? do_s : q_s;
-        uint16_t* tr = st_half ? dot_s : qt_s;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      if (lane == 0) __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+
+  if (nsteps > 0) issue_step(0, 0);
+
+  for (int i = 0; i < nsteps; ++i) {
+    const int stage = i & 1;
+    wait_vmcnt<0>();
+    __syncthreads();  // step i inputs are in LDS; dS^T of step i-1 is complete
+    if (i + 1 < nsteps) issue_step(i + 1, stage ^ 1);
+    if (i > 0) dq_step(i - 1);
+
+    const int q0 = step_qs(i) * QS;
+    const char* st = smem + stage * STAGE;
+    const char* qs_l = st;
+    const char* dos_l = st + TB;
+    const float* lse_l = (const float*)(st + 2 * TB);
+    const float* dlt_l = (const float*)(st + 2 * TB + 256);
+    char* dsw = ds_buf + stage * DSB;
+    // Keys of this wave exceed some query of the step only near the diagonal.
+    const bool need_mask = CAUSAL && (q0 < kw + 31);
+    const int lim = key - q0 - 4 * h;  // masked when 32qb + 8(r/4) + r%4 < lim
+
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = 0.f;
+        dp[r] = 0.f;
+      }
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) {
+        const bf16x8 qa = as_bf16x8(*(const u32x4*)(qs_l + qb * 32 * RB + a_off[t]));
+        const bf16x8 da = as_bf16x8(*(const u32x4*)(dos_l + qb * 32 * RB + a_off[t]));
+        s = mfma32(qa, kB[t], s);
+        dp = mfma32(da, vB[t], dp);
+      }
+      // Register r holds query q0 + 32qb + 8(r/4) + 4h + r%4 and key `key`.
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 l4 = *(const f32x4*)(lse_l + 32 * qb + 8 * r4 + 4 * h);
+        const f32x4 d4 = *(const f32x4*)(dlt_l + 32 * qb + 8 * r4 + 4 * h);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int r = 4 * st_g + j;
-          *(u32x4*)(rm + r * D + ((st_c ^ (r & 7)) * 8)) = rows[j];
+          const int r = 4 * r4 + j;
+          float pv = exp2_hw(__builtin_fmaf(s[r], p.c, -l4[j]));
+          if (need_mask && (32 * qb + 8 * r4 + j < lim)) pv = 0.f;  // selects: cheap next to 5 MFMAs
+          s[r] = pv;
+          dp[r] = pv * (dp[r] - d4[j]);
         }
-        const int pos = 16 * (st_g >> 2) + pos16(4 * (st_g & 3));
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int d = st_c * 8 + e;
-          const int w = e >> 1;
-          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-          u32x2 out;
-          out[0] = __builtin_amdgcn_perm(rows[1][w], rows[0][w], sel);
-          out[1] = __builtin_amdgcn_perm(rows[3][w], rows[2][w], sel);
-          const int chunk = (pos >> 3) ^ tswz<QS / 8>(d);
-          *(u32x2*)(tr + d * QS + chunk * 8 + (pos & 7)) = out;
-        }
-        if (tid < QS) lse_s[tid] = lv;
-        else if (tid >= 128 && tid < 128 + QS) dlt_s[tid - 128] = lv;
       }
-      __syncthreads();
-
-      // ---- per wave: S, dP, P, dS for each 32-query block; dV, dK --------
-      const bool need_mask = (CAUSAL && (q0 < kw + 31)) || (kw + 32 > p.N);
+      bf16x8 pa[2], dsa[2];
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        f32x16 s, dp;
+      for (int u = 0; u < 2; ++u) {
+        u32x4 w1, w2;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s[r] = 0.f;
-          dp[r] = 0.f;
+        for (int j = 0; j < 4; ++j) {
+          w1[j] = pack_bf16x2(s[8 * u + 2 * j], s[8 * u + 2 * j + 1]);
+          w2[j] = pack_bf16x2(dp[8 * u + 2 * j], dp[8 * u + 2 * j + 1]);
         }
-        const int qr = 32 * qb + n;  // query row this lane feeds (A operand)
+        pa[u] = as_bf16x8(w1);
+        dsa[u] = as_bf16x8(w2);
+      }
+      // dV += P^T dO and dK += dS^T Q; B operands by transposing reads.
 #pragma unroll
-        for (int t = 0; t < D / 16; ++t) {
-          const int c = (2 * t + h) ^ (qr & 7);
-          const bf16x8 qa = as_bf16x8(*(const u32x4*)(q_s + qr * D + c * 8));
-          const bf16x8 da = as_bf16x8(*(const u32x4*)(do_s + qr * D + c * 8));
-          s = mfma32(qa, kB[t], s);
-          dp = mfma32(da, vB[t], dp);
-        }
-        // Accumulator register r holds query 32qb + 8(r/4) + 4h + r%4, key `key`.
-        bf16x8 pa[2], dsa[2];
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int ql = 32 * qb + 8 * r4 + 4 * h;
-          const f32x4 l4 = *(const f32x4*)(lse_s + ql);
-          const f32x4 d4 = *(const f32x4*)(dlt_s + ql);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int r = 4 * r4 + j;
-            float pv = exp2_hw(__builtin_fmaf(s[r], p.c, -l4[j]));
-            if (need_mask) {
-              const int qg = q0 + ql + j;
-              const bool dead = key >= p.N || (CAUSAL && key > qg);
-              if (dead) pv = 0.f;
-            }
-            s[r] = pv;
-            dp[r] = pv * (dp[r] - d4[j]);
-          }
-        }
+      for (int db = 0; db < ND; ++db)
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          u32x4 w1, w2;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            w1[j] = pack_bf16x2(s[8 * u + 2 * j], s[8 * u + 2 * j + 1]);
-            w2[j] = pack_bf16x2(dp[8 * u + 2 * j], dp[8 * u + 2 * j + 1]);
-          }
-          pa[u] = as_bf16x8(w1);
-          dsa[u] = as_bf16x8(w2);
+          const int roff = (32 * qb + 16 * u) * RB + tr_off[db];
+          const u32x2 olo = lds_read_tr16((const lds_void*)(dos_l + roff));
+          const u32x2 ohi = lds_read_tr16((const lds_void*)(dos_l + roff + 8 * RB));
+          const u32x2 qlo = lds_read_tr16((const lds_void*)(qs_l + roff));
+          const u32x2 qhi = lds_read_tr16((const lds_void*)(qs_l + roff + 8 * RB));
+          const u32x4 ob = {olo[0], olo[1], ohi[0], ohi[1]};
+          const u32x4 qbv = {qlo[0], qlo[1], qhi[0], qhi[1]};
+          dv_acc[db] = mfma32(pa[u], as_bf16x8(ob), dv_acc[db]);
+          dk_acc[db] = mfma32(dsa[u], as_bf16x8(qbv), dk_acc[db]);
         }
-        // dV += P^T dO, dK += dS^T Q: B operand lane (d, h) reads 8 queries.
+      // dS^T -> LDS: lane (key 32 wave + n) writes queries 32qb + 8g + 4h .. +4.
 #pragma unroll
-        for (int db = 0; db < ND; ++db) {
-          const int d = 32 * db + n;
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int chunk = (2 * (2 * qb + u) + h) ^ tswz<QS / 8>(d);
-            const bf16x8 ob = as_bf16x8(*(const u32x4*)(dot_s + d * QS + chunk * 8));
-            const bf16x8 qbv = as_bf16x8(*(const u32x4*)(qt_s + d * QS + chunk * 8));
-            dv_acc[db] = mfma32(pa[u], ob, dv_acc[db]);
-            dk_acc[db] = mfma32(dsa[u], qbv, dk_acc[db]);
-          }
-        }
-        // dS -> LDS as [query][key] (bf16), for the dQ product.
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ql = 32 * qb + 8 * (r >> 2) + 4 * h + (r & 3);
-          const int kl = 32 * wave + n;
-          const int chunk = (kl >> 3) ^ (ql & 7);
-          const uint32_t bits = pack_bf16x2(dp[r], 0.f) & 0xffffu;
-          ds_s[ql * BN + chunk * 8 + (kl & 7)] = (uint16_t)bits;
-        }
-      }
-      __syncthreads();
-
-      // ---- dQ block (32 queries x 32 d) of this wave: dS (keys) . K ------
-      {
-        f32x16 acc;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-        const int qr = 32 * dq_qb + n;
-#pragma unroll
-        for (int t = 0; t < BN / 16; ++t) {
-          const int c = (2 * t + h) ^ (qr & 7);
-          const bf16x8 a = as_bf16x8(*(const u32x4*)(ds_s + qr * BN + c * 8));
-          acc = mfma32(a, kT[t], acc);
-        }
-        // acc register r: query 32 dq_qb + 8(r/4) + 4h + r%4, d = 32 dq_db + n.
-        const int d = 32 * dq_db + n;
-        if (!DET) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int qg = q0 + 32 * dq_qb + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (qg < p.N) atomicAdd(dq_h + (size_t)qg * D + d, acc[r]);
-          }
-        } else {
-          // Fixed order: key tiles add into a query step in ascending order.
-          // Thread 0 waits (bounded) until this tile's turn, the workgroup
-          // adds with plain coherent loads/stores, then publishes the turn.
-          int* cnt = p.counters + ((size_t)b * p.Hq + hq) * p.nqs + qs;
-          __shared__ int s_late;
-          if (tid == 0) {
-            int spins = 0;
-            while (__hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != kb &&
-                   spins < kMaxSpin) {
-              __builtin_amdgcn_s_sleep(1);
-              ++spins;
-            }
-            s_late = spins >= kMaxSpin;
-          }
-          __syncthreads();
-          const bool late = s_late;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int qg = q0 + 32 * dq_qb + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (qg < p.N) {
-              float* ptr = dq_h + (size_t)qg * D + d;
-              if (late) {
-                atomicAdd(ptr, acc[r]);
-              } else {
-                const float old = __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(ptr, old + acc[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              }
-            }
-          }
-          __threadfence();
-          __syncthreads();
-          if (tid == 0) __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        }
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int col = 32 * qb + 8 * g4 + 4 * h;
+        const u32x4 dsw4 = as_u32x4(dsa[g4 >> 1]);
+        u32x2 w;
+        w[0] = dsw4[(g4 & 1) * 2];
+        w[1] = dsw4[(g4 & 1) * 2 + 1];
+        *(u32x2*)(dsw + ds_wrow * DSRB + (((col >> 3) ^ fd(ds_wrow)) * 16) + ((col >> 2) & 1) * 8) = w;
       }
     }
+  }
+  if (nsteps > 0) {
+    __syncthreads();
+    dq_step(nsteps - 1);
   }
 
   // ---- dK (scaled) and dV of this wave's 32 keys ----------------------------
@@ -372,9 +410,9 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
   for (int db = 0; db < ND; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int kr = kw + 8 * (r >> 2) + 4 * h + (r & 3);
-      if (kr < p.N) {
-        const size_t off = (size_t)kr * D + 32 * db + n;
+      const int krow = kw + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (krow < p.N) {
+        const size_t off = (size_t)krow * D + 32 * db + n;
         dKh[off] = (uint16_t)(pack_bf16x2(dk_acc[db][r] * p.scale, 0.f) & 0xffffu);
         dVh[off] = (uint16_t)(pack_bf16x2(dv_acc[db][r], 0.f) & 0xffffu);
       }
@@ -403,7 +441,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, const BwdParams& p, hipStream_t s) {
   const dim3 grid((unsigned)(a.B * a.Hkv * p.nkb));
   hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL, DET>), grid, dim3(64 * kBwdWaves), 0, s,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (const uint16_t*)a.dout, a.lse, (uint16_t*)a.dk, (uint16_t*)a.dv, p);
+                     (const uint16_t*)a.dout, (uint16_t*)a.dk, (uint16_t*)a.dv, p);
   return hipGetLastError();
 }
 
@@ -422,7 +460,9 @@ BwdParams make_params(const BwdArgs& a) {
   p.scale = a.scale;
   p.dq_acc = (float*)(ws + lay.dq_acc);
   p.delta = (float*)(ws + lay.delta);
+  p.lse2 = (float*)(ws + lay.lse2);
   p.counters = a.deterministic ? (int*)(ws + lay.counters) : nullptr;
+  p.give_up = a.deterministic ? (int*)(ws + lay.give_up) : nullptr;
   return p;
 }
 
@@ -431,11 +471,11 @@ hipError_t launch_pre_d(const BwdArgs& a, hipStream_t s) {
   const BwdParams p = make_params(a);
   const int rows = a.B * a.Hq * a.N;
   constexpr int RPB = 256 / (D / 8);
-  const int ncount = a.deterministic ? a.B * a.Hq * p.nqs : 0;
+  const int ncount = a.deterministic ? a.B * a.Hq * p.nqs * kBwdWaves : 0;
   int blocks = (rows + RPB - 1) / RPB;
   blocks = max(blocks, (ncount + 255) / 256);
   hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3(blocks), dim3(256), 0, s, (const uint16_t*)a.o,
-                     (const uint16_t*)a.dout, p, rows, ncount);
+                     (const uint16_t*)a.dout, a.lse, p, rows, ncount);
   return hipGetLastError();
 }
 
@@ -452,12 +492,15 @@ hipError_t launch_main_d(const BwdArgs& a, hipStream_t s) {
 BwdLayout bwd_layout(int B, int Hq, int N, int D, int deterministic) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const int QS = 4096 / D;
+  const size_t rows = (size_t)B * Hq * N;
   BwdLayout l;
   l.dq_acc = 0;
-  l.delta = up((size_t)B * Hq * N * D * 4);
-  l.counters = l.delta + up((size_t)B * Hq * N * 4);
+  l.delta = up(rows * D * 4);
+  l.lse2 = l.delta + up(rows * 4);
+  l.counters = l.lse2 + up(rows * 4);
   const size_t nqs = (size_t)(N + QS - 1) / QS;
-  l.total = l.counters + (deterministic ? up((size_t)B * Hq * nqs * 4) : 0);
+  l.give_up = l.counters + (deterministic ? up((size_t)B * Hq * nqs * kBwdWaves * 4) : 0);
+  l.total = l.give_up + (deterministic ? 256 : 0);
   return l;
 }
 

@@ -43,8 +43,80 @@ __device__ __forceinline__ float bf16_bits_to_float(uint32_t b16) {
   return __builtin_bit_cast(float, b16 << 16);
 }
 
-// Value of the same register in lane l ^ 32 (the other half of the wave).
+// Combine a value with the same register of lane l ^ 32 (the other half of
+// the wave).  This goes through ds_bpermute (__shfl_xor); the gfx950
+// v_permlane32_swap builtin is not used because this compiler drops its
+// second result (r[0] + r[1] compiles to r[0] + r[0]).
+__device__ __forceinline__ float xhalf_max(float v) { return __builtin_fmaxf(v, __shfl_xor(v, 32, 64)); }
+__device__ __forceinline__ float xhalf_sum(float v) { return v + __shfl_xor(v, 32, 64); }
 __device__ __forceinline__ float xhalf(float v) { return __shfl_xor(v, 32, 64); }
+
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
+// ---- buffer resources -------------------------------------------------------
+// Raw buffer descriptor over [base, base + bytes): loads past `bytes` return
+// zero and stores there are dropped, which handles ragged tails without
+// branches.  Word 3 0x00020000 is the gfx9-family raw-buffer format.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+// Same, for a base and size that are the same in every lane: the values are
+// moved to scalar registers so the descriptor needs no per-lane handling.
+__device__ __forceinline__ rsrc_t make_rsrc_uniform(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint32_t nb = __builtin_amdgcn_readfirstlane(bytes);
+  return make_rsrc((const void*)(((uint64_t)hi << 32) | lo), nb);
+}
+// Keeps the compiler from turning the guarded block into selects that run on
+// every path (used for rare, wave-uniform branches).
+__device__ __forceinline__ void keep_branch() { asm volatile("" ::: "memory"); }
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+__device__ __forceinline__ void buf_store8(rsrc_t r, uint32_t voff, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, voff, 0, 0);
+}
+__device__ __forceinline__ void buf_store4(rsrc_t r, uint32_t voff, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, 0, 0);
+}
+// 16 bytes per lane from global memory straight into LDS
+// (buffer_load_dwordx4 ... lds): lane l's bytes land at lds + 16 l, where lds
+// is wave-uniform.  Completion is tracked by vmcnt.
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ void lds_dma16(rsrc_t r, lds_void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(rsrc_t r, lds_void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 4, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void buf_atomic_add(rsrc_t r, uint32_t voff, float v) {
+  __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r, voff, 0, 0);
+}
+// Wait until at most n vector-memory operations of this wave are in flight.
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
+}
+
+// ---- LDS transposing read -------------------------------------------------------
+// ds_read_b64_tr_b16: in each group of 16 lanes, lane j supplies the address of
+// 4 consecutive bf16 (8 bytes); lane i receives element i % 4 of the chunks
+// supplied by lanes i/4 + 4s, s = 0..3.  So if lane j points at row base + j/4,
+// column c0 + 4 (j % 4) of a row-major bf16 matrix, lane i receives the column
+// c0 + i of rows base .. base + 3.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+__device__ __forceinline__ u32x2 lds_read_tr16(const lds_void* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p));
+}
 
 // Hardware exp2 (v_exp_f32); exp2(-inf) = 0.
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -131,26 +131,27 @@ size_t lbytes(int B, int Hq, int N) { return (size_t)B * Hq * N * 4; }
 
 extern "C" {
 
-int fa_bwd_preprocess(const void* o, const void* dout, int B, int Hq, int Hkv, int N, int D,
-                      void* workspace, size_t workspace_bytes, int deterministic, void* stream) {
-  const size_t qb = qbytes(B, Hq, N, D);
+int fa_bwd_preprocess(const void* o, const void* dout, const float* lse, int B, int Hq, int Hkv,
+                      int N, int D, void* workspace, size_t workspace_bytes, int deterministic,
+                      void* stream) {
+  const size_t qb = qbytes(B, Hq, N, D), lb = lbytes(B, Hq, N);
   int rc = check_bwd(B, Hq, Hkv, N, D, 1.0f, workspace, workspace_bytes, deterministic,
-                     {{o, qb}, {dout, qb}}, {});
+                     {{o, qb}, {dout, qb}, {lse, lb}}, {});
   if (rc != FA_OK) return rc;
-  const fa::BwdArgs a = bwd_args(nullptr, nullptr, nullptr, o, nullptr, dout, nullptr, nullptr,
+  const fa::BwdArgs a = bwd_args(nullptr, nullptr, nullptr, o, lse, dout, nullptr, nullptr,
                                  nullptr, B, Hq, Hkv, N, D, 0, 1.0f, workspace, deterministic);
   return fa::launch_bwd_preprocess(a, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-int fa_bwd_main(const void* q, const void* k, const void* v, const float* lse, const void* dout,
-                void* dk, void* dv, int B, int Hq, int Hkv, int N, int D, int causal, float scale,
-                void* workspace, size_t workspace_bytes, int deterministic, void* stream) {
-  const size_t qb = qbytes(B, Hq, N, D), kb = qbytes(B, Hkv, N, D), lb = lbytes(B, Hq, N);
+int fa_bwd_main(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv,
+                int B, int Hq, int Hkv, int N, int D, int causal, float scale, void* workspace,
+                size_t workspace_bytes, int deterministic, void* stream) {
+  const size_t qb = qbytes(B, Hq, N, D), kb = qbytes(B, Hkv, N, D);
   int rc = check_bwd(B, Hq, Hkv, N, D, scale, workspace, workspace_bytes, deterministic,
-                     {{q, qb}, {k, kb}, {v, kb}, {lse, lb}, {dout, qb}}, {{dk, kb}, {dv, kb}});
+                     {{q, qb}, {k, kb}, {v, kb}, {dout, qb}}, {{dk, kb}, {dv, kb}});
   if (rc != FA_OK) return rc;
-  const fa::BwdArgs a = bwd_args(q, k, v, nullptr, lse, dout, nullptr, dk, dv, B, Hq, Hkv, N, D,
-                                 causal, scale, workspace, deterministic);
+  const fa::BwdArgs a = bwd_args(q, k, v, nullptr, nullptr, dout, nullptr, dk, dv, B, Hq, Hkv, N,
+                                 D, causal, scale, workspace, deterministic);
   return fa::launch_bwd_main(a, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -1,14 +1,16 @@
 // Fused exact-attention forward for gfx950 (MI355X).
 //
 // One workgroup of 4 waves owns a tile of 128 queries of one (batch, head);
-// each wave owns 32 of them.  K/V tiles of 64 keys stream through LDS
-// (double-buffered) past the resident Q fragments, and each tile runs
+// each wave owns 32 of them.  K/V tiles of 64 keys are copied from HBM
+// straight into LDS (buffer_load ... lds, double-buffered, one barrier per
+// tile) past the resident Q fragments, and each tile runs
 //   S^T = K Q^T          (bf16 MFMA 32x32x16, fp32 accumulate)
 //   mask                 (only on tiles that cross the diagonal or the tail)
-//   row max              (in-lane over 32 scores, then one cross-half step)
+//   row max              (in-lane over 32 scores, then one cross-half swap)
 //   conditional rescale  (only when a row max grows by more than tau = 8)
 //   P^T = exp2(S^T c - m_ref), c = scale * log2(e); row sum in fp32
-//   O^T += V^T P^T       (P^T used straight from the accumulator registers)
+//   O^T += V^T P^T       (P^T used straight from the accumulator registers,
+//                         V^T read from row-major V with ds_read_b64_tr_b16)
 // and the epilogue applies the one final correction O / l and writes
 // LSE = (m_ref + log2 l) ln 2.
 //
@@ -20,13 +22,17 @@
 // explainer, section 05 (the detail under "一个体现功力的细节").
 //
 // Why S^T: the 32x32 MFMA accumulator gives lane l the column l % 32.  With
-// queries as columns, each lane holds 16 scores of its own query, so the row
-// max and sum are in-lane plus one exchange with lane l ^ 32, the per-row
-// rescale factor is a per-lane scalar, and the accumulator of S^T is exactly
-// the B operand of O^T += V^T P^T (its rows are the contraction index).  The
-// A operand V^T needs 8 keys of one d per lane, so V is written to LDS
-// transposed, with keys permuted inside each group of 16 so that those 8 keys
-// are one 16-byte read.
+// queries as columns, each lane holds 16 scores of its own query per 32-key
+// block, so the row max and sum are in-lane plus one exchange with lane
+// l ^ 32, the per-row rescale factor is a per-lane scalar, and the
+// accumulator of S^T is exactly the B operand of O^T += V^T P^T (its rows are
+// the contraction index).
+//
+// LDS layout: K and V tiles are row-major [key][d] with the 16-byte chunk c of
+// row r stored at chunk c ^ f(r), f(r) = 2 (r & 3) + ((r >> 2) & 1).  Eight
+// consecutive rows at one logical chunk (the K reads) and four consecutive
+// rows at two adjacent chunks (the transposing V reads) both hit distinct
+// banks.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -37,15 +43,7 @@ constexpr int kFwdBM = 128;   // queries per workgroup
 constexpr int kFwdBN = 64;    // keys per K/V tile
 constexpr int kFwdWaves = 4;
 
-// Position of local key kl (0..15) inside its 16-key group of a transposed V
-// row: bits 2 and 3 swapped, so that accumulator register r of lane half h
-// (key 8 (r/4) + 4 h + r % 4) lands at position 8 h + r for r < 8.
-__device__ __forceinline__ int vt_pos16(int kl) {
-  return (kl & 3) | ((kl >> 3) & 1) << 2 | ((kl >> 2) & 1) << 3;
-}
-// 16-byte chunk swizzle of a transposed V row (8 chunks of 8 keys): distinct
-// chunks for 8 consecutive d (MFMA reads) and for d stepping by 8 (writes).
-__device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 
 template <int D, bool CAUSAL, int POLYQ>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict__ Q,
@@ -54,9 +52,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
                                                      uint16_t* __restrict__ O,
                                                      float* __restrict__ LSE, FwdParams p) {
   constexpr int BM = kFwdBM, BN = kFwdBN;
+  constexpr int RB = D * 2;             // bytes per K/V row
   constexpr int KCH = D / 8;            // 16-byte chunks per row
-  constexpr int KT_ELEMS = BN * D;      // one K (or V^T) tile, in bf16 elements
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2][2 * KT_ELEMS];
+  constexpr int TB = BN * RB;           // bytes per K (or V) tile
+  constexpr int NLD = TB / 1024 / kFwdWaves;  // 1 KiB direct loads per wave per tensor
+  static_assert(NLD >= 1, "tile too small");
+  // [stage][K, V] tiles.
+  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TB];
 
   // Grid order: consecutive workgroup ids walk heads first, so with B*Hq a
   // multiple of 8 every tile of a head lands on the same XCD (ids are dealt to
@@ -68,27 +70,24 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
   const int qb = p.nqb - 1 - wg / p.BH;
   const int b = bh / p.Hq, hq = bh % p.Hq;
   const int hk = hq / p.G;
-  const size_t kv_off = ((size_t)b * (p.Hq / p.G) + hk) * (size_t)p.N * D;
-  const uint16_t* __restrict__ Qh = Q + (size_t)bh * p.N * D;
-  const uint16_t* __restrict__ Kh = K + kv_off;
-  const uint16_t* __restrict__ Vh = V + kv_off;
+  const size_t head_elems = (size_t)p.N * D;
+  const uint16_t* Kh = K + ((size_t)b * (p.Hq / p.G) + hk) * head_elems;
+  const uint16_t* Vh = V + ((size_t)b * (p.Hq / p.G) + hk) * head_elems;
+  const uint32_t head_bytes = (uint32_t)(head_elems * 2);
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
   const int n = lane & 31, h = lane >> 5;
   const int q0 = qb * BM;
-  const int qw = q0 + wave * 32;
-  const int qi = qw + n;
+  const int qw = q0 + wave * 32;   // first query of this wave (uniform)
+  const int qi = qw + n;           // this lane's query
 
   // Q fragments (B operand of S^T = K Q^T): k-step t covers d in [16t, 16t+16),
-  // lane half h holds d = 16t + 8h .. +8 of query qi.
+  // lane half h holds d = 16t + 8h .. +8 of query qi (rows past N read as 0).
+  const rsrc_t qr = make_rsrc_uniform(Q + (size_t)bh * head_elems, head_bytes);
   bf16x8 qf[D / 16];
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t) {
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (qi < p.N) v = *(const u32x4*)(Qh + (size_t)qi * D + 16 * t + 8 * h);
-    qf[t] = as_bf16x8(v);
-  }
+  for (int t = 0; t < D / 16; ++t) qf[t] = as_bf16x8(buf_load16(qr, (uint32_t)(qi * RB + 32 * t + 16 * h)));
 
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -101,176 +100,157 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
   const int kend = CAUSAL ? min(p.N, q0 + BM) : p.N;
   const int ntiles = (kend + BN - 1) / BN;
 
-  // ---- staging: K row-major, V transposed --------------------------------
-  // K: chunk c of row r goes to chunk c ^ (r & 7) (conflict-free MFMA reads
-  // of 32 rows at one logical chunk).
-  constexpr int K_PER_T = BN * KCH / 256;
-  u32x4 kreg[K_PER_T];
-  // V: thread owns keys 4g..4g+3 of d-chunk vc (BN/4 * KCH slots).
-  constexpr int V_SLOTS = (BN / 4) * KCH;
-  const bool v_active = tid < V_SLOTS;
-  const int vc = tid % KCH, vg = tid / KCH;
-  u32x4 vreg[4];
-
-  auto load_tile = [&](int kt) {
-    const int k0 = kt * BN;
+  // ---- direct HBM -> LDS staging -------------------------------------------
+  // Load s of this wave fills LDS chunks g = (s*4 + wave)*64 + lane of the
+  // tile: row g / KCH, physical chunk g % KCH, holding logical chunk
+  // (g % KCH) ^ f(row).
+  uint32_t ld_off[NLD];
 #pragma unroll
-    for (int s = 0; s < K_PER_T; ++s) {
-      const int idx = tid + 256 * s;
-      const int r = idx / KCH, c = idx % KCH;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (k0 + r < p.N) v = *(const u32x4*)(Kh + (size_t)(k0 + r) * D + c * 8);
-      kreg[s] = v;
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 4 * vg + j;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (v_active && k0 + r < p.N) v = *(const u32x4*)(Vh + (size_t)(k0 + r) * D + vc * 8);
-      vreg[j] = v;
-    }
-  };
-  auto store_tile = [&](int buf) {
-    uint16_t* ks = smem[buf];
-    uint16_t* vs = smem[buf] + KT_ELEMS;
-#pragma unroll
-    for (int s = 0; s < K_PER_T; ++s) {
-      const int idx = tid + 256 * s;
-      const int r = idx / KCH, c = idx % KCH;
-      *(u32x4*)(ks + r * D + ((c ^ (r & 7)) * 8)) = kreg[s];
-    }
-    if (v_active) {
-      // 4 keys x 8 d -> 8 rows of V^T, 4 keys (8 bytes) each.
-      const int pos = 16 * (vg >> 2) + vt_pos16(4 * (vg & 3));
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = vc * 8 + e;
-        const int w = e >> 1;
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        u32x2 out;
-        out[0] = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], sel);
-        out[1] = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], sel);
-        const int chunk = (pos >> 3) ^ vt_swz(d);
-        *(u32x2*)(vs + d * BN + chunk * 8 + (pos & 7)) = out;
-      }
-    }
-  };
-
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
+  for (int s = 0; s < NLD; ++s) {
+    const int g = (s * kFwdWaves + wave) * 64 + lane;
+    const int row = g / KCH, pc = g % KCH;
+    ld_off[s] = (uint32_t)(row * RB + ((pc ^ swz(row)) * 16));
   }
-  __syncthreads();
+  auto issue_tile = [&](int kt, int stage) {
+    const uint32_t base = (uint32_t)kt * TB;
+    const uint32_t left = head_bytes > base ? head_bytes - base : 0u;
+    const rsrc_t kr = make_rsrc_uniform((const char*)Kh + base, left);
+    const rsrc_t vr = make_rsrc_uniform((const char*)Vh + base, left);
+    char* ks = smem + stage * 2 * TB;
+    char* vs = ks + TB;
+#pragma unroll
+    for (int s = 0; s < NLD; ++s) {
+      lds_dma16(kr, (lds_void*)(ks + (s * kFwdWaves + wave) * 1024), ld_off[s]);
+      lds_dma16(vr, (lds_void*)(vs + (s * kFwdWaves + wave) * 1024), ld_off[s]);
+    }
+  };
+
+  // Per-lane LDS read offsets (stage, sub-block and step offsets are constants).
+  // K (A operand of S^T): row n (+32 sb), logical chunk 2t + h.
+  uint32_t k_off[D / 16];
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) k_off[t] = (uint32_t)(n * RB + (((2 * t + h) ^ swz(n)) * 16));
+  // V (A operand of O^T = V^T P^T) through transposing reads: in 16-lane group
+  // gq = lane / 16, lane j points at row 4 h + j / 4 (+ 32 sb + 16 u + 8 rd)
+  // and d = 32 db + 16 (gq & 1) + 4 (j & 3).
+  uint32_t v_off[D / 32];
+  {
+    const int j = lane & 15, gq = lane >> 4;
+    const int row = 4 * h + (j >> 2);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int c = 4 * db + 2 * (gq & 1) + ((j & 3) >> 1);
+      v_off[db] = (uint32_t)(row * RB + ((c ^ swz(row)) * 16) + (j & 1) * 8);
+    }
+  }
+
+  if (ntiles > 0) issue_tile(0, 0);
 
   for (int kt = 0; kt < ntiles; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < ntiles) load_tile(kt + 1);
+    const int stage = kt & 1;
+    wait_vmcnt<0>();
+    __syncthreads();  // tile kt is in LDS; everyone is done with tile kt-1
+    if (kt + 1 < ntiles) issue_tile(kt + 1, stage ^ 1);
     const int k0 = kt * BN;
     // Tiles wholly above this wave's diagonal contribute nothing.
-    const bool skip = CAUSAL && (k0 > qw + 31);
-    if (!skip) {
-      const uint16_t* ks = smem[buf];
-      const uint16_t* vs = smem[buf] + KT_ELEMS;
-      // S^T for the two 32-key halves of the tile.
-      f32x16 s[2];
+    if (CAUSAL && k0 > qw + 31) continue;
+    const char* ks = smem + stage * 2 * TB;
+    const char* vs = ks + TB;
+
+    // S^T for the two 32-key halves of the tile.
+    f32x16 s[2];
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
+    for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[sb][r] = 0.f;
-        const int kr = 32 * sb + n;  // key row this lane feeds (A operand)
+      for (int r = 0; r < 16; ++r) s[sb][r] = 0.f;
 #pragma unroll
-        for (int t = 0; t < D / 16; ++t) {
-          const int c = (2 * t + h) ^ (kr & 7);
-          const bf16x8 a = as_bf16x8(*(const u32x4*)(ks + kr * D + c * 8));
-          s[sb] = mfma32(a, qf[t], s[sb]);
-        }
+      for (int t = 0; t < D / 16; ++t) {
+        const bf16x8 a = as_bf16x8(*(const u32x4*)(ks + sb * 32 * RB + k_off[t]));
+        s[sb] = mfma32(a, qf[t], s[sb]);
       }
-      // Mask keys past the end and, under causal, keys after the query.
-      const bool need_mask = (k0 + BN > p.N) || (CAUSAL && (k0 + BN - 1 > qw));
-      if (need_mask) {
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + 32 * sb + 8 * (r >> 2) + 4 * h + (r & 3);
-            const bool dead = key >= p.N || (CAUSAL && key > qi);
-            if (dead) s[sb][r] = -__builtin_inff();
-          }
-      }
-      // Row max of this tile (both halves end with the full-row value).
-      float mx = -__builtin_inff();
+    }
+    // Mask keys past the end and, under causal, keys after the query.
+    // Register r of half sb holds key k0 + 32 sb + 8 (r/4) + 4 h + r % 4.
+    if ((k0 + BN > p.N) || (CAUSAL && (k0 + BN - 1 > qw))) {
+      keep_branch();
+      int lim = p.N - 1 - k0 - 4 * h;
+      if (CAUSAL) lim = min(lim, qi - k0 - 4 * h);
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(s[sb][r], s[sb][r + 1]));
-      mx = __builtin_fmaxf(mx, xhalf(mx));
-      const float m_new = __builtin_fmaxf(m_ref, mx * p.c);
-      // Conditional rescale: taken by the whole wave when any of its rows'
-      // max grew by more than tau; each row then moves to its own new max.
-      const bool grow = m_new > m_ref + kTau;
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-        const float alpha = (m_new == -__builtin_inff()) ? 1.f : exp2_hw(m_ref - m_new);
-        l_part *= alpha;
+        for (int r = 0; r < 16; ++r)
+          if (32 * sb + 8 * (r >> 2) + (r & 3) > lim) s[sb][r] = -__builtin_inff();
+    }
+    // Row max of this tile (both halves end with the full-row value).
+    float mx = __builtin_fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-        for (int i = 0; i < D / 32; ++i)
+    for (int r = 2; r < 16; r += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(s[0][r], s[0][r + 1]));
 #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
-        m_ref = m_new;
+    for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(s[1][r], s[1][r + 1]));
+    mx = xhalf_max(mx);
+    const float m_new = __builtin_fmaxf(m_ref, mx * p.c);
+    // Conditional rescale: taken by the whole wave when any of its rows' max
+    // grew by more than tau; each row then moves to its own new max.
+    if (__builtin_amdgcn_ballot_w64(m_new > m_ref + kTau) != 0) {
+      const float alpha = (m_new == -__builtin_inff()) ? 1.f : exp2_hw(m_ref - m_new);
+      l_part *= alpha;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+      m_ref = m_new;
+    }
+    const float msub = (m_ref == -__builtin_inff()) ? 0.f : m_ref;
+    // P^T = exp2(S^T c - m_ref), row sum, and bf16 B operands.
+    bf16x8 pb[2][2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float x = __builtin_fmaf(s[sb][r], p.c, -msub);
+        const float e = ((r & 3) < POLYQ) ? exp2_poly(x) : exp2_hw(x);
+        s[sb][r] = e;
+        l_part += e;
       }
-      const float msub = (m_ref == -__builtin_inff()) ? 0.f : m_ref;
-      // P^T = exp2(S^T c - m_ref), row sum, and bf16 B operands.
-      bf16x8 pb[2][2];
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
+      for (int u = 0; u < 2; ++u) {
+        u32x4 w;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float x = __builtin_fmaf(s[sb][r], p.c, -msub);
-          const float e = ((r & 3) < POLYQ) ? exp2_poly(x) : exp2_hw(x);
-          s[sb][r] = e;
-          l_part += e;
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          u32x4 w;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) w[j] = pack_bf16x2(s[sb][8 * u + 2 * j], s[sb][8 * u + 2 * j + 1]);
-          pb[sb][u] = as_bf16x8(w);
-        }
-      }
-      // O^T += V^T P^T.
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const int d = 32 * db + n;
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int chunk = (2 * (2 * sb + u) + h) ^ vt_swz(d);
-            const bf16x8 a = as_bf16x8(*(const u32x4*)(vs + d * BN + chunk * 8));
-            oacc[db] = mfma32(a, pb[sb][u], oacc[db]);
-          }
+        for (int j = 0; j < 4; ++j) w[j] = pack_bf16x2(s[sb][8 * u + 2 * j], s[sb][8 * u + 2 * j + 1]);
+        pb[sb][u] = as_bf16x8(w);
       }
     }
-    if (kt + 1 < ntiles) store_tile(buf ^ 1);
-    __syncthreads();
-  }
-
-  // Final correction: O = O / l, LSE = (m_ref + log2 l) ln 2.
-  const float l_tot = l_part + xhalf(l_part);
-  if (qi < p.N) {
-    const float inv = 1.f / l_tot;
-    uint16_t* Oq = O + ((size_t)bh * p.N + qi) * D;
+    // O^T += V^T P^T: A operand = keys 32 sb + 16 u + 8 rd + 4 h + (0..3) of
+    // column d = 32 db + n, two transposing reads per operand.
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 w;
-        w[0] = pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv);
-        w[1] = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
-        *(u32x2*)(Oq + 32 * db + 8 * g + 4 * h) = w;
-      }
-    if (h == 0) LSE[(size_t)bh * p.N + qi] = (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2;
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const char* base = vs + (32 * sb + 16 * u) * RB + v_off[db];
+          const u32x2 lo = lds_read_tr16((const lds_void*)base);
+          const u32x2 hi = lds_read_tr16((const lds_void*)(base + 8 * RB));
+          const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+          oacc[db] = mfma32(as_bf16x8(a), pb[sb][u], oacc[db]);
+        }
   }
+
+  // Final correction: O = O / l, LSE = (m_ref + log2 l) ln 2.  Rows past N are
+  // dropped by the buffer range.
+  const float l_tot = xhalf_sum(l_part);
+  const float inv = 1.f / l_tot;
+  const rsrc_t orr = make_rsrc_uniform(O + (size_t)bh * head_elems, head_bytes);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      u32x2 w;
+      w[0] = pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv);
+      w[1] = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+      buf_store8(orr, (uint32_t)(qi * RB + (32 * db + 8 * g + 4 * h) * 2), w);
+    }
+  if (h == 0 && qi < p.N) LSE[(size_t)bh * p.N + qi] = (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2;
 }
 
 template <int D, bool CAUSAL, int POLYQ>

@@ -51,7 +51,9 @@ struct BwdArgs {
 struct BwdLayout {
   size_t dq_acc;    // fp32 [B][Hq][N][D]
   size_t delta;     // fp32 [B][Hq][N]
-  size_t counters;  // int32 [B][Hq][query tiles] (deterministic only)
+  size_t lse2;      // fp32 [B][Hq][N], LSE * log2(e)
+  size_t counters;  // int32 [B][Hq][query steps][waves] (deterministic only)
+  size_t give_up;   // int32 flag (deterministic only)
   size_t total;
 };
 

@@ -114,17 +114,20 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
  * problem and workspace, they are exactly fa_bwd.  Arguments have the
  * meaning given for fa_bwd; each stage checks the arguments it uses and
  * returns the same codes.
- *   fa_bwd_preprocess: Delta_i = rowsum(dO * O) into the workspace, and
- *     clears the workspace's fp32 dQ accumulator (and order counters).
- *   fa_bwd_main: recomputes P tile by tile and forms dK, dV (written to dk,
- *     dv) and the unscaled dQ sums (accumulated in the workspace).
+ *   fa_bwd_preprocess: Delta_i = rowsum(dO * O) and LSE_i * log2(e) into the
+ *     workspace, and clears the workspace's fp32 dQ accumulator (and order
+ *     counters).
+ *   fa_bwd_main: recomputes P tile by tile from q, k and the workspace's
+ *     LSE * log2(e), and forms dK, dV (written to dk, dv) and the unscaled
+ *     dQ sums (accumulated in the workspace).
  *   fa_bwd_dq_convert: dq = bf16(scale * accumulated dQ).
  */
-int fa_bwd_preprocess(const void* o, const void* dout, int B, int Hq, int Hkv, int N, int D,
-                      void* workspace, size_t workspace_bytes, int deterministic, void* stream);
-int fa_bwd_main(const void* q, const void* k, const void* v, const float* lse, const void* dout,
-                void* dk, void* dv, int B, int Hq, int Hkv, int N, int D, int causal, float scale,
-                void* workspace, size_t workspace_bytes, int deterministic, void* stream);
+int fa_bwd_preprocess(const void* o, const void* dout, const float* lse, int B, int Hq, int Hkv,
+                      int N, int D, void* workspace, size_t workspace_bytes, int deterministic,
+                      void* stream);
+int fa_bwd_main(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv,
+                int B, int Hq, int Hkv, int N, int D, int causal, float scale, void* workspace,
+                size_t workspace_bytes, int deterministic, void* stream);
 int fa_bwd_dq_convert(void* dq, int B, int Hq, int Hkv, int N, int D, float scale,
                       void* workspace, size_t workspace_bytes, int deterministic, void* stream);
 

@@ -103,14 +103,16 @@ def test_bwd_rejects(kw, code):
 
 def test_bwd_stages_reject():
     ws = 1 << 30
-    assert fa.fa_bwd_preprocess(None, DO, 1, 2, 2, 64, 64, WS, ws, 0, None) == fa.FA_ERR_INVALID
-    assert fa.fa_bwd_preprocess(O, DO, 1, 2, 2, 64, 64, WS, 16, 0, None) == fa.FA_ERR_WORKSPACE
-    assert fa.fa_bwd_preprocess(O, DO + 8, 1, 2, 2, 64, 64, WS, ws, 0, None) == fa.FA_ERR_ALIGN
-    assert fa.fa_bwd_main(Q, K, V, L, DO, DK, DV, 1, 2, 2, 64, 96, 1, 0.1, WS, ws, 0, None) == \
+    assert fa.fa_bwd_preprocess(None, DO, L, 1, 2, 2, 64, 64, WS, ws, 0, None) == fa.FA_ERR_INVALID
+    assert fa.fa_bwd_preprocess(O, DO, None, 1, 2, 2, 64, 64, WS, ws, 0, None) == fa.FA_ERR_INVALID
+    assert fa.fa_bwd_preprocess(O, DO, L, 1, 2, 2, 64, 64, WS, 16, 0, None) == fa.FA_ERR_WORKSPACE
+    assert fa.fa_bwd_preprocess(O, DO + 8, L, 1, 2, 2, 64, 64, WS, ws, 0, None) == fa.FA_ERR_ALIGN
+    assert fa.fa_bwd_preprocess(O, DO, WS, 1, 2, 2, 64, 64, WS, ws, 0, None) == fa.FA_ERR_INVALID
+    assert fa.fa_bwd_main(Q, K, V, DO, DK, DV, 1, 2, 2, 64, 96, 1, 0.1, WS, ws, 0, None) == \
         fa.FA_ERR_UNSUPPORTED
-    assert fa.fa_bwd_main(Q, K, V, L, DO, DK, DK, 1, 2, 2, 64, 64, 1, 0.1, WS, ws, 0, None) == \
+    assert fa.fa_bwd_main(Q, K, V, DO, DK, DK, 1, 2, 2, 64, 64, 1, 0.1, WS, ws, 0, None) == \
         fa.FA_ERR_INVALID
-    assert fa.fa_bwd_main(Q, K, V, L, DO, K, DV, 1, 2, 2, 64, 64, 1, 0.1, WS, ws, 0, None) == \
+    assert fa.fa_bwd_main(Q, K, V, DO, K, DV, 1, 2, 2, 64, 64, 1, 0.1, WS, ws, 0, None) == \
         fa.FA_ERR_INVALID
     assert fa.fa_bwd_dq_convert(WS, 1, 2, 2, 64, 64, 0.1, WS, ws, 0, None) == fa.FA_ERR_INVALID
     assert fa.fa_bwd_dq_convert(DQ + 2, 1, 2, 2, 64, 64, 0.1, WS, ws, 0, None) == fa.FA_ERR_ALIGN
