@@ -3,7 +3,7 @@
 
 One step = the whole path over one batch: the forward (fa_fwd: O and LSE)
 followed by the backward's three stages (fa_bwd_preprocess, fa_bwd_main,
-fa_bwd_dq_convert: dQ, dK, dV), at B=2, H=16, N=8192, D=128, causal, bf16,
+fa_bwd_dq: dK, dV, dQ), at B=2, H=16, N=8192, D=128, causal, bf16,
 on seeded synthetic N(0,1) inputs already resident in device memory.
 
 FLOPs per step follow the usual attention convention: forward 4*B*H*N^2*D,
@@ -33,6 +33,8 @@ KERNEL_SOURCES = {
                    "exact_attention_98_amd/csrc/common.hpp"],
     "bwd_main_kernel": ["exact_attention_98_amd/csrc/bwd_kernels.hip",
                         "exact_attention_98_amd/csrc/common.hpp"],
+    "bwd_dq_kernel": ["exact_attention_98_amd/csrc/bwd_kernels.hip",
+                      "exact_attention_98_amd/csrc/common.hpp"],
 }
 
 
@@ -56,6 +58,8 @@ def load_traffic(kernel: str):
         return None
     with open(path) as f:
         rec = json.load(f)
+    if kernel == "bwd_main_kernel" and not rec.get("kernel", "").endswith("fixed-order dQ mode)"):
+        return None
     if rec.get("source_sha256") != source_digest(kernel):
         return None
     return rec.get("hbm_bytes_per_launch")
@@ -82,10 +86,13 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--deterministic", action="store_true",
-                    help="fixed-order dQ accumulation in the backward")
+    ap.add_argument("--dq-mode", choices=["fixed", "atomic"], default="fixed",
+                    help="backward dQ: fixed-order pass (deterministic, default) or atomic adds")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=4)
+    ap.add_argument("--cpu-heads", type=int, default=16)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run a plain device-to-device copy of MIB MiB (read MIB, write MIB) "
+                         "so that memory-traffic counters can be scaled against known bytes")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -113,7 +120,7 @@ def main() -> int:
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    det = 1 if args.deterministic else 0
+    det = 1 if args.dq_mode == "fixed" else 0
     ws_bytes = fa.fa_bwd_workspace_size(B, Hq, Hkv, N, D, det)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -126,7 +133,8 @@ def main() -> int:
         if rc != 0:
             raise RuntimeError(f"{what}: {fa.fa_strerror(rc)}")
 
-    names = ["fwd_kernel", "bwd_pre_kernel", "bwd_main_kernel", "bwd_dq_convert_kernel"]
+    dq_name = "bwd_dq_kernel" if det else "bwd_dq_convert_kernel"
+    names = ["fwd_kernel", "bwd_pre_kernel", "bwd_main_kernel", dq_name]
 
     def step(ev):
         ev[0].record(stream)
@@ -139,12 +147,22 @@ def main() -> int:
         check(fa.fa_bwd_main(P["q"], P["k"], P["v"], P["do"], P["dk"], P["dv"], B, Hq, Hkv, N, D,
                              1, w.scale, P["ws"], ws_bytes, det, sh), "fa_bwd_main")
         ev[3].record(stream)
-        check(fa.fa_bwd_dq_convert(P["dq"], B, Hq, Hkv, N, D, w.scale, P["ws"], ws_bytes, det, sh),
-              "fa_bwd_dq_convert")
+        check(fa.fa_bwd_dq(P["q"], P["k"], P["v"], P["do"], P["dq"], B, Hq, Hkv, N, D, 1, w.scale,
+                           P["ws"], ws_bytes, det, sh), "fa_bwd_dq")
         ev[4].record(stream)
 
     def events():
         return [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+
+    if args.copy_calibration > 0:
+        nbytes = args.copy_calibration << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"copy calibration: {args.copy_calibration} MiB read + written")
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -173,13 +191,18 @@ def main() -> int:
     f_fwd, f_bwd = w.flops_fwd(), w.flops_bwd()
     value = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
     fwd_tf = f_fwd / (per_kernel["fwd_kernel"] * 1e-3) / 1e12
-    bwd_ms = per_kernel["bwd_pre_kernel"] + per_kernel["bwd_main_kernel"] + \
-        per_kernel["bwd_dq_convert_kernel"]
+    bwd_ms = per_kernel["bwd_pre_kernel"] + per_kernel["bwd_main_kernel"] + per_kernel[dq_name]
     bwd_tf = f_bwd / (bwd_ms * 1e-3) / 1e12
 
-    # Dominant kernel and its roofline (bf16 MFMA bound: attention is a dense contraction).
-    algo_flops = {"fwd_kernel": f_fwd, "bwd_main_kernel": f_bwd}
-    dom = max(algo_flops, key=lambda n: per_kernel[n])
+    # Dominant kernel and its roofline (bf16 MFMA bound: attention is a dense
+    # contraction).  Algorithmic FLOPs per launch: the forward does its 2
+    # products (f_fwd); the backward's 5 products are f_bwd, of which the main
+    # kernel does 4 (S, dP, dV, dK) in fixed-order mode and all 5 in atomic
+    # mode.  The fixed-order dQ kernel's algorithmic share is the dQ product
+    # (1 of 5); its S and dP recompute is overhead, not algorithmic work.
+    algo_flops = {"fwd_kernel": f_fwd, "bwd_main_kernel": f_bwd * (0.8 if det else 1.0),
+                  dq_name: f_bwd * 0.2 if det else 0.0}
+    dom = max(("fwd_kernel", "bwd_main_kernel", dq_name), key=lambda n: per_kernel[n])
     achieved = algo_flops[dom] / (per_kernel[dom] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -194,7 +217,7 @@ def main() -> int:
         "data": "synthetic (seeded N(0,1) bf16 Q, K, V, dO)",
         "config": {"workload": "attention forward+backward, B2 Hq16 Hkv16 N8192 D128 causal",
                    "B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "D": D, "causal": True,
-                   "dq_accumulation": "deterministic" if det else "atomic",
+                   "dq_accumulation": "fixed-order (deterministic)" if det else "atomic",
                    "flops_per_step": f_fwd + f_bwd},
         "roofline": roofline,
         "fwd": {"tflops": round(fwd_tf, 1), "frac_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
@@ -205,6 +228,29 @@ def main() -> int:
                                for n in names[1:]}},
         "host_wall_ms_per_step": round(wall / args.steps * 1e3, 4),
     }
+    # The other dQ mode, timed on the same inputs for comparison.
+    odet = 1 - det
+    ows_bytes = fa.fa_bwd_workspace_size(B, Hq, Hkv, N, D, odet)
+    ows = torch.empty(ows_bytes, dtype=torch.uint8, device=dev)
+
+    def obwd():
+        check(fa.fa_bwd(P["q"], P["k"], P["v"], P["o"], P["lse"], P["do"], P["dq"], P["dk"], P["dv"],
+                        B, Hq, Hkv, N, D, 1, w.scale, ows.data_ptr(), ows_bytes, odet, sh), "fa_bwd")
+
+    for _ in range(2):
+        obwd()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(5):
+        obwd()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    o_ms = e0.elapsed_time(e1) / 5
+    out["bwd_other_mode"] = {"dq_accumulation": "atomic" if det else "fixed-order (deterministic)",
+                             "us": round(o_ms * 1e3, 1),
+                             "tflops": round(f_bwd / (o_ms * 1e-3) / 1e12, 1)}
+    del ows
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_heads} heads")
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)

@@ -15,7 +15,7 @@ import ctypes
 import os
 
 __all__ = ["fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_workspace_size", "fa_bwd_preprocess",
-           "fa_bwd_main", "fa_bwd_dq_convert", "fa_strerror", "forward", "backward", "FaError",
+           "fa_bwd_main", "fa_bwd_dq", "fa_strerror", "forward", "backward", "FaError",
            "library_path", "load"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -31,7 +31,7 @@ FA_ERR_HIP = -5
 FA_ERR_TOO_LARGE = -6
 
 EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_workspace_size", "fa_bwd_preprocess",
-            "fa_bwd_main", "fa_bwd_dq_convert", "fa_strerror")
+            "fa_bwd_main", "fa_bwd_dq", "fa_strerror")
 
 
 class FaError(RuntimeError):
@@ -67,8 +67,8 @@ def load():
     lib.fa_bwd_preprocess.restype = ci
     lib.fa_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp, sz, ci, vp]
     lib.fa_bwd_main.restype = ci
-    lib.fa_bwd_dq_convert.argtypes = [vp, ci, ci, ci, ci, ci, cf, vp, sz, ci, vp]
-    lib.fa_bwd_dq_convert.restype = ci
+    lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp, sz, ci, vp]
+    lib.fa_bwd_dq.restype = ci
     lib.fa_strerror.argtypes = [ci]
     lib.fa_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -107,10 +107,10 @@ def fa_bwd_main(q, k, v, dout, dk, dv, B, Hq, Hkv, N, D, causal, scale, workspac
                               workspace, workspace_bytes, int(deterministic), stream)
 
 
-def fa_bwd_dq_convert(dq, B, Hq, Hkv, N, D, scale, workspace, workspace_bytes, deterministic,
-                      stream) -> int:
-    return load().fa_bwd_dq_convert(dq, B, Hq, Hkv, N, D, float(scale), workspace,
-                                    workspace_bytes, int(deterministic), stream)
+def fa_bwd_dq(q, k, v, dout, dq, B, Hq, Hkv, N, D, causal, scale, workspace, workspace_bytes,
+              deterministic, stream) -> int:
+    return load().fa_bwd_dq(q, k, v, dout, dq, B, Hq, Hkv, N, D, int(causal), float(scale),
+                            workspace, workspace_bytes, int(deterministic), stream)
 
 
 def fa_strerror(status: int) -> str:

@@ -6,9 +6,13 @@
 //   S  = Q K^T              P  = exp2(S c - LSE log2 e)
 //   dP = dO V^T             dS = P o (dP - Delta),  Delta_i = dO_i . O_i
 //   dV += P^T dO            dK += dS^T Q            dQ += dS K
-// dK and dV of a key tile are owned by one workgroup; dQ is accumulated in an
-// fp32 workspace either with atomics or, in deterministic mode, in a fixed
-// order (danialwang explainer, sections 05-06).
+// dK and dV of a key tile are owned by one workgroup.  dQ has two modes
+// (danialwang explainer, sections 05-06):
+//   atomic        the main kernel also forms dQ += dS K for its key tile and
+//                 adds it into an fp32 workspace with atomics;
+//   fixed order   a separate kernel owns each query tile, walks the key tiles
+//                 in ascending order recomputing S, dP and dS, and writes dQ
+//                 once: no atomics, so the result is bit-identical run to run.
 //
 // Layout choices.  S is computed with keys as the MFMA accumulator's column
 // (lane) index.  Its accumulator registers are then, unchanged, the A operand
@@ -20,10 +24,10 @@
 // contracts over keys, so dS^T takes one trip through LDS and is read back
 // with the same transposing read.
 //
-// Pipeline: Q, dO, LSE*log2e and Delta of query step i+1 are copied from HBM
-// straight into LDS (buffer_load ... lds) while step i computes; the dQ
-// product of step i runs during step i+1, after the one barrier per step that
-// publishes step i's dS^T.
+// Pipeline (main kernel): Q, dO, LSE*log2e and Delta of query step i+1 are
+// copied from HBM straight into LDS (buffer_load ... lds) while step i
+// computes; in atomic mode the dQ product of step i runs during step i+1,
+// after the one barrier per step that publishes step i's dS^T.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -32,7 +36,6 @@ namespace {
 
 constexpr int kBwdBN = 128;    // keys per workgroup (32 per wave)
 constexpr int kBwdWaves = 4;
-constexpr int kMaxSpin = 1 << 20;  // bound on a deterministic-order wait
 
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 
@@ -45,19 +48,17 @@ struct BwdParams {
   float* dq_acc;   // fp32 [B][Hq][N][D]
   float* delta;    // fp32 [B][Hq][N]
   float* lse2;     // fp32 [B][Hq][N]
-  int* counters;   // int32 [B][Hq][nqs][waves] (deterministic only)
-  int* give_up;    // int32: set once a wait has timed out (deterministic only)
 };
 
 // ---------------------------------------------------------------------------
 // Preprocess: Delta_i = sum_d dO[i,d] O[i,d] (fp32), LSE_i * log2(e), and
-// zero the dQ accumulator and the order counters.  A row of D bf16 is read by
-// D/8 lanes (16 B each).
+// (atomic mode) zero the dQ accumulator.  A row of D bf16 is read by D/8
+// lanes (16 B each).
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict__ O,
                                                       const uint16_t* __restrict__ dO,
                                                       const float* __restrict__ LSE,
-                                                      BwdParams p, int rows, int ncount) {
+                                                      BwdParams p, int rows) {
   constexpr int LPR = D / 8;                 // lanes per row
   constexpr int RPB = 256 / LPR;             // rows per block
   const int tid = threadIdx.x;
@@ -72,9 +73,11 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
       acc += bf16_bits_to_float(a[j] & 0xffffu) * bf16_bits_to_float(b[j] & 0xffffu);
       acc += bf16_bits_to_float(a[j] >> 16) * bf16_bits_to_float(b[j] >> 16);
     }
-    float4* z = (float4*)(p.dq_acc + (size_t)row * D + c * 8);
-    z[0] = make_float4(0.f, 0.f, 0.f, 0.f);
-    z[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (p.dq_acc) {
+      float4* z = (float4*)(p.dq_acc + (size_t)row * D + c * 8);
+      z[0] = make_float4(0.f, 0.f, 0.f, 0.f);
+      z[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
   }
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
@@ -82,17 +85,15 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
     p.delta[row] = acc;
     p.lse2[row] = LSE[row] * kLog2e;
   }
-  const int gid = blockIdx.x * 256 + tid;
-  if (p.counters && gid < ncount) p.counters[gid] = 0;
-  if (p.give_up && gid == 0) *p.give_up = 0;
 }
 
 // ---------------------------------------------------------------------------
-// Main backward kernel.  Workgroup = (batch, K/V head, key tile of 128);
-// wave w owns keys 32w..32w+31 of the tile.  Query steps of QS = 4096 / D
-// queries (32 for D = 128, 64 for D = 64) are walked from the last one down to
-// the first that meets the tile's diagonal, for each of the G query heads.
-template <int D, bool CAUSAL, bool DET>
+// Main backward kernel: dK, dV and, with FUSED_DQ, atomic dQ.  Workgroup =
+// (batch, K/V head, key tile of 128); wave w owns keys 32w..32w+31 of the
+// tile.  Query steps of QS = 4096 / D queries (32 for D = 128, 64 for D = 64)
+// are walked from the last one down to the first that meets the tile's
+// diagonal, for each of the G query heads.
+template <int D, bool CAUSAL, bool FUSED_DQ>
 __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
@@ -110,9 +111,10 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
   static_assert(NQB * ND == kBwdWaves, "one dQ output block per wave");
   static_assert(NLD >= 1, "step tile too small");
 
-  // Per stage: Q tile, dO tile, 256 B of LSE*log2e, 256 B of Delta.
+  // Per stage: Q tile, dO tile, 256 B of LSE*log2e, 256 B of Delta; then (atomic
+  // mode) two dS^T buffers.
   constexpr int STAGE = 2 * TB + 512;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE + 2 * DSB];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE + (FUSED_DQ ? 2 * DSB : 0)];
   char* const ds_buf = smem + 2 * STAGE;
 
   const int Hkv = p.Hq / p.G;
@@ -146,8 +148,8 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
   // lane (d, h) holds K[k0 + 16t + 8(i/4) + 4h + i%4][d] in slot i, matching
   // the transposing read of dS^T.
   const int dq_qb = wave / ND, dq_db = wave % ND;
-  bf16x8 kT[BN / 16];
-  {
+  bf16x8 kT[FUSED_DQ ? BN / 16 : 1];
+  if constexpr (FUSED_DQ) {
     const int d = 32 * dq_db + n;
     const uint16_t* Kh = K + kv_head;
 #pragma unroll
@@ -247,6 +249,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
 
   // dQ block of step i (dS^T of that step in ds buffer i & 1).
   auto dq_step = [&](int i) {
+    if constexpr (FUSED_DQ) {
     const int hq = step_head(i);
     const int q0 = step_qs(i) * QS;
     const char* dsb = ds_buf + (i & 1) * DSB;
@@ -266,46 +269,10 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
     float* dqh = p.dq_acc + qh * D;
     const int qrow0 = q0 + 32 * dq_qb + 4 * h;
     const int d = 32 * dq_db + n;
-    if (!DET) {
-      const rsrc_t dqr = make_rsrc_uniform(dqh, (uint32_t)(head_elems * 4));
+    const rsrc_t dqr = make_rsrc_uniform(dqh, (uint32_t)(head_elems * 4));
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        buf_atomic_add(dqr, (uint32_t)(((qrow0 + 8 * (r >> 2) + (r & 3)) * D + d) * 4), acc[r]);
-    } else {
-      // Fixed order: the key tiles add into this (query step, d block) in
-      // ascending tile order.  The wave waits (bounded) for its turn, adds
-      // with coherent loads and stores, then publishes the next turn.
-      int* cnt = p.counters + (((size_t)b * p.Hq + hq) * p.nqs + step_qs(i)) * kBwdWaves + wave;
-      // A wait that runs past kMaxSpin polls sets give_up, after which no
-      // wave of the call waits again and the remaining adds are atomic (still
-      // correct, no longer ordered), so a call ends in bounded time.
-      bool late = false;
-      int spins = 0;
-      while (__hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != kb) {
-        if (spins >= kMaxSpin ||
-            __hip_atomic_load(p.give_up, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
-          late = true;
-          if (lane == 0) __hip_atomic_store(p.give_up, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-        ++spins;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qg = qrow0 + 8 * (r >> 2) + (r & 3);
-        if (qg < p.N) {
-          float* ptr = dqh + (size_t)qg * D + d;
-          if (late) {
-            atomicAdd(ptr, acc[r]);
-          } else {
-            const float old = __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(ptr, old + acc[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-        }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      if (lane == 0) __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int r = 0; r < 16; ++r)
+      buf_atomic_add(dqr, (uint32_t)(((qrow0 + 8 * (r >> 2) + (r & 3)) * D + d) * 4), acc[r]);
     }
   };
 
@@ -316,7 +283,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
     wait_vmcnt<0>();
     __syncthreads();  // step i inputs are in LDS; dS^T of step i-1 is complete
     if (i + 1 < nsteps) issue_step(i + 1, stage ^ 1);
-    if (i > 0) dq_step(i - 1);
+    if (FUSED_DQ && i > 0) dq_step(i - 1);
 
     const int q0 = step_qs(i) * QS;
     const char* st = smem + stage * STAGE;
@@ -386,6 +353,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
           dk_acc[db] = mfma32(dsa[u], as_bf16x8(qbv), dk_acc[db]);
         }
       // dS^T -> LDS: lane (key 32 wave + n) writes queries 32qb + 8g + 4h .. +4.
+      if constexpr (FUSED_DQ)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int col = 32 * qb + 8 * g4 + 4 * h;
@@ -397,7 +365,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
       }
     }
   }
-  if (nsteps > 0) {
+  if (FUSED_DQ && nsteps > 0) {
     __syncthreads();
     dq_step(nsteps - 1);
   }
@@ -420,6 +388,184 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Fixed-order dQ kernel.  Workgroup = (batch, query head, 128 queries), 4
+// waves of 32 queries.  K/V tiles of 64 keys are copied straight into LDS
+// (double-buffered, one barrier per tile) and walked in ascending order:
+//   S^T  = K Q^T,  dP^T = V dO^T      (Q, dO resident as B operands)
+//   P^T  = exp2(S^T c - LSE log2 e),  dS^T = P^T o (dP^T - Delta)
+//   dQ^T += K^T dS^T                  (K^T by transposing reads of the K tile,
+//                                      dS^T straight from the accumulators)
+// and dQ = scale * dQ^T is written once, so the sum order is fixed.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t* __restrict__ Q,
+                                                        const uint16_t* __restrict__ K,
+                                                        const uint16_t* __restrict__ V,
+                                                        const uint16_t* __restrict__ dO,
+                                                        uint16_t* __restrict__ dQ, BwdParams p,
+                                                        int nqb) {
+  constexpr int BM = 128, BN = 64, NW = 4;
+  constexpr int RB = D * 2;
+  constexpr int KCH = D / 8;
+  constexpr int TB = BN * RB;
+  constexpr int NLD = TB / 1024 / NW;
+  static_assert(NLD >= 1, "tile too small");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TB];  // [stage][K, V]
+
+  const int BH = p.B * p.Hq;
+  const int wg = blockIdx.x;
+  const int bh = wg % BH;
+  const int qb = nqb - 1 - wg / BH;
+  const int b = bh / p.Hq, hq = bh % p.Hq;
+  const int hk = hq / p.G;
+  const size_t head_elems = (size_t)p.N * D;
+  const uint32_t head_bytes = (uint32_t)(head_elems * 2);
+  const uint16_t* Kh = K + ((size_t)b * (p.Hq / p.G) + hk) * head_elems;
+  const uint16_t* Vh = V + ((size_t)b * (p.Hq / p.G) + hk) * head_elems;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int n = lane & 31, h = lane >> 5;
+  const int q0 = qb * BM;
+  const int qw = q0 + wave * 32;
+  const int qi = qw + n;
+
+  // Q and dO fragments (B operands; k-step t: d = 16t + 8h .. +8 of query qi).
+  const rsrc_t qr = make_rsrc_uniform(Q + (size_t)bh * head_elems, head_bytes);
+  const rsrc_t dr = make_rsrc_uniform(dO + (size_t)bh * head_elems, head_bytes);
+  bf16x8 qf[D / 16], df[D / 16];
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+    qf[t] = as_bf16x8(buf_load16(qr, (uint32_t)(qi * RB + 32 * t + 16 * h)));
+    df[t] = as_bf16x8(buf_load16(dr, (uint32_t)(qi * RB + 32 * t + 16 * h)));
+  }
+  // Row constants of this lane's query (rows past N read as 0; their results
+  // are dropped at the store).
+  const rsrc_t lr = make_rsrc_uniform(p.lse2 + (size_t)bh * p.N, (uint32_t)p.N * 4u);
+  const rsrc_t er = make_rsrc_uniform(p.delta + (size_t)bh * p.N, (uint32_t)p.N * 4u);
+  const float lse2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lr, (uint32_t)qi * 4u, 0, 0));
+  const float dlt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(er, (uint32_t)qi * 4u, 0, 0));
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+
+  const int kend = CAUSAL ? min(p.N, q0 + BM) : p.N;
+  const int ntiles = (kend + BN - 1) / BN;
+
+  uint32_t ld_off[NLD];
+#pragma unroll
+  for (int s = 0; s < NLD; ++s) {
+    const int g = (s * NW + wave) * 64 + lane;
+    const int row = g / KCH, pc = g % KCH;
+    ld_off[s] = (uint32_t)(row * RB + ((pc ^ swz(row)) * 16));
+  }
+  auto issue_tile = [&](int kt, int stage) {
+    const uint32_t base = (uint32_t)kt * TB;
+    const uint32_t left = head_bytes > base ? head_bytes - base : 0u;
+    const rsrc_t kr = make_rsrc_uniform((const char*)Kh + base, left);
+    const rsrc_t vr = make_rsrc_uniform((const char*)Vh + base, left);
+    char* ks = smem + stage * 2 * TB;
+#pragma unroll
+    for (int s = 0; s < NLD; ++s) {
+      lds_dma16(kr, (lds_void*)(ks + (s * NW + wave) * 1024), ld_off[s]);
+      lds_dma16(vr, (lds_void*)(ks + TB + (s * NW + wave) * 1024), ld_off[s]);
+    }
+  };
+  // Row reads (A operands of S^T and dP^T): row n (+32 sb), logical chunk 2t + h.
+  uint32_t a_off[D / 16];
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) a_off[t] = (uint32_t)(n * RB + (((2 * t + h) ^ swz(n)) * 16));
+  // Transposing reads of K (A operand K^T of dQ^T): in 16-lane group gq, lane j
+  // points at key row 4h + j/4 (+ 32 sb + 16 u + 8 rd), d = 32 db + 16 (gq & 1) + 4 (j & 3).
+  uint32_t t_off[D / 32];
+  {
+    const int j = lane & 15, gq = lane >> 4;
+    const int row = 4 * h + (j >> 2);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int c = 4 * db + 2 * (gq & 1) + ((j & 3) >> 1);
+      t_off[db] = (uint32_t)(row * RB + ((c ^ swz(row)) * 16) + (j & 1) * 8);
+    }
+  }
+
+  if (ntiles > 0) issue_tile(0, 0);
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int stage = kt & 1;
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (kt + 1 < ntiles) issue_tile(kt + 1, stage ^ 1);
+    const int k0 = kt * BN;
+    if (CAUSAL && k0 > qw + 31) continue;
+    const char* ks = smem + stage * 2 * TB;
+    const char* vs = ks + TB;
+
+    f32x16 st[2], dp[2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        st[sb][r] = 0.f;
+        dp[sb][r] = 0.f;
+      }
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) {
+        const bf16x8 ka = as_bf16x8(*(const u32x4*)(ks + sb * 32 * RB + a_off[t]));
+        const bf16x8 va = as_bf16x8(*(const u32x4*)(vs + sb * 32 * RB + a_off[t]));
+        st[sb] = mfma32(ka, qf[t], st[sb]);
+        dp[sb] = mfma32(va, df[t], dp[sb]);
+      }
+    }
+    // Register r of half sb holds key k0 + 32 sb + 8 (r/4) + 4 h + r % 4.
+    const bool need_mask = CAUSAL && (k0 + BN - 1 > qw);
+    const int lim = qi - k0 - 4 * h;
+    bf16x8 dsb[2][2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pv = exp2_hw(__builtin_fmaf(st[sb][r], p.c, -lse2));
+        if (need_mask && (32 * sb + 8 * (r >> 2) + (r & 3) > lim)) pv = 0.f;
+        st[sb][r] = pv * (dp[sb][r] - dlt);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        u32x4 w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = pack_bf16x2(st[sb][8 * u + 2 * j], st[sb][8 * u + 2 * j + 1]);
+        dsb[sb][u] = as_bf16x8(w);
+      }
+    }
+    // dQ^T += K^T dS^T.
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const char* base = ks + (32 * sb + 16 * u) * RB + t_off[db];
+          const u32x2 lo = lds_read_tr16((const lds_void*)base);
+          const u32x2 hi = lds_read_tr16((const lds_void*)(base + 8 * RB));
+          const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+          acc[db] = mfma32(as_bf16x8(a), dsb[sb][u], acc[db]);
+        }
+  }
+
+  // dQ = scale * dQ^T; register r of block db is d = 32 db + 8 (r/4) + 4 h + r % 4.
+  const rsrc_t out = make_rsrc_uniform(dQ + (size_t)bh * head_elems, head_bytes);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      u32x2 w;
+      w[0] = pack_bf16x2(acc[db][4 * g] * p.scale, acc[db][4 * g + 1] * p.scale);
+      w[1] = pack_bf16x2(acc[db][4 * g + 2] * p.scale, acc[db][4 * g + 3] * p.scale);
+      buf_store8(out, (uint32_t)(qi * RB + (32 * db + 8 * g + 4 * h) * 2), w);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // dQ = bf16(scale * dQ_acc), 8 elements per thread.
 __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(const float* __restrict__ acc,
                                                              uint16_t* __restrict__ dq,
@@ -436,10 +582,10 @@ __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(const float* __rest
   ((u32x4*)dq)[i] = w;
 }
 
-template <int D, bool CAUSAL, bool DET>
+template <int D, bool CAUSAL, bool FUSED_DQ>
 hipError_t launch_bwd_t(const BwdArgs& a, const BwdParams& p, hipStream_t s) {
   const dim3 grid((unsigned)(a.B * a.Hkv * p.nkb));
-  hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL, DET>), grid, dim3(64 * kBwdWaves), 0, s,
+  hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL, FUSED_DQ>), grid, dim3(64 * kBwdWaves), 0, s,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, (uint16_t*)a.dk, (uint16_t*)a.dv, p);
   return hipGetLastError();
@@ -458,11 +604,9 @@ BwdParams make_params(const BwdArgs& a) {
   p.nqs = (a.N + QS - 1) / QS;
   p.c = a.scale * kLog2e;
   p.scale = a.scale;
-  p.dq_acc = (float*)(ws + lay.dq_acc);
+  p.dq_acc = a.deterministic ? nullptr : (float*)(ws + lay.dq_acc);
   p.delta = (float*)(ws + lay.delta);
   p.lse2 = (float*)(ws + lay.lse2);
-  p.counters = a.deterministic ? (int*)(ws + lay.counters) : nullptr;
-  p.give_up = a.deterministic ? (int*)(ws + lay.give_up) : nullptr;
   return p;
 }
 
@@ -471,36 +615,48 @@ hipError_t launch_pre_d(const BwdArgs& a, hipStream_t s) {
   const BwdParams p = make_params(a);
   const int rows = a.B * a.Hq * a.N;
   constexpr int RPB = 256 / (D / 8);
-  const int ncount = a.deterministic ? a.B * a.Hq * p.nqs * kBwdWaves : 0;
-  int blocks = (rows + RPB - 1) / RPB;
-  blocks = max(blocks, (ncount + 255) / 256);
+  const int blocks = (rows + RPB - 1) / RPB;
   hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3(blocks), dim3(256), 0, s, (const uint16_t*)a.o,
-                     (const uint16_t*)a.dout, a.lse, p, rows, ncount);
+                     (const uint16_t*)a.dout, a.lse, p, rows);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_main_d(const BwdArgs& a, hipStream_t s) {
   const BwdParams p = make_params(a);
+  // Fixed-order mode leaves dQ to bwd_dq_kernel.
   if (a.causal)
-    return a.deterministic ? launch_bwd_t<D, true, true>(a, p, s) : launch_bwd_t<D, true, false>(a, p, s);
-  return a.deterministic ? launch_bwd_t<D, false, true>(a, p, s) : launch_bwd_t<D, false, false>(a, p, s);
+    return a.deterministic ? launch_bwd_t<D, true, false>(a, p, s) : launch_bwd_t<D, true, true>(a, p, s);
+  return a.deterministic ? launch_bwd_t<D, false, false>(a, p, s) : launch_bwd_t<D, false, true>(a, p, s);
+}
+
+template <int D>
+hipError_t launch_dq_d(const BwdArgs& a, hipStream_t s) {
+  const BwdParams p = make_params(a);
+  const int nqb = (a.N + 127) / 128;
+  const dim3 grid((unsigned)(a.B * a.Hq * nqb));
+  if (a.causal)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, true>), grid, dim3(256), 0, s, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
+                       (uint16_t*)a.dq, p, nqb);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<D, false>), grid, dim3(256), 0, s, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
+                       (uint16_t*)a.dq, p, nqb);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 BwdLayout bwd_layout(int B, int Hq, int N, int D, int deterministic) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  const int QS = 4096 / D;
+  (void)D;
   const size_t rows = (size_t)B * Hq * N;
   BwdLayout l;
-  l.dq_acc = 0;
-  l.delta = up(rows * D * 4);
-  l.lse2 = l.delta + up(rows * 4);
-  l.counters = l.lse2 + up(rows * 4);
-  const size_t nqs = (size_t)(N + QS - 1) / QS;
-  l.give_up = l.counters + (deterministic ? up((size_t)B * Hq * nqs * kBwdWaves * 4) : 0);
-  l.total = l.give_up + (deterministic ? 256 : 0);
+  l.delta = 0;
+  l.lse2 = up(rows * 4);
+  l.dq_acc = l.lse2 + up(rows * 4);
+  l.total = l.dq_acc + (deterministic ? 0 : up(rows * D * 4));
   return l;
 }
 
@@ -512,7 +668,8 @@ hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t s) {
   return a.D == 64 ? launch_main_d<64>(a, s) : launch_main_d<128>(a, s);
 }
 
-hipError_t launch_bwd_dq_convert(const BwdArgs& a, hipStream_t s) {
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t s) {
+  if (a.deterministic) return a.D == 64 ? launch_dq_d<64>(a, s) : launch_dq_d<128>(a, s);
   const BwdParams p = make_params(a);
   const size_t n8 = (size_t)a.B * a.Hq * a.N * a.D / 8;
   hipLaunchKernelGGL(bwd_dq_convert_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s,

@@ -155,14 +155,16 @@ int fa_bwd_main(const void* q, const void* k, const void* v, const void* dout, v
   return fa::launch_bwd_main(a, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-int fa_bwd_dq_convert(void* dq, int B, int Hq, int Hkv, int N, int D, float scale,
-                      void* workspace, size_t workspace_bytes, int deterministic, void* stream) {
-  int rc = check_bwd(B, Hq, Hkv, N, D, scale, workspace, workspace_bytes, deterministic, {},
-                     {{dq, qbytes(B, Hq, N, D)}});
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq, int B,
+              int Hq, int Hkv, int N, int D, int causal, float scale, void* workspace,
+              size_t workspace_bytes, int deterministic, void* stream) {
+  const size_t qb = qbytes(B, Hq, N, D), kb = qbytes(B, Hkv, N, D);
+  int rc = check_bwd(B, Hq, Hkv, N, D, scale, workspace, workspace_bytes, deterministic,
+                     {{q, qb}, {k, kb}, {v, kb}, {dout, qb}}, {{dq, qb}});
   if (rc != FA_OK) return rc;
-  const fa::BwdArgs a = bwd_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, dq, nullptr,
-                                 nullptr, B, Hq, Hkv, N, D, 0, scale, workspace, deterministic);
-  return fa::launch_bwd_dq_convert(a, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+  const fa::BwdArgs a = bwd_args(q, k, v, nullptr, nullptr, dout, dq, nullptr, nullptr, B, Hq, Hkv,
+                                 N, D, causal, scale, workspace, deterministic);
+  return fa::launch_bwd_dq(a, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -179,7 +181,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   hipStream_t s = (hipStream_t)stream;
   if (fa::launch_bwd_preprocess(a, s) != hipSuccess) return FA_ERR_HIP;
   if (fa::launch_bwd_main(a, s) != hipSuccess) return FA_ERR_HIP;
-  if (fa::launch_bwd_dq_convert(a, s) != hipSuccess) return FA_ERR_HIP;
+  if (fa::launch_bwd_dq(a, s) != hipSuccess) return FA_ERR_HIP;
   return FA_OK;
 }
 

@@ -49,11 +49,9 @@ struct BwdArgs {
 
 // Workspace layout of the backward (offsets in bytes, 256-byte aligned).
 struct BwdLayout {
-  size_t dq_acc;    // fp32 [B][Hq][N][D]
   size_t delta;     // fp32 [B][Hq][N]
   size_t lse2;      // fp32 [B][Hq][N], LSE * log2(e)
-  size_t counters;  // int32 [B][Hq][query steps][waves] (deterministic only)
-  size_t give_up;   // int32 flag (deterministic only)
+  size_t dq_acc;    // fp32 [B][Hq][N][D] (atomic mode only)
   size_t total;
 };
 
@@ -61,6 +59,8 @@ BwdLayout bwd_layout(int B, int Hq, int N, int D, int deterministic);
 // The three backward stages; each reads only the BwdArgs fields it needs.
 hipError_t launch_bwd_preprocess(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t stream);
-hipError_t launch_bwd_dq_convert(const BwdArgs& a, hipStream_t stream);
+// Atomic mode: dq = bf16(scale * accumulated dQ).  Fixed-order mode: the dQ
+// kernel.
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 
 }  // namespace fa

@@ -79,9 +79,9 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
               int exp_poly_quarters, void* stream);
 
 /*
- * Bytes of device workspace fa_bwd needs for this problem (fp32 dQ
- * accumulator, per-row Delta = rowsum(dO * O), and for deterministic mode the
- * per-query-tile order counters).  Returns 0 for invalid sizes.
+ * Bytes of device workspace fa_bwd needs for this problem: per-row
+ * Delta = rowsum(dO * O) and LSE * log2(e), plus, in atomic mode, the fp32 dQ
+ * accumulator.  Returns 0 for invalid sizes.
  */
 size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int D, int deterministic);
 
@@ -96,9 +96,11 @@ size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int D, int determini
  *     256-byte aligned, owned by the caller; its contents on entry do not
  *     matter and are scratch afterwards.  Two calls in flight at once must
  *     not share a workspace.
- *   deterministic = 0: dQ contributions are added with fp32 atomics (no
- *     run-to-run bitwise guarantee).  deterministic = 1: they are added in a
- *     fixed order, so dq, dk and dv are bit-identical across calls with the
+ *   deterministic = 0: each key tile's dQ contribution is added into an fp32
+ *     accumulator with atomics (no run-to-run bitwise guarantee for dq).
+ *   deterministic = 1: dQ is formed by a separate pass that owns each query
+ *     tile and sums the key tiles in a fixed ascending order (recomputing S,
+ *     dP and dS), so dq, dk and dv are bit-identical across calls with the
  *     same inputs on the same device.
  * With Hq != Hkv, dk and dv sum over the query heads that share a K/V head.
  * dq, dk, dv must not overlap any input.
@@ -118,9 +120,10 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
  *     workspace, and clears the workspace's fp32 dQ accumulator (and order
  *     counters).
  *   fa_bwd_main: recomputes P tile by tile from q, k and the workspace's
- *     LSE * log2(e), and forms dK, dV (written to dk, dv) and the unscaled
- *     dQ sums (accumulated in the workspace).
- *   fa_bwd_dq_convert: dq = bf16(scale * accumulated dQ).
+ *     LSE * log2(e), and forms dK, dV (written to dk, dv); in atomic mode it
+ *     also accumulates the unscaled dQ sums in the workspace.
+ *   fa_bwd_dq: atomic mode: dq = bf16(scale * accumulated dQ) (q, k, v, dout
+ *     unused but checked); fixed-order mode: the dQ pass described above.
  */
 int fa_bwd_preprocess(const void* o, const void* dout, const float* lse, int B, int Hq, int Hkv,
                       int N, int D, void* workspace, size_t workspace_bytes, int deterministic,
@@ -128,8 +131,9 @@ int fa_bwd_preprocess(const void* o, const void* dout, const float* lse, int B, 
 int fa_bwd_main(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv,
                 int B, int Hq, int Hkv, int N, int D, int causal, float scale, void* workspace,
                 size_t workspace_bytes, int deterministic, void* stream);
-int fa_bwd_dq_convert(void* dq, int B, int Hq, int Hkv, int N, int D, float scale,
-                      void* workspace, size_t workspace_bytes, int deterministic, void* stream);
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq, int B,
+              int Hq, int Hkv, int N, int D, int causal, float scale, void* workspace,
+              size_t workspace_bytes, int deterministic, void* stream);
 
 /* Static text for a status code. */
 const char* fa_strerror(int status);
