@@ -37,7 +37,6 @@ namespace {
 constexpr int kBwdBN = 128;    // keys per workgroup (32 per wave)
 constexpr int kBwdWaves = 4;
 
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 
 struct BwdParams {
   int B, Hq, G, N;
@@ -113,9 +112,14 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
 
   // Per stage: Q tile, dO tile, 256 B of LSE*log2e, 256 B of Delta; then (atomic
   // mode) two dS^T buffers.
+  // Each double buffer is two arrays so the compiler can tell an in-flight
+  // copy into one from reads of the other.
   constexpr int STAGE = 2 * TB + 512;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE + (FUSED_DQ ? 2 * DSB : 0)];
-  char* const ds_buf = smem + 2 * STAGE;
+  constexpr int DSA = FUSED_DQ ? DSB : 16;
+  __shared__ __attribute__((aligned(1024))) char stage0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage1[STAGE];
+  __shared__ __attribute__((aligned(1024))) char dsbuf0[DSA];
+  __shared__ __attribute__((aligned(1024))) char dsbuf1[DSA];
 
   const int Hkv = p.Hq / p.G;
   const int wg = blockIdx.x;
@@ -184,29 +188,30 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
   for (int s = 0; s < NLD; ++s) {
     const int g = (s * kBwdWaves + wave) * 64 + lane;
     const int row = g / KCH, pc = g % KCH;
-    ld_off[s] = (uint32_t)(row * RB + ((pc ^ swz(row)) * 16));
+    ld_off[s] = (uint32_t)(row * RB + ((pc ^ tile_swz<D>(row)) * 16));
   }
   // Row-major A operand (Q of S, dO of dP): row 32 qb + n, logical chunk 2t+h.
   uint32_t a_off[D / 16];
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t) a_off[t] = (uint32_t)(n * RB + (((2 * t + h) ^ swz(n)) * 16));
+  for (int t = 0; t < D / 16; ++t) a_off[t] = (uint32_t)(n * RB + (((2 * t + h) ^ tile_swz<D>(n)) * 16));
   // Transposing B-operand reads of Q / dO (queries 32 qb + 16 u + 8 rd + 4 h +
   // 0..3 of column d = 32 db + n): lane j of 16-lane group gq points at row
-  // 4 h + j/4 and d = 32 db + 16 (gq & 1) + 4 (j & 3).
+  // 8 rd + 4 h + j/4 and d = 32 db + 16 (gq & 1) + 4 (j & 3).
   const int tj = lane & 15, gq = lane >> 4;
-  uint32_t tr_off[ND];
-  {
-    const int row = 4 * h + (tj >> 2);
+  uint32_t tr_off[ND][2];
+#pragma unroll
+  for (int rd = 0; rd < 2; ++rd) {
+    const int row = 8 * rd + 4 * h + (tj >> 2);
 #pragma unroll
     for (int db = 0; db < ND; ++db) {
       const int c = 4 * db + 2 * (gq & 1) + ((tj & 3) >> 1);
-      tr_off[db] = (uint32_t)(row * RB + ((c ^ swz(row)) * 16) + (tj & 1) * 8);
+      tr_off[db][rd] = (uint32_t)(row * RB + ((c ^ tile_swz<D>(row)) * 16) + (tj & 1) * 8);
     }
   }
   // dS^T [key][query] (rows of DSRB bytes).  Chunk swizzle for 4 consecutive
   // rows read at two adjacent chunks: fd(r) keeps those 8 chunks on distinct
   // banks for both 64-byte and 128-byte rows.
-  auto fd = [](int r) { return QS == 32 ? (((r >> 1) & 1) << 1) : swz(r); };
+  auto fd = [](int r) { return QS == 32 ? (((r >> 1) & 1) << 1) : (((r & 3) << 1) | ((r >> 2) & 1)); };
   // Writer: lane (key 32 wave + n) stores 4 consecutive queries 32 qb + 8 g + 4 h.
   // Reader (A operand of dQ): lane j of group gq points at key row
   // 16 t + 8 rd + 4 h + j/4 and query 32 dq_qb + 16 (gq & 1) + 4 (j & 3).
@@ -226,7 +231,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
   auto step_head = [&](int i) { return hk * p.G + i / per_head; };
   auto step_qs = [&](int i) { return p.nqs - 1 - (i % per_head); };
 
-  auto issue_step = [&](int i, int stage) {
+  auto issue_step = [&](int i, char* st) {
     const int hq = step_head(i);
     const int q0 = step_qs(i) * QS;
     const size_t qh = ((size_t)b * p.Hq + hq) * head_elems;
@@ -234,7 +239,6 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
     const uint32_t left = head_bytes > base ? head_bytes - base : 0u;
     const rsrc_t qrr = make_rsrc_uniform((const char*)(Q + qh) + base, left);
     const rsrc_t dor = make_rsrc_uniform((const char*)(dO + qh) + base, left);
-    char* st = smem + stage * STAGE;
 #pragma unroll
     for (int s = 0; s < NLD; ++s) {
       lds_dma16(qrr, (lds_void*)(st + (s * kBwdWaves + wave) * 1024), ld_off[s]);
@@ -248,11 +252,10 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
   };
 
   // dQ block of step i (dS^T of that step in ds buffer i & 1).
-  auto dq_step = [&](int i) {
+  auto dq_step = [&](int i, const char* dsb) {
     if constexpr (FUSED_DQ) {
     const int hq = step_head(i);
     const int q0 = step_qs(i) * QS;
-    const char* dsb = ds_buf + (i & 1) * DSB;
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
@@ -276,22 +279,19 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
     }
   };
 
-  if (nsteps > 0) issue_step(0, 0);
-
-  for (int i = 0; i < nsteps; ++i) {
-    const int stage = i & 1;
+  // One step: wait for its inputs, start the next step's copy into the other
+  // stage, (atomic mode) finish the previous step's dQ, compute.
+  auto step = [&](int i, const char* st, char* next, char* dsw, const char* dsprev) {
     wait_vmcnt<0>();
     __syncthreads();  // step i inputs are in LDS; dS^T of step i-1 is complete
-    if (i + 1 < nsteps) issue_step(i + 1, stage ^ 1);
-    if (FUSED_DQ && i > 0) dq_step(i - 1);
+    if (i + 1 < nsteps) issue_step(i + 1, next);
+    if (FUSED_DQ && i > 0) dq_step(i - 1, dsprev);
 
     const int q0 = step_qs(i) * QS;
-    const char* st = smem + stage * STAGE;
     const char* qs_l = st;
     const char* dos_l = st + TB;
     const float* lse_l = (const float*)(st + 2 * TB);
     const float* dlt_l = (const float*)(st + 2 * TB + 256);
-    char* dsw = ds_buf + stage * DSB;
     // Keys of this wave exceed some query of the step only near the diagonal.
     const bool need_mask = CAUSAL && (q0 < kw + 31);
     const int lim = key - q0 - 4 * h;  // masked when 32qb + 8(r/4) + r%4 < lim
@@ -342,11 +342,11 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
       for (int db = 0; db < ND; ++db)
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const int roff = (32 * qb + 16 * u) * RB + tr_off[db];
-          const u32x2 olo = lds_read_tr16((const lds_void*)(dos_l + roff));
-          const u32x2 ohi = lds_read_tr16((const lds_void*)(dos_l + roff + 8 * RB));
-          const u32x2 qlo = lds_read_tr16((const lds_void*)(qs_l + roff));
-          const u32x2 qhi = lds_read_tr16((const lds_void*)(qs_l + roff + 8 * RB));
+          const int roff = (32 * qb + 16 * u) * RB;
+          const u32x2 olo = lds_read_tr16((const lds_void*)(dos_l + roff + tr_off[db][0]));
+          const u32x2 ohi = lds_read_tr16((const lds_void*)(dos_l + roff + tr_off[db][1]));
+          const u32x2 qlo = lds_read_tr16((const lds_void*)(qs_l + roff + tr_off[db][0]));
+          const u32x2 qhi = lds_read_tr16((const lds_void*)(qs_l + roff + tr_off[db][1]));
           const u32x4 ob = {olo[0], olo[1], ohi[0], ohi[1]};
           const u32x4 qbv = {qlo[0], qlo[1], qhi[0], qhi[1]};
           dv_acc[db] = mfma32(pa[u], as_bf16x8(ob), dv_acc[db]);
@@ -364,10 +364,16 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
         *(u32x2*)(dsw + ds_wrow * DSRB + (((col >> 3) ^ fd(ds_wrow)) * 16) + ((col >> 2) & 1) * 8) = w;
       }
     }
+  };
+
+  if (nsteps > 0) issue_step(0, stage0);
+  for (int i = 0; i < nsteps; i += 2) {
+    step(i, stage0, stage1, dsbuf0, dsbuf1);
+    if (i + 1 < nsteps) step(i + 1, stage1, stage0, dsbuf1, dsbuf0);
   }
   if (FUSED_DQ && nsteps > 0) {
     __syncthreads();
-    dq_step(nsteps - 1);
+    dq_step(nsteps - 1, (nsteps - 1) & 1 ? dsbuf1 : dsbuf0);
   }
 
   // ---- dK (scaled) and dV of this wave's 32 keys ----------------------------
@@ -409,7 +415,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t* __restri
   constexpr int TB = BN * RB;
   constexpr int NLD = TB / 1024 / NW;
   static_assert(NLD >= 1, "tile too small");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TB];  // [stage][K, V]
+  // Two stages of [K, V] tiles as two arrays (see the main kernel).
+  __shared__ __attribute__((aligned(1024))) char kv0[2 * TB];
+  __shared__ __attribute__((aligned(1024))) char kv1[2 * TB];
 
   const int BH = p.B * p.Hq;
   const int wg = blockIdx.x;
@@ -459,14 +467,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t* __restri
   for (int s = 0; s < NLD; ++s) {
     const int g = (s * NW + wave) * 64 + lane;
     const int row = g / KCH, pc = g % KCH;
-    ld_off[s] = (uint32_t)(row * RB + ((pc ^ swz(row)) * 16));
+    ld_off[s] = (uint32_t)(row * RB + ((pc ^ tile_swz<D>(row)) * 16));
   }
-  auto issue_tile = [&](int kt, int stage) {
+  auto issue_tile = [&](int kt, char* ks) {
     const uint32_t base = (uint32_t)kt * TB;
     const uint32_t left = head_bytes > base ? head_bytes - base : 0u;
     const rsrc_t kr = make_rsrc_uniform((const char*)Kh + base, left);
     const rsrc_t vr = make_rsrc_uniform((const char*)Vh + base, left);
-    char* ks = smem + stage * 2 * TB;
 #pragma unroll
     for (int s = 0; s < NLD; ++s) {
       lds_dma16(kr, (lds_void*)(ks + (s * NW + wave) * 1024), ld_off[s]);
@@ -476,29 +483,29 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t* __restri
   // Row reads (A operands of S^T and dP^T): row n (+32 sb), logical chunk 2t + h.
   uint32_t a_off[D / 16];
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t) a_off[t] = (uint32_t)(n * RB + (((2 * t + h) ^ swz(n)) * 16));
+  for (int t = 0; t < D / 16; ++t) a_off[t] = (uint32_t)(n * RB + (((2 * t + h) ^ tile_swz<D>(n)) * 16));
   // Transposing reads of K (A operand K^T of dQ^T): in 16-lane group gq, lane j
-  // points at key row 4h + j/4 (+ 32 sb + 16 u + 8 rd), d = 32 db + 16 (gq & 1) + 4 (j & 3).
-  uint32_t t_off[D / 32];
+  // points at key row 8 rd + 4h + j/4 (+ 32 sb + 16 u), d = 32 db + 16 (gq & 1) + 4 (j & 3).
+  uint32_t t_off[D / 32][2];
   {
     const int j = lane & 15, gq = lane >> 4;
-    const int row = 4 * h + (j >> 2);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const int c = 4 * db + 2 * (gq & 1) + ((j & 3) >> 1);
-      t_off[db] = (uint32_t)(row * RB + ((c ^ swz(row)) * 16) + (j & 1) * 8);
+    for (int rd = 0; rd < 2; ++rd) {
+      const int row = 8 * rd + 4 * h + (j >> 2);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int c = 4 * db + 2 * (gq & 1) + ((j & 3) >> 1);
+        t_off[db][rd] = (uint32_t)(row * RB + ((c ^ tile_swz<D>(row)) * 16) + (j & 1) * 8);
+      }
     }
   }
 
-  if (ntiles > 0) issue_tile(0, 0);
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int stage = kt & 1;
+  auto tile = [&](int kt, const char* ks, char* next) {
     wait_vmcnt<0>();
     __syncthreads();
-    if (kt + 1 < ntiles) issue_tile(kt + 1, stage ^ 1);
+    if (kt + 1 < ntiles) issue_tile(kt + 1, next);
     const int k0 = kt * BN;
-    if (CAUSAL && k0 > qw + 31) continue;
-    const char* ks = smem + stage * 2 * TB;
+    if (CAUSAL && k0 > qw + 31) return;
     const char* vs = ks + TB;
 
     f32x16 st[2], dp[2];
@@ -544,12 +551,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t* __restri
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const char* base = ks + (32 * sb + 16 * u) * RB + t_off[db];
-          const u32x2 lo = lds_read_tr16((const lds_void*)base);
-          const u32x2 hi = lds_read_tr16((const lds_void*)(base + 8 * RB));
+          const char* base = ks + (32 * sb + 16 * u) * RB;
+          const u32x2 lo = lds_read_tr16((const lds_void*)(base + t_off[db][0]));
+          const u32x2 hi = lds_read_tr16((const lds_void*)(base + t_off[db][1]));
           const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
           acc[db] = mfma32(as_bf16x8(a), dsb[sb][u], acc[db]);
         }
+  };
+
+  if (ntiles > 0) issue_tile(0, kv0);
+  for (int kt = 0; kt < ntiles; kt += 2) {
+    tile(kt, kv0, kv1);
+    if (kt + 1 < ntiles) tile(kt + 1, kv1, kv0);
   }
 
   // dQ = scale * dQ^T; register r of block db is d = 32 db + 8 (r/4) + 4 h + r % 4.

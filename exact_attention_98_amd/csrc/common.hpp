@@ -118,6 +118,23 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const lds_void* p) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p));
 }
 
+// ---- LDS tile swizzle ------------------------------------------------------------
+// Row-major bf16 tiles of D columns keep 16-byte chunk c of row r at chunk
+// c ^ tile_swz<D>(r).  gfx950's LDS serves 256 bytes (64 four-byte banks) per
+// cycle; with this swizzle both access patterns the kernels use are
+// conflict-free:
+//   - 16 consecutive rows at one logical chunk (MFMA row operands, ds_read_b128);
+//   - 4 consecutive rows (first row a multiple of 4) at 4 consecutive chunks
+//     starting at a multiple of 4 (ds_read_b64_tr_b16, 32 lanes).
+// D = 128 (256-byte rows): bits 0-1 and 2-3 of r swapped.  D = 64 (128-byte
+// rows, two per 256 bytes): a bijection of bits 1-3 of r with bit 1 moved to
+// bit 2.  Both depend on r mod 16 only.
+template <int D>
+__device__ __forceinline__ int tile_swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
 // Hardware exp2 (v_exp_f32); exp2(-inf) = 0.
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 

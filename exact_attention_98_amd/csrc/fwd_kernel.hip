@@ -29,10 +29,8 @@
 // the contraction index).
 //
 // LDS layout: K and V tiles are row-major [key][d] with the 16-byte chunk c of
-// row r stored at chunk c ^ f(r), f(r) = 2 (r & 3) + ((r >> 2) & 1).  Eight
-// consecutive rows at one logical chunk (the K reads) and four consecutive
-// rows at two adjacent chunks (the transposing V reads) both hit distinct
-// banks.
+// row r stored at chunk c ^ tile_swz<D>(r), which keeps the row reads of K and
+// the transposing reads of V free of bank conflicts.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -42,8 +40,6 @@ namespace {
 constexpr int kFwdBM = 128;   // queries per workgroup
 constexpr int kFwdBN = 64;    // keys per K/V tile
 constexpr int kFwdWaves = 4;
-
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 
 template <int D, bool CAUSAL, int POLYQ>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict__ Q,
@@ -57,8 +53,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
   constexpr int TB = BN * RB;           // bytes per K (or V) tile
   constexpr int NLD = TB / 1024 / kFwdWaves;  // 1 KiB direct loads per wave per tensor
   static_assert(NLD >= 1, "tile too small");
-  // [stage][K, V] tiles.
-  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TB];
+  // Two stages of [K, V] tiles, as two arrays: with the stage known at compile
+  // time the compiler can tell the in-flight copy into one stage from reads of
+  // the other, and does not wait for the copy before those reads.
+  __shared__ __attribute__((aligned(1024))) char stage0[2 * TB];
+  __shared__ __attribute__((aligned(1024))) char stage1[2 * TB];
 
   // Grid order: consecutive workgroup ids walk heads first, so with B*Hq a
   // multiple of 8 every tile of a head lands on the same XCD (ids are dealt to
@@ -109,14 +108,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
   for (int s = 0; s < NLD; ++s) {
     const int g = (s * kFwdWaves + wave) * 64 + lane;
     const int row = g / KCH, pc = g % KCH;
-    ld_off[s] = (uint32_t)(row * RB + ((pc ^ swz(row)) * 16));
+    ld_off[s] = (uint32_t)(row * RB + ((pc ^ tile_swz<D>(row)) * 16));
   }
-  auto issue_tile = [&](int kt, int stage) {
+  auto issue_tile = [&](int kt, char* ks) {
     const uint32_t base = (uint32_t)kt * TB;
     const uint32_t left = head_bytes > base ? head_bytes - base : 0u;
     const rsrc_t kr = make_rsrc_uniform((const char*)Kh + base, left);
     const rsrc_t vr = make_rsrc_uniform((const char*)Vh + base, left);
-    char* ks = smem + stage * 2 * TB;
     char* vs = ks + TB;
 #pragma unroll
     for (int s = 0; s < NLD; ++s) {
@@ -129,32 +127,33 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
   // K (A operand of S^T): row n (+32 sb), logical chunk 2t + h.
   uint32_t k_off[D / 16];
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t) k_off[t] = (uint32_t)(n * RB + (((2 * t + h) ^ swz(n)) * 16));
+  for (int t = 0; t < D / 16; ++t) k_off[t] = (uint32_t)(n * RB + (((2 * t + h) ^ tile_swz<D>(n)) * 16));
   // V (A operand of O^T = V^T P^T) through transposing reads: in 16-lane group
-  // gq = lane / 16, lane j points at row 4 h + j / 4 (+ 32 sb + 16 u + 8 rd)
+  // gq = lane / 16, lane j points at row 8 rd + 4 h + j / 4 (+ 32 sb + 16 u)
   // and d = 32 db + 16 (gq & 1) + 4 (j & 3).
-  uint32_t v_off[D / 32];
+  uint32_t v_off[D / 32][2];
   {
     const int j = lane & 15, gq = lane >> 4;
-    const int row = 4 * h + (j >> 2);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const int c = 4 * db + 2 * (gq & 1) + ((j & 3) >> 1);
-      v_off[db] = (uint32_t)(row * RB + ((c ^ swz(row)) * 16) + (j & 1) * 8);
+    for (int rd = 0; rd < 2; ++rd) {
+      const int row = 8 * rd + 4 * h + (j >> 2);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int c = 4 * db + 2 * (gq & 1) + ((j & 3) >> 1);
+        v_off[db][rd] = (uint32_t)(row * RB + ((c ^ tile_swz<D>(row)) * 16) + (j & 1) * 8);
+      }
     }
   }
 
-  if (ntiles > 0) issue_tile(0, 0);
-
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int stage = kt & 1;
+  // One tile: wait for its copy, start the next tile's copy into the other
+  // stage, compute.
+  auto tile = [&](int kt, const char* ks, char* next) {
     wait_vmcnt<0>();
     __syncthreads();  // tile kt is in LDS; everyone is done with tile kt-1
-    if (kt + 1 < ntiles) issue_tile(kt + 1, stage ^ 1);
+    if (kt + 1 < ntiles) issue_tile(kt + 1, next);
     const int k0 = kt * BN;
     // Tiles wholly above this wave's diagonal contribute nothing.
-    if (CAUSAL && k0 > qw + 31) continue;
-    const char* ks = smem + stage * 2 * TB;
+    if (CAUSAL && k0 > qw + 31) return;
     const char* vs = ks + TB;
 
     // S^T for the two 32-key halves of the tile.
@@ -228,12 +227,18 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const char* base = vs + (32 * sb + 16 * u) * RB + v_off[db];
-          const u32x2 lo = lds_read_tr16((const lds_void*)base);
-          const u32x2 hi = lds_read_tr16((const lds_void*)(base + 8 * RB));
+          const char* base = vs + (32 * sb + 16 * u) * RB;
+          const u32x2 lo = lds_read_tr16((const lds_void*)(base + v_off[db][0]));
+          const u32x2 hi = lds_read_tr16((const lds_void*)(base + v_off[db][1]));
           const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
           oacc[db] = mfma32(as_bf16x8(a), pb[sb][u], oacc[db]);
         }
+  };
+
+  if (ntiles > 0) issue_tile(0, stage0);
+  for (int kt = 0; kt < ntiles; kt += 2) {
+    tile(kt, stage0, stage1);
+    if (kt + 1 < ntiles) tile(kt + 1, stage1, stage0);
   }
 
   // Final correction: O = O / l, LSE = (m_ref + log2 l) ln 2.  Rows past N are
