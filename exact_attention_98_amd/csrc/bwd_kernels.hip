@@ -112,14 +112,18 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
 
   // Per stage: Q tile, dO tile, 256 B of LSE*log2e, 256 B of Delta; then (atomic
   // mode) two dS^T buffers.
-  // Each double buffer is two arrays so the compiler can tell an in-flight
-  // copy into one from reads of the other.
+  // Three stages: the step being finished (its LSE, Delta and the transposing
+  // reads of its Q and dO), the next step (row reads of Q and dO for its S and
+  // dP), and the step after that, being copied in.  Each buffer is its own
+  // array so the compiler can tell an in-flight copy from reads of the others.
   constexpr int STAGE = 2 * TB + 512;
   constexpr int DSA = FUSED_DQ ? DSB : 16;
   __shared__ __attribute__((aligned(1024))) char stage0[STAGE];
   __shared__ __attribute__((aligned(1024))) char stage1[STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage2[STAGE];
   __shared__ __attribute__((aligned(1024))) char dsbuf0[DSA];
   __shared__ __attribute__((aligned(1024))) char dsbuf1[DSA];
+  __shared__ __attribute__((aligned(1024))) char dsbuf2[DSA];
 
   const int Hkv = p.Hq / p.G;
   const int wg = blockIdx.x;
@@ -279,39 +283,60 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
     }
   };
 
-  // One step: wait for its inputs, start the next step's copy into the other
-  // stage, (atomic mode) finish the previous step's dQ, compute.
-  auto step = [&](int i, const char* st, char* next, char* dsw, const char* dsprev) {
-    wait_vmcnt<0>();
-    __syncthreads();  // step i inputs are in LDS; dS^T of step i-1 is complete
-    if (i + 1 < nsteps) issue_step(i + 1, next);
-    if (FUSED_DQ && i > 0) dq_step(i - 1, dsprev);
-
-    const int q0 = step_qs(i) * QS;
-    const char* qs_l = st;
-    const char* dos_l = st + TB;
-    const float* lse_l = (const float*)(st + 2 * TB);
-    const float* dlt_l = (const float*)(st + 2 * TB + 256);
-    // Keys of this wave exceed some query of the step only near the diagonal.
-    const bool need_mask = CAUSAL && (q0 < kw + 31);
-    const int lim = key - q0 - 4 * h;  // masked when 32qb + 8(r/4) + r%4 < lim
-
+  // S and dP of one step (A operands Q, dO by row reads of its stage).
+  auto compute_sdp = [&](const char* st, f32x16 (&sv)[NQB], f32x16 (&dv)[NQB]) {
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
-      f32x16 s, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        s[r] = 0.f;
-        dp[r] = 0.f;
+        sv[qb][r] = 0.f;
+        dv[qb][r] = 0.f;
       }
 #pragma unroll
       for (int t = 0; t < D / 16; ++t) {
-        const bf16x8 qa = as_bf16x8(*(const u32x4*)(qs_l + qb * 32 * RB + a_off[t]));
-        const bf16x8 da = as_bf16x8(*(const u32x4*)(dos_l + qb * 32 * RB + a_off[t]));
-        s = mfma32(qa, kB[t], s);
-        dp = mfma32(da, vB[t], dp);
+        const bf16x8 qa = as_bf16x8(*(const u32x4*)(st + qb * 32 * RB + a_off[t]));
+        const bf16x8 da = as_bf16x8(*(const u32x4*)(st + TB + qb * 32 * RB + a_off[t]));
+        sv[qb] = mfma32(qa, kB[t], sv[qb]);
+        dv[qb] = mfma32(da, vB[t], dv[qb]);
       }
-      // Register r holds query q0 + 32qb + 8(r/4) + 4h + r%4 and key `key`.
+    }
+  };
+
+  // One step i, software-pipelined: while the VALU forms P(i) and dS(i), the
+  // MFMA unit computes S(i+1) and dP(i+1); then dV, dK take step i's products.
+  // sv/dv hold S(i), dP(i); sn/dn receive S(i+1), dP(i+1).
+  auto body = [&](int i, const char* cur, const char* nxt, char* ld, char* dsw,
+                  const char* dsprev, f32x16 (&sv)[NQB], f32x16 (&dv)[NQB], f32x16 (&sn)[NQB],
+                  f32x16 (&dn)[NQB]) {
+    wait_vmcnt<0>();
+    __syncthreads();  // step i+1 is in LDS; step i-1's stage and dS^T are free
+    if (i + 2 < nsteps) issue_step(i + 2, ld);
+    if (FUSED_DQ && i > 0) dq_step(i - 1, dsprev);
+
+    const int q0 = step_qs(i) * QS;
+    // Causal mask of step i, only near the diagonal: S = -inf where key > query.
+    // Register r of block qb holds query q0 + 32qb + 8(r/4) + 4h + r%4.
+    if (CAUSAL && (q0 < kw + 31)) {
+      keep_branch();
+      const int lim = key - q0 - 4 * h;
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * qb + 8 * (r >> 2) + (r & 3) < lim) sv[qb][r] = -__builtin_inff();
+    }
+
+    // S(i+1), dP(i+1): always computed (on a stale stage after the last step,
+    // results unused) so this block has no branch to split the interleaving.
+    compute_sdp(nxt, sn, dn);
+
+    const char* qs_l = cur;
+    const char* dos_l = cur + TB;
+    const float* lse_l = (const float*)(cur + 2 * TB);
+    const float* dlt_l = (const float*)(cur + 2 * TB + 256);
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      // P = exp2(S c - LSE log2 e), dS = P (dP - Delta).
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const f32x4 l4 = *(const f32x4*)(lse_l + 32 * qb + 8 * r4 + 4 * h);
@@ -319,10 +344,9 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int r = 4 * r4 + j;
-          float pv = exp2_hw(__builtin_fmaf(s[r], p.c, -l4[j]));
-          if (need_mask && (32 * qb + 8 * r4 + j < lim)) pv = 0.f;  // selects: cheap next to 5 MFMAs
-          s[r] = pv;
-          dp[r] = pv * (dp[r] - d4[j]);
+          const float pv = exp2_hw(__builtin_fmaf(sv[qb][r], p.c, -l4[j]));
+          sv[qb][r] = pv;
+          dv[qb][r] = pv * (dv[qb][r] - d4[j]);
         }
       }
       bf16x8 pa[2], dsa[2];
@@ -331,8 +355,8 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
         u32x4 w1, w2;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          w1[j] = pack_bf16x2(s[8 * u + 2 * j], s[8 * u + 2 * j + 1]);
-          w2[j] = pack_bf16x2(dp[8 * u + 2 * j], dp[8 * u + 2 * j + 1]);
+          w1[j] = pack_bf16x2(sv[qb][8 * u + 2 * j], sv[qb][8 * u + 2 * j + 1]);
+          w2[j] = pack_bf16x2(dv[qb][8 * u + 2 * j], dv[qb][8 * u + 2 * j + 1]);
         }
         pa[u] = as_bf16x8(w1);
         dsa[u] = as_bf16x8(w2);
@@ -366,14 +390,27 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
     }
   };
 
-  if (nsteps > 0) issue_step(0, stage0);
-  for (int i = 0; i < nsteps; i += 2) {
-    step(i, stage0, stage1, dsbuf0, dsbuf1);
-    if (i + 1 < nsteps) step(i + 1, stage1, stage0, dsbuf1, dsbuf0);
+  f32x16 sA[NQB], dA[NQB], sB[NQB], dB[NQB];
+  if (nsteps > 0) {
+    issue_step(0, stage0);
+    if (nsteps > 1) issue_step(1, stage1);
+    wait_vmcnt<0>();
+    __syncthreads();
+    compute_sdp(stage0, sA, dA);
+  }
+  // Stages rotate with period 3 and the S/dP register sets with period 2.
+  for (int i = 0; i < nsteps; i += 6) {
+    body(i, stage0, stage1, stage2, dsbuf0, dsbuf2, sA, dA, sB, dB);
+    if (i + 1 < nsteps) body(i + 1, stage1, stage2, stage0, dsbuf1, dsbuf0, sB, dB, sA, dA);
+    if (i + 2 < nsteps) body(i + 2, stage2, stage0, stage1, dsbuf2, dsbuf1, sA, dA, sB, dB);
+    if (i + 3 < nsteps) body(i + 3, stage0, stage1, stage2, dsbuf0, dsbuf2, sB, dB, sA, dA);
+    if (i + 4 < nsteps) body(i + 4, stage1, stage2, stage0, dsbuf1, dsbuf0, sA, dA, sB, dB);
+    if (i + 5 < nsteps) body(i + 5, stage2, stage0, stage1, dsbuf2, dsbuf1, sB, dB, sA, dA);
   }
   if (FUSED_DQ && nsteps > 0) {
     __syncthreads();
-    dq_step(nsteps - 1, (nsteps - 1) & 1 ? dsbuf1 : dsbuf0);
+    const int last = (nsteps - 1) % 3;
+    dq_step(nsteps - 1, last == 0 ? dsbuf0 : (last == 1 ? dsbuf1 : dsbuf2));
   }
 
   // ---- dK (scaled) and dV of this wave's 32 keys ----------------------------
