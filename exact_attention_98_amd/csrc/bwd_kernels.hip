@@ -112,18 +112,19 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
 
   // Per stage: Q tile, dO tile, 256 B of LSE*log2e, 256 B of Delta; then (atomic
   // mode) two dS^T buffers.
-  // Three stages: the step being finished (its LSE, Delta and the transposing
+  // Four stages: the step being finished (its LSE, Delta and the transposing
   // reads of its Q and dO), the next step (row reads of Q and dO for its S and
-  // dP), and the step after that, being copied in.  Each buffer is its own
-  // array so the compiler can tell an in-flight copy from reads of the others.
+  // dP), and two more in flight, so a copy has two steps to land.  Each buffer
+  // is its own array so the compiler can tell an in-flight copy from reads of
+  // the others.
   constexpr int STAGE = 2 * TB + 512;
   constexpr int DSA = FUSED_DQ ? DSB : 16;
   __shared__ __attribute__((aligned(1024))) char stage0[STAGE];
   __shared__ __attribute__((aligned(1024))) char stage1[STAGE];
   __shared__ __attribute__((aligned(1024))) char stage2[STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage3[STAGE];
   __shared__ __attribute__((aligned(1024))) char dsbuf0[DSA];
   __shared__ __attribute__((aligned(1024))) char dsbuf1[DSA];
-  __shared__ __attribute__((aligned(1024))) char dsbuf2[DSA];
 
   const int Hkv = p.Hq / p.G;
   const int wg = blockIdx.x;
@@ -228,38 +229,67 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
   const int ds_wrow = 32 * wave + n;
 
   // ---- step schedule -------------------------------------------------------
-  // Linear step index i covers (head g, query step qs) with qs descending.
+  // Steps walk (head g, query step qs) with qs descending from the last step
+  // to the first that meets the tile's diagonal, then on to the next of the G
+  // query heads.  Two cursors follow it with scalar increments only: the next
+  // step to copy in and the step being finished.
   const int qs_first = CAUSAL ? (k0 / QS) : 0;
   const int per_head = max(p.nqs - qs_first, 0);
   const int nsteps = p.G * per_head;
-  auto step_head = [&](int i) { return hk * p.G + i / per_head; };
-  auto step_qs = [&](int i) { return p.nqs - 1 - (i % per_head); };
+  const int hq0 = hk * p.G;
+  const uint32_t lse_head_bytes = (uint32_t)p.N * 4u;
 
-  auto issue_step = [&](int i, char* st) {
-    const int hq = step_head(i);
-    const int q0 = step_qs(i) * QS;
-    const size_t qh = ((size_t)b * p.Hq + hq) * head_elems;
-    const uint32_t base = (uint32_t)q0 * RB;
-    const uint32_t left = head_bytes > base ? head_bytes - base : 0u;
-    const rsrc_t qrr = make_rsrc_uniform((const char*)(Q + qh) + base, left);
-    const rsrc_t dor = make_rsrc_uniform((const char*)(dO + qh) + base, left);
+  // Copy cursor: query step and the per-head base addresses of Q, dO, LSE, Delta.
+  int iss_qs = p.nqs - 1;
+  const char* iss_q = (const char*)(Q + ((size_t)b * p.Hq + hq0) * head_elems);
+  const char* iss_do = (const char*)(dO + ((size_t)b * p.Hq + hq0) * head_elems);
+  const char* iss_l = (const char*)(p.lse2 + ((size_t)b * p.Hq + hq0) * p.N);
+  const char* iss_d = (const char*)(p.delta + ((size_t)b * p.Hq + hq0) * p.N);
+  auto issue_next = [&](char* st) {
+    const uint32_t base = (uint32_t)iss_qs * (uint32_t)TB;
+    const uint32_t left = head_bytes - base;  // qs < nqs, so base < head_bytes
+    const rsrc_t qrr = make_rsrc_uniform(iss_q + base, left);
+    const rsrc_t dor = make_rsrc_uniform(iss_do + base, left);
 #pragma unroll
     for (int s = 0; s < NLD; ++s) {
       lds_dma16(qrr, (lds_void*)(st + (s * kBwdWaves + wave) * 1024), ld_off[s]);
       lds_dma16(dor, (lds_void*)(st + TB + (s * kBwdWaves + wave) * 1024), ld_off[s]);
     }
-    const size_t rh = ((size_t)b * p.Hq + hq) * p.N + q0;
-    const uint32_t rleft = (uint32_t)max(p.N - q0, 0) * 4u;
-    if (wave == 0) lds_dma4(make_rsrc_uniform(p.lse2 + rh, rleft), (lds_void*)(st + 2 * TB), lane * 4);
-    if (wave == 1)
-      lds_dma4(make_rsrc_uniform(p.delta + rh, rleft), (lds_void*)(st + 2 * TB + 256), lane * 4);
+    const uint32_t rbase = (uint32_t)iss_qs * (uint32_t)(QS * 4);
+    const uint32_t rleft = lse_head_bytes - rbase;
+    if (wave == 0) lds_dma4(make_rsrc_uniform(iss_l + rbase, rleft), (lds_void*)(st + 2 * TB), lane * 4);
+    if (wave == 1) lds_dma4(make_rsrc_uniform(iss_d + rbase, rleft), (lds_void*)(st + 2 * TB + 256), lane * 4);
+    if (--iss_qs < qs_first) {
+      iss_qs = p.nqs - 1;
+      iss_q += head_bytes;
+      iss_do += head_bytes;
+      iss_l += lse_head_bytes;
+      iss_d += lse_head_bytes;
+    }
+  };
+  // Cursor of the step being finished (query step and head offset g).
+  int cur_qs = p.nqs - 1, cur_g = 0;
+  int prev_qs = 0, prev_g = 0;  // the step before it (atomic dQ)
+  auto advance_cur = [&]() {
+    prev_qs = cur_qs;
+    prev_g = cur_g;
+    if (--cur_qs < qs_first) {
+      cur_qs = p.nqs - 1;
+      ++cur_g;
+    }
+  };
+  // Wait until at most one step's copies (the newest) are outstanding: waves 0
+  // and 1 issue one extra row-constant copy per step.
+  auto wait_all_but_one_step = [&]() {
+    if (wave < 2) wait_vmcnt<2 * NLD + 1>();
+    else wait_vmcnt<2 * NLD>();
   };
 
-  // dQ block of step i (dS^T of that step in ds buffer i & 1).
-  auto dq_step = [&](int i, const char* dsb) {
+  // dQ block of the step at (head offset g, query step qs), whose dS^T is in dsb.
+  auto dq_step = [&](int g, int qs, const char* dsb) {
     if constexpr (FUSED_DQ) {
-    const int hq = step_head(i);
-    const int q0 = step_qs(i) * QS;
+    const int hq = hq0 + g;
+    const int q0 = qs * QS;
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
@@ -308,12 +338,14 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
   auto body = [&](int i, const char* cur, const char* nxt, char* ld, char* dsw,
                   const char* dsprev, f32x16 (&sv)[NQB], f32x16 (&dv)[NQB], f32x16 (&sn)[NQB],
                   f32x16 (&dn)[NQB]) {
-    wait_vmcnt<0>();
-    __syncthreads();  // step i+1 is in LDS; step i-1's stage and dS^T are free
-    if (i + 2 < nsteps) issue_step(i + 2, ld);
-    if (FUSED_DQ && i > 0) dq_step(i - 1, dsprev);
+    // Step i+1 must be in LDS; step i+2 may still be in flight.
+    if (i + 2 < nsteps) wait_all_but_one_step();
+    else wait_vmcnt<0>();
+    __syncthreads();  // step i+1 visible to all; step i-1's stage and dS^T free
+    if (i + 3 < nsteps) issue_next(ld);
+    if (FUSED_DQ && i > 0) dq_step(prev_g, prev_qs, dsprev);
 
-    const int q0 = step_qs(i) * QS;
+    const int q0 = cur_qs * QS;
     // Causal mask of step i, only near the diagonal: S = -inf where key > query.
     // Register r of block qb holds query q0 + 32qb + 8(r/4) + 4h + r%4.
     if (CAUSAL && (q0 < kw + 31)) {
@@ -326,91 +358,145 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
           if (32 * qb + 8 * (r >> 2) + (r & 3) < lim) sv[qb][r] = -__builtin_inff();
     }
 
-    // S(i+1), dP(i+1): always computed (on a stale stage after the last step,
-    // results unused) so this block has no branch to split the interleaving.
-    compute_sdp(nxt, sn, dn);
-
+    // The issue order below is fixed by hand (sched_barrier fences): the
+    // MFMA unit runs one instruction at a time, in program order, so each
+    // matrix instruction is followed by the VALU work that should run under it.
+    // Phase A: the 16 S(i+1)/dP(i+1) MFMAs (always computed, on a stale stage
+    // after the last step, so the phase has no branch), each pair followed by
+    // 2 NQB elements of P(i) = exp2(S c - LSE log2 e), dS(i) = P (dP - Delta).
+    // Phase B: the dV += P^T dO, dK += dS^T Q MFMAs with their transposing
+    // reads one pair ahead.
+    constexpr int T = D / 16;
+    constexpr int NPAIR = NQB * T;         // S/dP MFMA pairs (8 for D = 64, 128)
+    constexpr int EPP = 16 * NQB / NPAIR;  // elements per lane per pair
     const char* qs_l = cur;
     const char* dos_l = cur + TB;
     const float* lse_l = (const float*)(cur + 2 * TB);
     const float* dlt_l = (const float*)(cur + 2 * TB + 256);
+    f32x4 l4[NQB][4], d4[NQB][4];
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      // P = exp2(S c - LSE log2 e), dS = P (dP - Delta).
+    for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 l4 = *(const f32x4*)(lse_l + 32 * qb + 8 * r4 + 4 * h);
-        const f32x4 d4 = *(const f32x4*)(dlt_l + 32 * qb + 8 * r4 + 4 * h);
+        l4[qb][r4] = *(const f32x4*)(lse_l + 32 * qb + 8 * r4 + 4 * h);
+        d4[qb][r4] = *(const f32x4*)(dlt_l + 32 * qb + 8 * r4 + 4 * h);
+      }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = 4 * r4 + j;
-          const float pv = exp2_hw(__builtin_fmaf(sv[qb][r], p.c, -l4[j]));
-          sv[qb][r] = pv;
-          dv[qb][r] = pv * (dv[qb][r] - d4[j]);
+    for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sn[qb][r] = 0.f;
+        dn[qb][r] = 0.f;
+      }
+    bf16x8 qa = as_bf16x8(*(const u32x4*)(nxt + a_off[0]));
+    bf16x8 da = as_bf16x8(*(const u32x4*)(nxt + TB + a_off[0]));
+    bf16x8 pa[NQB][2], dsa[NQB][2];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < NPAIR; ++j) {
+      const int qb = j / T, t = j % T;
+      sn[qb] = mfma32(qa, kB[t], sn[qb]);
+      dn[qb] = mfma32(da, vB[t], dn[qb]);
+      if (j + 1 < NPAIR) {
+        const int qb1 = (j + 1) / T, t1 = (j + 1) % T;
+        qa = as_bf16x8(*(const u32x4*)(nxt + qb1 * 32 * RB + a_off[t1]));
+        da = as_bf16x8(*(const u32x4*)(nxt + TB + qb1 * 32 * RB + a_off[t1]));
+      }
+#pragma unroll
+      for (int e = j * EPP; e < (j + 1) * EPP; ++e) {
+        const int eq = e / 16, r = e % 16;
+        const float pv = exp2_hw(__builtin_fmaf(sv[eq][r], p.c, -l4[eq][r >> 2][r & 3]));
+        sv[eq][r] = pv;
+        dv[eq][r] = pv * (dv[eq][r] - d4[eq][r >> 2][r & 3]);
+        if ((r & 7) == 7) {
+          const int u = r >> 3;
+          u32x4 w1, w2;
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            w1[m] = pack_bf16x2(sv[eq][8 * u + 2 * m], sv[eq][8 * u + 2 * m + 1]);
+            w2[m] = pack_bf16x2(dv[eq][8 * u + 2 * m], dv[eq][8 * u + 2 * m + 1]);
+          }
+          pa[eq][u] = as_bf16x8(w1);
+          dsa[eq][u] = as_bf16x8(w2);
         }
       }
-      bf16x8 pa[2], dsa[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        u32x4 w1, w2;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          w1[j] = pack_bf16x2(sv[qb][8 * u + 2 * j], sv[qb][8 * u + 2 * j + 1]);
-          w2[j] = pack_bf16x2(dv[qb][8 * u + 2 * j], dv[qb][8 * u + 2 * j + 1]);
-        }
-        pa[u] = as_bf16x8(w1);
-        dsa[u] = as_bf16x8(w2);
-      }
-      // dV += P^T dO and dK += dS^T Q; B operands by transposing reads.
-#pragma unroll
-      for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int roff = (32 * qb + 16 * u) * RB;
-          const u32x2 olo = lds_read_tr16((const lds_void*)(dos_l + roff + tr_off[db][0]));
-          const u32x2 ohi = lds_read_tr16((const lds_void*)(dos_l + roff + tr_off[db][1]));
-          const u32x2 qlo = lds_read_tr16((const lds_void*)(qs_l + roff + tr_off[db][0]));
-          const u32x2 qhi = lds_read_tr16((const lds_void*)(qs_l + roff + tr_off[db][1]));
-          const u32x4 ob = {olo[0], olo[1], ohi[0], ohi[1]};
-          const u32x4 qbv = {qlo[0], qlo[1], qhi[0], qhi[1]};
-          dv_acc[db] = mfma32(pa[u], as_bf16x8(ob), dv_acc[db]);
-          dk_acc[db] = mfma32(dsa[u], as_bf16x8(qbv), dk_acc[db]);
-        }
-      // dS^T -> LDS: lane (key 32 wave + n) writes queries 32qb + 8g + 4h .. +4.
-      if constexpr (FUSED_DQ)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int col = 32 * qb + 8 * g4 + 4 * h;
-        const u32x4 dsw4 = as_u32x4(dsa[g4 >> 1]);
-        u32x2 w;
-        w[0] = dsw4[(g4 & 1) * 2];
-        w[1] = dsw4[(g4 & 1) * 2 + 1];
-        *(u32x2*)(dsw + ds_wrow * DSRB + (((col >> 3) ^ fd(ds_wrow)) * 16) + ((col >> 2) & 1) * 8) = w;
-      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+
+    // Phase B.  Pair index jb = (qb, u, db), db fastest so that consecutive
+    // MFMAs never accumulate into the same registers; operands of the next pair are read
+    // while the current pair runs.
+    constexpr int NB = NQB * ND * 2;
+    auto tr_operands = [&](int jb, u32x4& ob, u32x4& qbv) {
+      const int qb = jb / (2 * ND), u = (jb / ND) & 1, db = jb % ND;
+      const int roff = (32 * qb + 16 * u) * RB;
+      const u32x2 olo = lds_read_tr16((const lds_void*)(dos_l + roff + tr_off[db][0]));
+      const u32x2 ohi = lds_read_tr16((const lds_void*)(dos_l + roff + tr_off[db][1]));
+      const u32x2 qlo = lds_read_tr16((const lds_void*)(qs_l + roff + tr_off[db][0]));
+      const u32x2 qhi = lds_read_tr16((const lds_void*)(qs_l + roff + tr_off[db][1]));
+      ob = u32x4{olo[0], olo[1], ohi[0], ohi[1]};
+      qbv = u32x4{qlo[0], qlo[1], qhi[0], qhi[1]};
+    };
+    u32x4 ob, qbv;
+    tr_operands(0, ob, qbv);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int jb = 0; jb < NB; ++jb) {
+      const int qb = jb / (2 * ND), u = (jb / ND) & 1, db = jb % ND;
+      const u32x4 obc = ob, qbc = qbv;
+      if (jb + 1 < NB) tr_operands(jb + 1, ob, qbv);
+      dv_acc[db] = mfma32(pa[qb][u], as_bf16x8(obc), dv_acc[db]);
+      dk_acc[db] = mfma32(dsa[qb][u], as_bf16x8(qbc), dk_acc[db]);
+      // dS^T -> LDS: lane (key 32 wave + n) writes queries 32qb + 8g + 4h .. +4.
+      if constexpr (FUSED_DQ) {
+        if (db == 0 && u == 0) {
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int col = 32 * qb + 8 * g4 + 4 * h;
+            const u32x4 dsw4 = as_u32x4(dsa[qb][g4 >> 1]);
+            u32x2 w;
+            w[0] = dsw4[(g4 & 1) * 2];
+            w[1] = dsw4[(g4 & 1) * 2 + 1];
+            *(u32x2*)(dsw + ds_wrow * DSRB + (((col >> 3) ^ fd(ds_wrow)) * 16) + ((col >> 2) & 1) * 8) = w;
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    advance_cur();
   };
 
   f32x16 sA[NQB], dA[NQB], sB[NQB], dB[NQB];
   if (nsteps > 0) {
-    issue_step(0, stage0);
-    if (nsteps > 1) issue_step(1, stage1);
-    wait_vmcnt<0>();
+    issue_next(stage0);
+    if (nsteps > 1) issue_next(stage1);
+    if (nsteps > 2) issue_next(stage2);
+    // Step 0 complete: with three steps issued, two may still be in flight.
+    if (nsteps > 2) {
+      if (wave < 2) wait_vmcnt<4 * NLD + 2>();
+      else wait_vmcnt<4 * NLD>();
+    } else {
+      wait_vmcnt<0>();
+    }
     __syncthreads();
     compute_sdp(stage0, sA, dA);
   }
-  // Stages rotate with period 3 and the S/dP register sets with period 2.
-  for (int i = 0; i < nsteps; i += 6) {
-    body(i, stage0, stage1, stage2, dsbuf0, dsbuf2, sA, dA, sB, dB);
-    if (i + 1 < nsteps) body(i + 1, stage1, stage2, stage0, dsbuf1, dsbuf0, sB, dB, sA, dA);
-    if (i + 2 < nsteps) body(i + 2, stage2, stage0, stage1, dsbuf2, dsbuf1, sA, dA, sB, dB);
-    if (i + 3 < nsteps) body(i + 3, stage0, stage1, stage2, dsbuf0, dsbuf2, sB, dB, sA, dA);
-    if (i + 4 < nsteps) body(i + 4, stage1, stage2, stage0, dsbuf1, dsbuf0, sA, dA, sB, dB);
-    if (i + 5 < nsteps) body(i + 5, stage2, stage0, stage1, dsbuf2, dsbuf1, sB, dB, sA, dA);
+  // Stages rotate with period 4, S/dP register sets and dS^T buffers with
+  // period 2.  The main loop has no bounds checks between bodies, so the
+  // register sets keep their places; the tail checks each step.
+  int i = 0;
+  for (; i + 4 <= nsteps; i += 4) {
+    body(i, stage0, stage1, stage3, dsbuf0, dsbuf1, sA, dA, sB, dB);
+    body(i + 1, stage1, stage2, stage0, dsbuf1, dsbuf0, sB, dB, sA, dA);
+    body(i + 2, stage2, stage3, stage1, dsbuf0, dsbuf1, sA, dA, sB, dB);
+    body(i + 3, stage3, stage0, stage2, dsbuf1, dsbuf0, sB, dB, sA, dA);
   }
+  if (i < nsteps) body(i, stage0, stage1, stage3, dsbuf0, dsbuf1, sA, dA, sB, dB);
+  if (i + 1 < nsteps) body(i + 1, stage1, stage2, stage0, dsbuf1, dsbuf0, sB, dB, sA, dA);
+  if (i + 2 < nsteps) body(i + 2, stage2, stage3, stage1, dsbuf0, dsbuf1, sA, dA, sB, dB);
   if (FUSED_DQ && nsteps > 0) {
     __syncthreads();
-    const int last = (nsteps - 1) % 3;
-    dq_step(nsteps - 1, last == 0 ? dsbuf0 : (last == 1 ? dsbuf1 : dsbuf2));
+    dq_step(prev_g, prev_qs, ((nsteps - 1) & 1) ? dsbuf1 : dsbuf0);
   }
 
   // ---- dK (scaled) and dV of this wave's 32 keys ----------------------------
