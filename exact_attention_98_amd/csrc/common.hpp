@@ -74,6 +74,10 @@ __device__ __forceinline__ rsrc_t make_rsrc_uniform(const void* base, uint32_t b
   const uint32_t nb = __builtin_amdgcn_readfirstlane(bytes);
   return make_rsrc((const void*)(((uint64_t)hi << 32) | lo), nb);
 }
+// Makes a value opaque at this point in program order: it must be computed
+// before here and cannot be moved past or re-associated across this point.
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(u32x4& x) { asm volatile("" : "+v"(x)); }
 // Keeps the compiler from turning the guarded block into selects that run on
 // every path (used for rare, wave-uniform branches).
 __device__ __forceinline__ void keep_branch() { asm volatile("" ::: "memory"); }

@@ -53,11 +53,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
   constexpr int TB = BN * RB;           // bytes per K (or V) tile
   constexpr int NLD = TB / 1024 / kFwdWaves;  // 1 KiB direct loads per wave per tensor
   static_assert(NLD >= 1, "tile too small");
-  // Two stages of [K, V] tiles, as two arrays: with the stage known at compile
-  // time the compiler can tell the in-flight copy into one stage from reads of
-  // the other, and does not wait for the copy before those reads.
-  __shared__ __attribute__((aligned(1024))) char stage0[2 * TB];
-  __shared__ __attribute__((aligned(1024))) char stage1[2 * TB];
+  // K and V tiles double-buffered separately, each buffer its own array so the
+  // compiler can tell an in-flight copy into one from reads of another.  While
+  // tile kt is finished (P(kt), O += V(kt) P(kt)), S(kt+1) is computed from
+  // K(kt+1); the copies of K(kt+2) and V(kt+1) are in flight.
+  __shared__ __attribute__((aligned(1024))) char kbuf0[TB];
+  __shared__ __attribute__((aligned(1024))) char kbuf1[TB];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[TB];
+  __shared__ __attribute__((aligned(1024))) char vbuf1[TB];
 
   // Grid order: consecutive workgroup ids walk heads first, so with B*Hq a
   // multiple of 8 every tile of a head lands on the same XCD (ids are dealt to
@@ -96,6 +99,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
   float m_ref = -__builtin_inff();
   float l_part = 0.f;  // this lane half's share of the row sum
 
+  // Every wave walks all tiles of the workgroup; a tile wholly above a wave's
+  // diagonal is masked to -inf and adds exactly nothing (at most one such tile
+  // per wave, kept so the pipeline has no per-wave branch).
   const int kend = CAUSAL ? min(p.N, q0 + BM) : p.N;
   const int ntiles = (kend + BN - 1) / BN;
 
@@ -110,20 +116,15 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
     const int row = g / KCH, pc = g % KCH;
     ld_off[s] = (uint32_t)(row * RB + ((pc ^ tile_swz<D>(row)) * 16));
   }
-  auto issue_tile = [&](int kt, char* ks) {
+  auto issue = [&](const uint16_t* src, int kt, char* dst) {
     const uint32_t base = (uint32_t)kt * TB;
     const uint32_t left = head_bytes > base ? head_bytes - base : 0u;
-    const rsrc_t kr = make_rsrc_uniform((const char*)Kh + base, left);
-    const rsrc_t vr = make_rsrc_uniform((const char*)Vh + base, left);
-    char* vs = ks + TB;
+    const rsrc_t r = make_rsrc_uniform((const char*)src + base, left);
 #pragma unroll
-    for (int s = 0; s < NLD; ++s) {
-      lds_dma16(kr, (lds_void*)(ks + (s * kFwdWaves + wave) * 1024), ld_off[s]);
-      lds_dma16(vr, (lds_void*)(vs + (s * kFwdWaves + wave) * 1024), ld_off[s]);
-    }
+    for (int s = 0; s < NLD; ++s) lds_dma16(r, (lds_void*)(dst + (s * kFwdWaves + wave) * 1024), ld_off[s]);
   };
 
-  // Per-lane LDS read offsets (stage, sub-block and step offsets are constants).
+  // Per-lane LDS read offsets (buffer, sub-block and step offsets are constants).
   // K (A operand of S^T): row n (+32 sb), logical chunk 2t + h.
   uint32_t k_off[D / 16];
 #pragma unroll
@@ -145,31 +146,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
     }
   }
 
-  // One tile: wait for its copy, start the next tile's copy into the other
-  // stage, compute.
-  auto tile = [&](int kt, const char* ks, char* next) {
-    wait_vmcnt<0>();
-    __syncthreads();  // tile kt is in LDS; everyone is done with tile kt-1
-    if (kt + 1 < ntiles) issue_tile(kt + 1, next);
+  constexpr int T = D / 16;
+  // Mask keys past the end and, under causal, keys after the query, on the
+  // tiles that need it.  Register r of half sb holds key
+  // k0 + 32 sb + 8 (r/4) + 4 h + r % 4.
+  auto mask = [&](int kt, f32x16 (&sv)[2]) {
     const int k0 = kt * BN;
-    // Tiles wholly above this wave's diagonal contribute nothing.
-    if (CAUSAL && k0 > qw + 31) return;
-    const char* vs = ks + TB;
-
-    // S^T for the two 32-key halves of the tile.
-    f32x16 s[2];
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[sb][r] = 0.f;
-#pragma unroll
-      for (int t = 0; t < D / 16; ++t) {
-        const bf16x8 a = as_bf16x8(*(const u32x4*)(ks + sb * 32 * RB + k_off[t]));
-        s[sb] = mfma32(a, qf[t], s[sb]);
-      }
-    }
-    // Mask keys past the end and, under causal, keys after the query.
-    // Register r of half sb holds key k0 + 32 sb + 8 (r/4) + 4 h + r % 4.
     if ((k0 + BN > p.N) || (CAUSAL && (k0 + BN - 1 > qw))) {
       keep_branch();
       int lim = p.N - 1 - k0 - 4 * h;
@@ -178,18 +160,23 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (32 * sb + 8 * (r >> 2) + (r & 3) > lim) s[sb][r] = -__builtin_inff();
+          if (32 * sb + 8 * (r >> 2) + (r & 3) > lim) sv[sb][r] = -__builtin_inff();
     }
-    // Row max of this tile (both halves end with the full-row value).
-    float mx = __builtin_fmaxf(s[0][0], s[0][1]);
+  };
+  // Row max of a masked S^T tile (in-lane, then across the lane halves) and
+  // the wave's rescale decision: m_new is the candidate new reference.
+  auto row_max = [&](const f32x16 (&sv)[2], float& m_new) {
+    float mx = __builtin_fmaxf(sv[0][0], sv[0][1]);
 #pragma unroll
-    for (int r = 2; r < 16; r += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(s[0][r], s[0][r + 1]));
+    for (int r = 2; r < 16; r += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(sv[0][r], sv[0][r + 1]));
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(s[1][r], s[1][r + 1]));
+    for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(sv[1][r], sv[1][r + 1]));
     mx = xhalf_max(mx);
-    const float m_new = __builtin_fmaxf(m_ref, mx * p.c);
-    // Conditional rescale: taken by the whole wave when any of its rows' max
-    // grew by more than tau; each row then moves to its own new max.
+    m_new = __builtin_fmaxf(m_ref, mx * p.c);
+  };
+  // Conditional rescale: taken by the whole wave when any of its rows' max
+  // grew by more than tau; each row then moves to its own new max.
+  auto rescale = [&](float m_new) {
     if (__builtin_amdgcn_ballot_w64(m_new > m_ref + kTau) != 0) {
       const float alpha = (m_new == -__builtin_inff()) ? 1.f : exp2_hw(m_ref - m_new);
       l_part *= alpha;
@@ -199,47 +186,126 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
         for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
       m_ref = m_new;
     }
+  };
+
+  // One tile kt.  sv holds S^T(kt), masked, with m_new its candidate max; sn
+  // receives S^T(kt+1).  Issue order is fixed by hand (sched_barrier fences):
+  // the MFMA unit runs one instruction at a time in program order, so each
+  // matrix instruction is followed by VALU work that runs under it.
+  auto body = [&](int kt, const char* kn, const char* vc, char* kld, char* vld, f32x16 (&sv)[2],
+                  f32x16 (&sn)[2], float& m_new) {
+    wait_vmcnt<0>();
+    __syncthreads();  // K(kt+1), V(kt) in LDS; tile kt-1's buffers are free
+    if (kt + 2 < ntiles) issue(Kh, kt + 2, kld);
+    if (kt + 1 < ntiles) issue(Vh, kt + 1, vld);
+    rescale(m_new);
     const float msub = (m_ref == -__builtin_inff()) ? 0.f : m_ref;
-    // P^T = exp2(S^T c - m_ref), row sum, and bf16 B operands.
+
+    // Phase A: the 16 MFMAs of S^T(kt+1) (on a stale buffer after the last
+    // tile, results unused), each pair with 4 elements of P^T(kt) =
+    // exp2(S^T c - m_ref), the row sum and the bf16 packing.
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sn[sb][r] = 0.f;
     bf16x8 pb[2][2];
+    bf16x8 ka = as_bf16x8(*(const u32x4*)(kn + k_off[0]));
+    bf16x8 kb2 = as_bf16x8(*(const u32x4*)(kn + k_off[1]));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < T; ++j) {
+      // MFMA pair j: sub-block j / (T/2), k-steps 2 (j % (T/2)) and +1.
+      const int sb = j / (T / 2), t = 2 * (j % (T / 2));
+      sn[sb] = mfma32(ka, qf[t], sn[sb]);
+      const bf16x8 kc = kb2;
+      if (j + 1 < T) {
+        const int sb1 = (j + 1) / (T / 2), t1 = 2 * ((j + 1) % (T / 2));
+        ka = as_bf16x8(*(const u32x4*)(kn + sb1 * 32 * RB + k_off[t1]));
+        kb2 = as_bf16x8(*(const u32x4*)(kn + sb1 * 32 * RB + k_off[t1 + 1]));
+      }
+      sn[sb] = mfma32(kc, qf[t + 1], sn[sb]);
+#pragma unroll
+      for (int e = j * (32 / T); e < (j + 1) * (32 / T); ++e) {
+        const int esb = e / 16, r = e % 16;
+        const float x = __builtin_fmaf(sv[esb][r], p.c, -msub);
+        const float ev = ((r & 3) < POLYQ) ? exp2_poly(x) : exp2_hw(x);
+        sv[esb][r] = ev;
+        l_part += ev;
+        if ((r & 7) == 7) {
+          const int u = r >> 3;
+          u32x4 w;
+#pragma unroll
+          for (int m = 0; m < 4; ++m) w[m] = pack_bf16x2(sv[esb][8 * u + 2 * m], sv[esb][8 * u + 2 * m + 1]);
+          pin(w);
+          pb[esb][u] = as_bf16x8(w);
+        }
+      }
+      pin(l_part);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    mask(kt + 1, sn);
+
+    // Phase B: O^T += V^T P^T(kt), A operand = keys 32 sb + 16 u + 8 rd + 4 h
+    // (0..3) of column d = 32 db + n by two transposing reads, one MFMA ahead;
+    // the row max of S^T(kt+1) is spread over it.
+    constexpr int NB = (D / 32) * 4;
+    // MFMA jb: d block db = jb % (D/32) (fastest, so consecutive MFMAs never
+    // accumulate into the same registers), key quarter (sb, u) = jb / (D/32).
+    auto vread = [&](int jb) {
+      const int db = jb % (D / 32), sb = (jb / (D / 32)) >> 1, u = (jb / (D / 32)) & 1;
+      const char* base = vc + (32 * sb + 16 * u) * RB;
+      const u32x2 lo = lds_read_tr16((const lds_void*)(base + v_off[db][0]));
+      const u32x2 hi = lds_read_tr16((const lds_void*)(base + v_off[db][1]));
+      return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+    };
+    bf16x8 va = vread(0);
+    float mx = -__builtin_inff();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int jb = 0; jb < NB; ++jb) {
+      const int db = jb % (D / 32), sb = (jb / (D / 32)) >> 1, u = (jb / (D / 32)) & 1;
+      const bf16x8 vcur = va;
+      if (jb + 1 < NB) va = vread(jb + 1);
+      oacc[db] = mfma32(vcur, pb[sb][u], oacc[db]);
+#pragma unroll
+      for (int e = jb * (32 / NB); e < (jb + 1) * (32 / NB); ++e)
+        mx = __builtin_fmaxf(mx, sn[e / 16][e % 16]);
+      pin(mx);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    mx = xhalf_max(mx);
+    m_new = __builtin_fmaxf(m_ref, mx * p.c);
+  };
+
+  f32x16 sA[2], sB[2];
+  float m_new = -__builtin_inff();
+  if (ntiles > 0) {
+    issue(Kh, 0, kbuf0);
+    issue(Vh, 0, vbuf0);
+    if (ntiles > 1) issue(Kh, 1, kbuf1);
+    wait_vmcnt<0>();
+    __syncthreads();
+    // S^T(0), its mask and row max.
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float x = __builtin_fmaf(s[sb][r], p.c, -msub);
-        const float e = ((r & 3) < POLYQ) ? exp2_poly(x) : exp2_hw(x);
-        s[sb][r] = e;
-        l_part += e;
-      }
+      for (int r = 0; r < 16; ++r) sA[sb][r] = 0.f;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        u32x4 w;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) w[j] = pack_bf16x2(s[sb][8 * u + 2 * j], s[sb][8 * u + 2 * j + 1]);
-        pb[sb][u] = as_bf16x8(w);
-      }
+      for (int t = 0; t < T; ++t)
+        sA[sb] = mfma32(as_bf16x8(*(const u32x4*)(kbuf0 + sb * 32 * RB + k_off[t])), qf[t], sA[sb]);
     }
-    // O^T += V^T P^T: A operand = keys 32 sb + 16 u + 8 rd + 4 h + (0..3) of
-    // column d = 32 db + n, two transposing reads per operand.
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const char* base = vs + (32 * sb + 16 * u) * RB;
-          const u32x2 lo = lds_read_tr16((const lds_void*)(base + v_off[db][0]));
-          const u32x2 hi = lds_read_tr16((const lds_void*)(base + v_off[db][1]));
-          const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-          oacc[db] = mfma32(as_bf16x8(a), pb[sb][u], oacc[db]);
-        }
-  };
-
-  if (ntiles > 0) issue_tile(0, stage0);
-  for (int kt = 0; kt < ntiles; kt += 2) {
-    tile(kt, stage0, stage1);
-    if (kt + 1 < ntiles) tile(kt + 1, stage1, stage0);
+    mask(0, sA);
+    row_max(sA, m_new);
   }
+  // Buffers alternate with the tile parity: K(kt+1) in kbuf[(kt+1)&1], V(kt)
+  // in vbuf[kt&1]; the copies go to kbuf[kt&1] and vbuf[(kt+1)&1].
+  int kt = 0;
+  for (; kt + 2 <= ntiles; kt += 2) {
+    body(kt, kbuf1, vbuf0, kbuf0, vbuf1, sA, sB, m_new);
+    body(kt + 1, kbuf0, vbuf1, kbuf1, vbuf0, sB, sA, m_new);
+  }
+  if (kt < ntiles) body(kt, kbuf1, vbuf0, kbuf0, vbuf1, sA, sB, m_new);
 
   // Final correction: O = O / l, LSE = (m_ref + log2 l) ln 2.  Rows past N are
   // dropped by the buffer range.
