@@ -348,9 +348,11 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
     const int q0 = cur_qs * QS;
     // Causal mask of step i, only near the diagonal: S = -inf where key > query.
     // Register r of block qb holds query q0 + 32qb + 8(r/4) + 4h + r%4.
-    if (CAUSAL && (q0 < kw + 31)) {
+    // Padding keys (key >= N, rows read as zero) are masked too: their score 0
+    // can exceed every real score and overflow P.
+    if ((CAUSAL && (q0 < kw + 31)) || (kw + 32 > p.N)) {
       keep_branch();
-      const int lim = key - q0 - 4 * h;
+      const int lim = (key >= p.N) ? 1 << 30 : (CAUSAL ? key - q0 - 4 * h : -1);
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
@@ -648,8 +650,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t* __restri
       }
     }
     // Register r of half sb holds key k0 + 32 sb + 8 (r/4) + 4 h + r % 4.
-    const bool need_mask = CAUSAL && (k0 + BN - 1 > qw);
-    const int lim = qi - k0 - 4 * h;
+    // Causal mask, and padding keys (key >= N, rows read as zero, whose score
+    // 0 can exceed every real score).
+    const bool need_mask = (CAUSAL && (k0 + BN - 1 > qw)) || (k0 + BN > p.N);
+    const int lim = CAUSAL ? min(qi, p.N - 1) - k0 - 4 * h : p.N - 1 - k0 - 4 * h;
     bf16x8 dsb[2][2];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {

@@ -209,21 +209,20 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
 #pragma unroll
       for (int r = 0; r < 16; ++r) sn[sb][r] = 0.f;
     bf16x8 pb[2][2];
+    // MFMA pair j = k-step t: sub-blocks 0 and 1 alternate, so consecutive
+    // MFMAs never accumulate into the same registers.
     bf16x8 ka = as_bf16x8(*(const u32x4*)(kn + k_off[0]));
-    bf16x8 kb2 = as_bf16x8(*(const u32x4*)(kn + k_off[1]));
+    bf16x8 kb2 = as_bf16x8(*(const u32x4*)(kn + 32 * RB + k_off[0]));
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < T; ++j) {
-      // MFMA pair j: sub-block j / (T/2), k-steps 2 (j % (T/2)) and +1.
-      const int sb = j / (T / 2), t = 2 * (j % (T / 2));
-      sn[sb] = mfma32(ka, qf[t], sn[sb]);
+      sn[0] = mfma32(ka, qf[j], sn[0]);
       const bf16x8 kc = kb2;
       if (j + 1 < T) {
-        const int sb1 = (j + 1) / (T / 2), t1 = 2 * ((j + 1) % (T / 2));
-        ka = as_bf16x8(*(const u32x4*)(kn + sb1 * 32 * RB + k_off[t1]));
-        kb2 = as_bf16x8(*(const u32x4*)(kn + sb1 * 32 * RB + k_off[t1 + 1]));
+        ka = as_bf16x8(*(const u32x4*)(kn + k_off[j + 1]));
+        kb2 = as_bf16x8(*(const u32x4*)(kn + 32 * RB + k_off[j + 1]));
       }
-      sn[sb] = mfma32(kc, qf[t + 1], sn[sb]);
+      sn[1] = mfma32(kc, qf[j], sn[1]);
 #pragma unroll
       for (int e = j * (32 / T); e < (j + 1) * (32 / T); ++e) {
         const int esb = e / 16, r = e % 16;

@@ -87,3 +87,29 @@ def test_full_size_config(name):
         s = dk.double().sum(dim=2).abs().max().item()
         scale_ref = dk.double().abs().sum(dim=2).max().item()
         assert s <= 2e-2 * scale_ref, (tag, s, scale_ref)
+
+
+@pytest.mark.parametrize("deterministic", [False, True])
+@pytest.mark.parametrize("D", [64, 128])
+def test_padding_keys_with_very_negative_scores(D, deterministic):
+    # Non-causal, N not a multiple of any tile: the padding key rows read as
+    # zero give the score 0, far above every real score (about -150 +- 20
+    # here, so every row's LSE is below -90), and an unmasked padding key would
+    # get P = exp(> 88.7) = inf in fp32 and dQ = inf * 0.  K's noise is as large
+    # as its offset so that dQ = scale * sum_j dS_ij K_j is not a cancellation
+    # of bf16-rounded terms.
+    say(f"bwd padding keys, scores near -150, N130 D{D} det={deterministic}")
+    B, H, N = 1, 2, 130
+    g = torch.Generator().manual_seed(11)
+    scale = 1.0 / math.sqrt(D)
+    k = (1.0 + torch.randn(B, H, N, D, generator=g)).to(torch.bfloat16)
+    q = (-150.0 / (D * scale) + 0.1 * torch.randn(B, H, N, D, generator=g)).to(torch.bfloat16)
+    v = torch.randn(B, H, N, D, generator=g).to(torch.bfloat16)
+    do = torch.randn(B, H, N, D, generator=g).to(torch.bfloat16)
+    (dq, dk, dv), = run_bwd(q, k, v, do, False, scale, deterministic)
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t.float()).all()
+    rq, rk, rv = oracle.attention_bwd(q, k, v, do, False, scale)
+    check_grad(dq, rq, "dQ")
+    check_grad(dk, rk, "dK")
+    check_grad(dv, rv, "dV")
