@@ -35,7 +35,15 @@ KERNEL_SOURCES = {
                         "exact_attention_98_amd/csrc/common.hpp"],
     "bwd_dq_kernel": ["exact_attention_98_amd/csrc/bwd_kernels.hip",
                       "exact_attention_98_amd/csrc/common.hpp"],
+    "bwd_dq_ds_kernel": ["exact_attention_98_amd/csrc/bwd_kernels.hip",
+                         "exact_attention_98_amd/csrc/common.hpp"],
 }
+# dQ modes of the backward (the deterministic argument of fa_bwd) and the
+# kernel that finishes dQ in each.
+DQ_MODES = {"stored": 1, "recompute": 2, "atomic": 0}
+DQ_KERNEL = {0: "bwd_dq_convert_kernel", 1: "bwd_dq_ds_kernel", 2: "bwd_dq_kernel"}
+DQ_LABEL = {0: "atomic", 1: "fixed order from stored dS (deterministic)",
+            2: "fixed order, dS recomputed (deterministic)"}
 
 
 def log(msg: str):
@@ -50,15 +58,16 @@ def source_digest(kernel: str) -> str:
     return h.hexdigest()
 
 
-def load_traffic(kernel: str):
+def load_traffic(kernel: str, dq_mode: int):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; otherwise None."""
+    was taken on the current kernel source (and, for the backward, in the same
+    dQ mode); otherwise None."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
-    if not os.path.exists(path):
+    if not os.path.exists(path) or kernel not in KERNEL_SOURCES:
         return None
     with open(path) as f:
         rec = json.load(f)
-    if kernel == "bwd_main_kernel" and not rec.get("kernel", "").endswith("fixed-order dQ mode)"):
+    if kernel != "fwd_kernel" and rec.get("dq_mode") != dq_mode:
         return None
     if rec.get("source_sha256") != source_digest(kernel):
         return None
@@ -86,8 +95,10 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--dq-mode", choices=["fixed", "atomic"], default="fixed",
-                    help="backward dQ: fixed-order pass (deterministic, default) or atomic adds")
+    ap.add_argument("--dq-mode", choices=list(DQ_MODES), default="stored",
+                    help="backward dQ: fixed order from stored dS blocks (deterministic, "
+                         "default), fixed order recomputing dS (deterministic, small "
+                         "workspace), or atomic adds")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=16)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -120,7 +131,7 @@ def main() -> int:
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    det = 1 if args.dq_mode == "fixed" else 0
+    det = DQ_MODES[args.dq_mode]
     ws_bytes = fa.fa_bwd_workspace_size(B, Hq, Hkv, N, D, det)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -133,7 +144,7 @@ def main() -> int:
         if rc != 0:
             raise RuntimeError(f"{what}: {fa.fa_strerror(rc)}")
 
-    dq_name = "bwd_dq_kernel" if det else "bwd_dq_convert_kernel"
+    dq_name = DQ_KERNEL[det]
     names = ["fwd_kernel", "bwd_pre_kernel", "bwd_main_kernel", dq_name]
 
     def step(ev):
@@ -197,9 +208,10 @@ def main() -> int:
     # Dominant kernel and its roofline (bf16 MFMA bound: attention is a dense
     # contraction).  Algorithmic FLOPs per launch: the forward does its 2
     # products (f_fwd); the backward's 5 products are f_bwd, of which the main
-    # kernel does 4 (S, dP, dV, dK) in fixed-order mode and all 5 in atomic
-    # mode.  The fixed-order dQ kernel's algorithmic share is the dQ product
-    # (1 of 5); its S and dP recompute is overhead, not algorithmic work.
+    # kernel does 4 (S, dP, dV, dK) in the fixed-order modes and all 5 in
+    # atomic mode.  A fixed-order dQ kernel's algorithmic share is the dQ
+    # product (1 of 5); the recompute mode's S and dP are overhead, not
+    # algorithmic work.
     algo_flops = {"fwd_kernel": f_fwd, "bwd_main_kernel": f_bwd * (0.8 if det else 1.0),
                   dq_name: f_bwd * 0.2 if det else 0.0}
     dom = max(("fwd_kernel", "bwd_main_kernel", dq_name), key=lambda n: per_kernel[n])
@@ -207,7 +219,7 @@ def main() -> int:
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": load_traffic(dom),
+                "traffic": load_traffic(dom, det),
                 "avg_launch_us": round(per_kernel[dom] * 1e3, 1)}
 
     out = {
@@ -217,7 +229,7 @@ def main() -> int:
         "data": "synthetic (seeded N(0,1) bf16 Q, K, V, dO)",
         "config": {"workload": "attention forward+backward, B2 Hq16 Hkv16 N8192 D128 causal",
                    "B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "D": D, "causal": True,
-                   "dq_accumulation": "fixed-order (deterministic)" if det else "atomic",
+                   "dq_accumulation": DQ_LABEL[det],
                    "flops_per_step": f_fwd + f_bwd},
         "roofline": roofline,
         "fwd": {"tflops": round(fwd_tf, 1), "frac_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
@@ -228,29 +240,34 @@ def main() -> int:
                                for n in names[1:]}},
         "host_wall_ms_per_step": round(wall / args.steps * 1e3, 4),
     }
-    # The other dQ mode, timed on the same inputs for comparison.
-    odet = 1 - det
-    ows_bytes = fa.fa_bwd_workspace_size(B, Hq, Hkv, N, D, odet)
-    ows = torch.empty(ows_bytes, dtype=torch.uint8, device=dev)
+    # The other dQ modes, timed on the same inputs for comparison (whole
+    # fa_bwd call).
+    out["bwd_other_modes"] = []
+    for odet in sorted(set(DQ_MODES.values()) - {det}):
+        ows_bytes = fa.fa_bwd_workspace_size(B, Hq, Hkv, N, D, odet)
+        ows = torch.empty(ows_bytes, dtype=torch.uint8, device=dev)
 
-    def obwd():
-        check(fa.fa_bwd(P["q"], P["k"], P["v"], P["o"], P["lse"], P["do"], P["dq"], P["dk"], P["dv"],
-                        B, Hq, Hkv, N, D, 1, w.scale, ows.data_ptr(), ows_bytes, odet, sh), "fa_bwd")
+        def obwd():
+            check(fa.fa_bwd(P["q"], P["k"], P["v"], P["o"], P["lse"], P["do"], P["dq"], P["dk"],
+                            P["dv"], B, Hq, Hkv, N, D, 1, w.scale, ows.data_ptr(), ows_bytes, odet,
+                            sh), "fa_bwd")
 
-    for _ in range(2):
-        obwd()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(5):
-        obwd()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    o_ms = e0.elapsed_time(e1) / 5
-    out["bwd_other_mode"] = {"dq_accumulation": "atomic" if det else "fixed-order (deterministic)",
-                             "us": round(o_ms * 1e3, 1),
-                             "tflops": round(f_bwd / (o_ms * 1e-3) / 1e12, 1)}
-    del ows
+        for _ in range(2):
+            obwd()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(5):
+            obwd()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        o_ms = e0.elapsed_time(e1) / 5
+        out["bwd_other_modes"].append({"dq_accumulation": DQ_LABEL[odet],
+                                       "us": round(o_ms * 1e3, 1),
+                                       "tflops": round(f_bwd / (o_ms * 1e-3) / 1e12, 1),
+                                       "workspace_bytes": ows_bytes})
+        del ows
+    out["bwd"]["workspace_bytes"] = ws_bytes
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_heads} heads")
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)

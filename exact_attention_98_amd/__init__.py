@@ -166,9 +166,14 @@ def forward(q, k, v, causal: bool, scale: float, *, exp_poly_quarters: int | Non
     return out, lse
 
 
-def backward(q, k, v, o, lse, dout, causal: bool, scale: float, *, deterministic: bool = False,
+def backward(q, k, v, o, lse, dout, causal: bool, scale: float, *, deterministic=False,
              workspace=None, dq=None, dk=None, dv=None):
-    """dQ, dK, dV (bf16) for the forward's inputs/outputs and dO."""
+    """dQ, dK, dV (bf16) for the forward's inputs/outputs and dO.
+
+    deterministic selects the dQ mode of fa_bwd: 0 / False atomic; 1 / True
+    fixed order from stored dS blocks (largest workspace); 2 fixed order,
+    recomputing dS (smallest workspace).
+    """
     import torch
     B, Hq, N, D = q.shape
     Hkv = k.shape[1]

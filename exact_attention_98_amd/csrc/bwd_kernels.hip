@@ -6,13 +6,17 @@
 //   S  = Q K^T              P  = exp2(S c - LSE log2 e)
 //   dP = dO V^T             dS = P o (dP - Delta),  Delta_i = dO_i . O_i
 //   dV += P^T dO            dK += dS^T Q            dQ += dS K
-// dK and dV of a key tile are owned by one workgroup.  dQ has two modes
-// (danialwang explainer, sections 05-06):
+// dK and dV of a key tile are owned by one workgroup.  dQ has three modes
+// (atomic and fixed-order accumulation: danialwang explainer, sections 05-06):
 //   atomic        the main kernel also forms dQ += dS K for its key tile and
 //                 adds it into an fp32 workspace with atomics;
-//   fixed order   a separate kernel owns each query tile, walks the key tiles
-//                 in ascending order recomputing S, dP and dS, and writes dQ
-//                 once: no atomics, so the result is bit-identical run to run.
+//   stored dS     the main kernel writes its bf16 dS blocks to the workspace
+//                 and a separate kernel owns each query tile, sums dS K over
+//                 the key tiles in ascending order and writes dQ once;
+//   recompute     like stored dS, but the dQ kernel recomputes S, dP and dS
+//                 instead of reading them (small workspace).
+// The two fixed-order modes use no atomics, so their results are
+// bit-identical run to run.
 //
 // Layout choices.  S is computed with keys as the MFMA accumulator's column
 // (lane) index.  Its accumulator registers are then, unchanged, the A operand
@@ -44,10 +48,24 @@ struct BwdParams {
   int nqs;         // query steps per head
   float c;         // scale * log2(e)
   float scale;
-  float* dq_acc;   // fp32 [B][Hq][N][D]
+  float* dq_acc;   // fp32 [B][Hq][N][D] (atomic mode)
   float* delta;    // fp32 [B][Hq][N]
   float* lse2;     // fp32 [B][Hq][N]
+  char* ds;        // dS^T blocks (stored-dS mode), ds_head bytes per (b, hq)
+  uint32_t ds_head;
+  int nb32;        // 32-row blocks per head, ceil(N / 32)
 };
+
+// dQ modes (the deterministic argument of the C ABI).
+constexpr int kDqAtomic = 0;     // main kernel adds dS K into an fp32 buffer
+constexpr int kDqStored = 1;     // main kernel stores dS; a fixed-order pass forms dS K
+constexpr int kDqRecompute = 2;  // a fixed-order pass recomputes S, dP, dS and forms dS K
+
+// Stored-dS layout: per (b, hq), block (query block qb32, key block kb32) of
+// 32 x 32 at byte (qb32 * nb32 + kb32) * 2048, as dS^T: 32 rows of keys, 64
+// bytes each.  Within a row, position p = 16u + 8h + i holds query
+// 16u + 4h + (i & 3) + 8 (i >> 2) of the block (the order of the main
+// kernel's MFMA A-operand registers, stored unchanged).
 
 // ---------------------------------------------------------------------------
 // Preprocess: Delta_i = sum_d dO[i,d] O[i,d] (fp32), LSE_i * log2(e), and
@@ -87,12 +105,13 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// Main backward kernel: dK, dV and, with FUSED_DQ, atomic dQ.  Workgroup =
+// Main backward kernel: dK, dV and, by dQ mode, atomic dQ or stored dS
+// blocks.  Workgroup =
 // (batch, K/V head, key tile of 128); wave w owns keys 32w..32w+31 of the
 // tile.  Query steps of QS = 4096 / D queries (32 for D = 128, 64 for D = 64)
 // are walked from the last one down to the first that meets the tile's
 // diagonal, for each of the G query heads.
-template <int D, bool CAUSAL, bool FUSED_DQ>
+template <int D, bool CAUSAL, int DQM>
 __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
@@ -108,6 +127,8 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
   constexpr int DSB = BN * QS * 2;    // bytes of one dS^T buffer [key][query]
   constexpr int DSRB = QS * 2;        // bytes per dS^T row
   static_assert(NQB * ND == kBwdWaves, "one dQ output block per wave");
+  constexpr bool FUSED_DQ = DQM == kDqAtomic;
+  constexpr bool STORE_DS = DQM == kDqStored;
   static_assert(NLD >= 1, "step tile too small");
 
   // Per stage: Q tile, dO tile, 256 B of LSE*log2e, 256 B of Delta; then (atomic
@@ -313,6 +334,30 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
     }
   };
 
+  // Stored-dS mode: this wave's dS^T blocks of one step, 32 keys x 32 queries
+  // per block, 16 bytes per lane and block half u (lane of key n, half h:
+  // positions 16u + 8h .. +8 of row n).  Blocks that do not exist (padding
+  // rows, or above the diagonal under causal) get an offset past the end of
+  // the head's range and the store is dropped.
+  u32x4 ds_keep[NQB][2];
+  const int kb32 = kw / 32;
+  const uint32_t ds_lane = (uint32_t)(n * 64 + h * 16);
+  auto store_ds = [&](int g, int qs) {
+    if constexpr (STORE_DS) {
+      const rsrc_t r = make_rsrc_uniform(p.ds + ((size_t)b * p.Hq + hq0 + g) * p.ds_head, p.ds_head);
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        const int qb32 = qs * NQB + qb;
+        const bool ok = qb32 < p.nb32 && kb32 < p.nb32 && (!CAUSAL || kb32 <= qb32);
+        const uint32_t off = ok ? (uint32_t)(qb32 * p.nb32 + kb32) * 2048u : 0xFFFFF000u;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          // Plain (cached) stores: measured faster here than non-temporal ones.
+          __builtin_amdgcn_raw_buffer_store_b128(ds_keep[qb][u], r, off + ds_lane + 32u * u, 0, 0);
+      }
+    }
+  };
+
   // S and dP of one step (A operands Q, dO by row reads of its stage).
   auto compute_sdp = [&](const char* st, f32x16 (&sv)[NQB], f32x16 (&dv)[NQB]) {
 #pragma unroll
@@ -342,6 +387,10 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
     if (i + 2 < nsteps) wait_all_but_one_step();
     else wait_vmcnt<0>();
     __syncthreads();  // step i+1 visible to all; step i-1's stage and dS^T free
+    // Stored-dS mode: step i-1's dS blocks go out before step i+3's copies,
+    // so the copies are the newest memory operations when the next step
+    // waits for its own (loads complete in order; stores need not).
+    if (STORE_DS && i > 0) store_ds(prev_g, prev_qs);
     if (i + 3 < nsteps) issue_next(ld);
     if (FUSED_DQ && i > 0) dq_step(prev_g, prev_qs, dsprev);
 
@@ -425,6 +474,13 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
       __builtin_amdgcn_sched_barrier(0);
     }
 
+    if constexpr (STORE_DS)
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        ds_keep[qb][0] = as_u32x4(dsa[qb][0]);
+        ds_keep[qb][1] = as_u32x4(dsa[qb][1]);
+      }
+
     // Phase B.  Pair index jb = (qb, u, db), db fastest so that consecutive
     // MFMAs never accumulate into the same registers; operands of the next pair are read
     // while the current pair runs.
@@ -496,6 +552,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
   if (i < nsteps) body(i, stage0, stage1, stage3, dsbuf0, dsbuf1, sA, dA, sB, dB);
   if (i + 1 < nsteps) body(i + 1, stage1, stage2, stage0, dsbuf1, dsbuf0, sB, dB, sA, dA);
   if (i + 2 < nsteps) body(i + 2, stage2, stage3, stage1, dsbuf0, dsbuf1, sA, dA, sB, dB);
+  if (STORE_DS && nsteps > 0) store_ds(prev_g, prev_qs);
   if (FUSED_DQ && nsteps > 0) {
     __syncthreads();
     dq_step(prev_g, prev_qs, ((nsteps - 1) & 1) ? dsbuf1 : dsbuf0);
@@ -706,6 +763,145 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t* __restri
 }
 
 // ---------------------------------------------------------------------------
+// Stored-dS mode: dQ = scale dS K from the dS^T blocks the main kernel wrote.
+// Workgroup = (batch, query head, 128 queries), wave = 32 queries (one block
+// row); key tiles of 64 (two blocks) in ascending order, so the sum order is
+// fixed.  Per tile: K (shared) and this wave's two dS^T blocks are copied
+// into LDS; dQ^T += K^T dS^T with both operands by transposing reads.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void bwd_dq_ds_kernel(const uint16_t* __restrict__ K,
+                                                           uint16_t* __restrict__ dQ, BwdParams p,
+                                                           int nqb) {
+  constexpr int BM = 128, BN = 64, NW = 4;
+  constexpr int RB = D * 2;
+  constexpr int KCH = D / 8;
+  constexpr int TB = BN * RB;
+  constexpr int NLD = TB / 1024 / NW;
+  constexpr int ND = D / 32;
+  static_assert(NLD >= 1, "tile too small");
+  __shared__ __attribute__((aligned(1024))) char kbuf0[TB];
+  __shared__ __attribute__((aligned(1024))) char kbuf1[TB];
+  __shared__ __attribute__((aligned(1024))) char dbuf0[NW * 4096];
+  __shared__ __attribute__((aligned(1024))) char dbuf1[NW * 4096];
+
+  const int BH = p.B * p.Hq;
+  const int wg = blockIdx.x;
+  const int bh = wg % BH;
+  const int qb = nqb - 1 - wg / BH;
+  const int b = bh / p.Hq, hq = bh % p.Hq;
+  const int hk = hq / p.G;
+  const size_t head_elems = (size_t)p.N * D;
+  const uint32_t head_bytes = (uint32_t)(head_elems * 2);
+  const uint16_t* Kh = K + ((size_t)b * (p.Hq / p.G) + hk) * head_elems;
+  const char* dsh = p.ds + (size_t)bh * p.ds_head;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int n = lane & 31, h = lane >> 5;
+  const int q0 = qb * BM;
+  const int qb32 = qb * 4 + wave;   // this wave's query block
+
+  const int kend = CAUSAL ? min(p.N, q0 + BM) : p.N;
+  const int ntiles = (kend + BN - 1) / BN;
+
+  uint32_t ld_off[NLD];
+#pragma unroll
+  for (int s = 0; s < NLD; ++s) {
+    const int g = (s * NW + wave) * 64 + lane;
+    const int row = g / KCH, pc = g % KCH;
+    ld_off[s] = (uint32_t)(row * RB + ((pc ^ tile_swz<D>(row)) * 16));
+  }
+  auto issue_tile = [&](int kt, char* ks, char* dsb) {
+    const uint32_t base = (uint32_t)kt * TB;
+    const uint32_t left = head_bytes > base ? head_bytes - base : 0u;
+    const rsrc_t kr = make_rsrc_uniform((const char*)Kh + base, left);
+#pragma unroll
+    for (int s = 0; s < NLD; ++s) lds_dma16(kr, (lds_void*)(ks + (s * NW + wave) * 1024), ld_off[s]);
+    // This wave's blocks (qb32, 2kt) and (qb32, 2kt + 1); a block that was
+    // never written (padding, or above the diagonal) reads as zeros.
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int kb32 = 2 * kt + j;
+      const bool ok = qb32 < p.nb32 && kb32 < p.nb32 && (!CAUSAL || kb32 <= qb32);
+      const uint32_t off = ok ? (uint32_t)(qb32 * p.nb32 + kb32) * 2048u : 0u;
+      const rsrc_t dr = make_rsrc_uniform(dsh + off, ok ? 2048u : 0u);
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        lds_dma16_nt(dr, (lds_void*)(dsb + wave * 4096 + j * 2048 + s * 1024),
+                     (uint32_t)(s * 1024 + lane * 16));
+    }
+  };
+
+  // Transposing reads.  K^T (A operand, row d = 32 db + n, 8 keys): lane j of
+  // 16-lane group gq points at key row 8 rd + 4h + j/4 (+ 16 t), d = 32 db +
+  // 16 (gq & 1) + 4 (j & 3).  dS^T (B operand, column = block position n, 8
+  // keys): key row 8 rd + 4h + j/4 (+ 16 t), position 16 (gq & 1) + 4 (j & 3).
+  const int j16 = lane & 15, gq = lane >> 4;
+  uint32_t t_off[ND][2], s_off[2];
+#pragma unroll
+  for (int rd = 0; rd < 2; ++rd) {
+    const int row = 8 * rd + 4 * h + (j16 >> 2);
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+      const int c = 4 * db + 2 * (gq & 1) + ((j16 & 3) >> 1);
+      t_off[db][rd] = (uint32_t)(row * RB + ((c ^ tile_swz<D>(row)) * 16) + (j16 & 1) * 8);
+    }
+    s_off[rd] = (uint32_t)(wave * 4096 + row * 64 + (16 * (gq & 1) + 4 * (j16 & 3)) * 2);
+  }
+
+  f32x16 acc[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+
+  auto tile = [&](int kt, const char* ks, const char* dsb, char* kn, char* dn) {
+    wait_vmcnt<0>();
+    __syncthreads();  // tile kt in LDS; tile kt-1's buffers free
+    if (kt + 1 < ntiles) issue_tile(kt + 1, kn, dn);
+    // k-step t covers keys 16t .. 16t + 15 of the tile (block t / 2, rows
+    // 16 (t & 1) ..); db fastest so consecutive MFMAs use different
+    // accumulators.
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const char* sb = dsb + (t >> 1) * 2048 + (t & 1) * 16 * 64;
+      const u32x2 slo = lds_read_tr16((const lds_void*)(sb + s_off[0]));
+      const u32x2 shi = lds_read_tr16((const lds_void*)(sb + s_off[1]));
+      const bf16x8 bs = as_bf16x8(u32x4{slo[0], slo[1], shi[0], shi[1]});
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+        const char* kb = ks + 16 * t * RB;
+        const u32x2 lo = lds_read_tr16((const lds_void*)(kb + t_off[db][0]));
+        const u32x2 hi = lds_read_tr16((const lds_void*)(kb + t_off[db][1]));
+        acc[db] = mfma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), bs, acc[db]);
+      }
+    }
+  };
+
+  if (ntiles > 0) issue_tile(0, kbuf0, dbuf0);
+  for (int kt = 0; kt < ntiles; kt += 2) {
+    tile(kt, kbuf0, dbuf0, kbuf1, dbuf1);
+    if (kt + 1 < ntiles) tile(kt + 1, kbuf1, dbuf1, kbuf0, dbuf0);
+  }
+
+  // dQ = scale * (dQ^T)^T.  Column n of the accumulator is block position n,
+  // i.e. query 16u + 4h' + (i & 3) + 8 (i >> 2) for n = 16u + 8h' + i; row
+  // (register r of block db) is d = 32 db + 8 (r/4) + 4 h + r % 4.
+  const int pu = n >> 4, ph = (n >> 3) & 1, pi = n & 7;
+  const int qi = qb32 * 32 + 16 * pu + 4 * ph + (pi & 3) + 8 * (pi >> 2);
+  const rsrc_t out = make_rsrc_uniform(dQ + (size_t)bh * head_elems, head_bytes);
+#pragma unroll
+  for (int db = 0; db < ND; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      u32x2 w;
+      w[0] = pack_bf16x2(acc[db][4 * g] * p.scale, acc[db][4 * g + 1] * p.scale);
+      w[1] = pack_bf16x2(acc[db][4 * g + 2] * p.scale, acc[db][4 * g + 3] * p.scale);
+      buf_store8(out, (uint32_t)(qi * RB + (32 * db + 8 * g + 4 * h) * 2), w);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // dQ = bf16(scale * dQ_acc), 8 elements per thread.
 __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(const float* __restrict__ acc,
                                                              uint16_t* __restrict__ dq,
@@ -722,10 +918,10 @@ __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(const float* __rest
   ((u32x4*)dq)[i] = w;
 }
 
-template <int D, bool CAUSAL, bool FUSED_DQ>
+template <int D, bool CAUSAL, int DQM>
 hipError_t launch_bwd_t(const BwdArgs& a, const BwdParams& p, hipStream_t s) {
   const dim3 grid((unsigned)(a.B * a.Hkv * p.nkb));
-  hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL, FUSED_DQ>), grid, dim3(64 * kBwdWaves), 0, s,
+  hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL, DQM>), grid, dim3(64 * kBwdWaves), 0, s,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, (uint16_t*)a.dk, (uint16_t*)a.dv, p);
   return hipGetLastError();
@@ -744,9 +940,12 @@ BwdParams make_params(const BwdArgs& a) {
   p.nqs = (a.N + QS - 1) / QS;
   p.c = a.scale * kLog2e;
   p.scale = a.scale;
-  p.dq_acc = a.deterministic ? nullptr : (float*)(ws + lay.dq_acc);
+  p.dq_acc = a.deterministic == kDqAtomic ? (float*)(ws + lay.dq_acc) : nullptr;
   p.delta = (float*)(ws + lay.delta);
   p.lse2 = (float*)(ws + lay.lse2);
+  p.nb32 = (a.N + 31) / 32;
+  p.ds_head = (uint32_t)ds_head_bytes(a.N);
+  p.ds = a.deterministic == kDqStored ? ws + lay.ds : nullptr;
   return p;
 }
 
@@ -764,10 +963,29 @@ hipError_t launch_pre_d(const BwdArgs& a, hipStream_t s) {
 template <int D>
 hipError_t launch_main_d(const BwdArgs& a, hipStream_t s) {
   const BwdParams p = make_params(a);
-  // Fixed-order mode leaves dQ to bwd_dq_kernel.
+  switch (a.deterministic) {
+    case kDqAtomic:
+      return a.causal ? launch_bwd_t<D, true, kDqAtomic>(a, p, s) : launch_bwd_t<D, false, kDqAtomic>(a, p, s);
+    case kDqStored:
+      return a.causal ? launch_bwd_t<D, true, kDqStored>(a, p, s) : launch_bwd_t<D, false, kDqStored>(a, p, s);
+    default:
+      return a.causal ? launch_bwd_t<D, true, kDqRecompute>(a, p, s)
+                      : launch_bwd_t<D, false, kDqRecompute>(a, p, s);
+  }
+}
+
+template <int D>
+hipError_t launch_dq_ds_d(const BwdArgs& a, hipStream_t s) {
+  const BwdParams p = make_params(a);
+  const int nqb = (a.N + 127) / 128;
+  const dim3 grid((unsigned)(a.B * a.Hq * nqb));
   if (a.causal)
-    return a.deterministic ? launch_bwd_t<D, true, false>(a, p, s) : launch_bwd_t<D, true, true>(a, p, s);
-  return a.deterministic ? launch_bwd_t<D, false, false>(a, p, s) : launch_bwd_t<D, false, true>(a, p, s);
+    hipLaunchKernelGGL((bwd_dq_ds_kernel<D, true>), grid, dim3(256), 0, s, (const uint16_t*)a.k,
+                       (uint16_t*)a.dq, p, nqb);
+  else
+    hipLaunchKernelGGL((bwd_dq_ds_kernel<D, false>), grid, dim3(256), 0, s, (const uint16_t*)a.k,
+                       (uint16_t*)a.dq, p, nqb);
+  return hipGetLastError();
 }
 
 template <int D>
@@ -788,15 +1006,22 @@ hipError_t launch_dq_d(const BwdArgs& a, hipStream_t s) {
 
 }  // namespace
 
+size_t ds_head_bytes(int N) {
+  const size_t nb = ((size_t)N + 31) / 32;
+  return nb * nb * 2048;
+}
+
 BwdLayout bwd_layout(int B, int Hq, int N, int D, int deterministic) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  (void)D;
   const size_t rows = (size_t)B * Hq * N;
   BwdLayout l;
   l.delta = 0;
   l.lse2 = up(rows * 4);
-  l.dq_acc = l.lse2 + up(rows * 4);
-  l.total = l.dq_acc + (deterministic ? 0 : up(rows * D * 4));
+  l.dq_acc = l.ds = l.lse2 + up(rows * 4);
+  size_t extra = 0;
+  if (deterministic == kDqAtomic) extra = up(rows * D * 4);
+  if (deterministic == kDqStored) extra = up((size_t)B * Hq * ds_head_bytes(N));
+  l.total = l.dq_acc + extra;
   return l;
 }
 
@@ -809,7 +1034,8 @@ hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t s) {
-  if (a.deterministic) return a.D == 64 ? launch_dq_d<64>(a, s) : launch_dq_d<128>(a, s);
+  if (a.deterministic == kDqStored) return a.D == 64 ? launch_dq_ds_d<64>(a, s) : launch_dq_ds_d<128>(a, s);
+  if (a.deterministic == kDqRecompute) return a.D == 64 ? launch_dq_d<64>(a, s) : launch_dq_d<128>(a, s);
   const BwdParams p = make_params(a);
   const size_t n8 = (size_t)a.B * a.Hq * a.N * a.D / 8;
   hipLaunchKernelGGL(bwd_dq_convert_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s,

@@ -94,8 +94,15 @@ __device__ __forceinline__ void buf_store4(rsrc_t r, uint32_t voff, float v) {
 // (buffer_load_dwordx4 ... lds): lane l's bytes land at lds + 16 l, where lds
 // is wave-uniform.  Completion is tracked by vmcnt.
 typedef __attribute__((address_space(3))) void lds_void;
+// Cache-policy operand of the buffer intrinsics: the non-temporal bit (nt
+// on gfx950) for data that is written or read exactly once.
+constexpr int kCachePolicyNT = 2;
 __device__ __forceinline__ void lds_dma16(rsrc_t r, lds_void* lds, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, 0, 0, 0);
+}
+// Same, for data read once (non-temporal: not kept in the caches).
+__device__ __forceinline__ void lds_dma16_nt(rsrc_t r, lds_void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, 0, 0, kCachePolicyNT);
 }
 __device__ __forceinline__ void lds_dma4(rsrc_t r, lds_void* lds, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 4, voff, 0, 0, 0);

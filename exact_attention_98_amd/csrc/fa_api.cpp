@@ -34,6 +34,15 @@ int check_shape(int B, int Hq, int Hkv, int N, int D, float scale) {
   return FA_OK;
 }
 
+// The dQ mode (the deterministic argument): 0 atomic, 1 stored dS, 2
+// recompute.  Stored-dS blocks of one head are addressed with 32-bit offsets,
+// with offsets from 2^32 - 4096 up reserved as "no block".
+int check_mode(int N, int deterministic) {
+  if (deterministic < 0 || deterministic > 2) return FA_ERR_INVALID;
+  if (deterministic == 1 && fa::ds_head_bytes(N) > 0xFFFFF000ull - 4096) return FA_ERR_TOO_LARGE;
+  return FA_OK;
+}
+
 int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
              int Hkv, int N, int D, int causal, float scale, int poly_quarters, void* stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID;
@@ -71,7 +80,8 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, 
 
 size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int D, int deterministic) {
   if (check_shape(B, Hq, Hkv, N, D, 1.0f) != FA_OK) return 0;
-  return fa::bwd_layout(B, Hq, N, D, deterministic ? 1 : 0).total;
+  if (check_mode(N, deterministic) != FA_OK) return 0;
+  return fa::bwd_layout(B, Hq, N, D, deterministic).total;
 }
 
 }  // extern "C"
@@ -95,11 +105,13 @@ int check_bwd(int B, int Hq, int Hkv, int N, int D, float scale, const void* wor
     if (!b.p) return FA_ERR_INVALID;
   int rc = check_shape(B, Hq, Hkv, N, D, scale);
   if (rc != FA_OK) return rc;
+  rc = check_mode(N, deterministic);
+  if (rc != FA_OK) return rc;
   for (const Buf& b : reads)
     if (!aligned16(b.p)) return FA_ERR_ALIGN;
   for (const Buf& b : writes)
     if (!aligned16(b.p)) return FA_ERR_ALIGN;
-  const fa::BwdLayout lay = fa::bwd_layout(B, Hq, N, D, deterministic ? 1 : 0);
+  const fa::BwdLayout lay = fa::bwd_layout(B, Hq, N, D, deterministic);
   if (!workspace || workspace_bytes < lay.total) return FA_ERR_WORKSPACE;
   if (((uintptr_t)workspace & 255u) != 0) return FA_ERR_ALIGN;
   const Buf ws{workspace, lay.total};
@@ -121,7 +133,7 @@ fa::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* o,
                      const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N,
                      int D, int causal, float scale, void* workspace, int deterministic) {
   return fa::BwdArgs{q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, D, causal ? 1 : 0, scale,
-                     deterministic ? 1 : 0, workspace};
+                     deterministic, workspace};
 }
 
 size_t qbytes(int B, int Hq, int N, int D) { return (size_t)B * Hq * N * D * 2; }

@@ -52,15 +52,20 @@ struct BwdLayout {
   size_t delta;     // fp32 [B][Hq][N]
   size_t lse2;      // fp32 [B][Hq][N], LSE * log2(e)
   size_t dq_acc;    // fp32 [B][Hq][N][D] (atomic mode only)
+  size_t ds;        // dS^T blocks, ds_head_bytes(N) per (b, hq) (stored-dS mode only)
   size_t total;
 };
+
+// Bytes of the stored-dS blocks of one (batch, query head).
+size_t ds_head_bytes(int N);
 
 BwdLayout bwd_layout(int B, int Hq, int N, int D, int deterministic);
 // The three backward stages; each reads only the BwdArgs fields it needs.
 hipError_t launch_bwd_preprocess(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t stream);
-// Atomic mode: dq = bf16(scale * accumulated dQ).  Fixed-order mode: the dQ
-// kernel.
+// By dQ mode (the deterministic argument): 0 atomic, dq = bf16(scale *
+// accumulated dQ); 1 stored dS, the fixed-order dS K pass; 2 recompute, the
+// fixed-order pass that recomputes S, dP and dS.
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 
 }  // namespace fa

@@ -79,9 +79,10 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
               int exp_poly_quarters, void* stream);
 
 /*
- * Bytes of device workspace fa_bwd needs for this problem: per-row
- * Delta = rowsum(dO * O) and LSE * log2(e), plus, in atomic mode, the fp32 dQ
- * accumulator.  Returns 0 for invalid sizes.
+ * Bytes of device workspace fa_bwd needs for this problem and dQ mode
+ * (deterministic, see fa_bwd): per-row Delta = rowsum(dO * O) and
+ * LSE * log2(e), plus the fp32 dQ accumulator (mode 0) or the bf16 dS blocks
+ * (mode 1).  Returns 0 for invalid sizes or modes.
  */
 size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int D, int deterministic);
 
@@ -96,12 +97,19 @@ size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int D, int determini
  *     256-byte aligned, owned by the caller; its contents on entry do not
  *     matter and are scratch afterwards.  Two calls in flight at once must
  *     not share a workspace.
- *   deterministic = 0: each key tile's dQ contribution is added into an fp32
- *     accumulator with atomics (no run-to-run bitwise guarantee for dq).
- *   deterministic = 1: dQ is formed by a separate pass that owns each query
- *     tile and sums the key tiles in a fixed ascending order (recomputing S,
- *     dP and dS), so dq, dk and dv are bit-identical across calls with the
- *     same inputs on the same device.
+ *   deterministic selects how dQ is accumulated (danialwang explainer,
+ *   sections 05-06, atomic and fixed-order accumulation):
+ *   0: each key tile's dQ contribution is added into an fp32 accumulator
+ *     with atomics (no run-to-run bitwise guarantee for dq); workspace
+ *     B*Hq*N*(D+2)*4 bytes.
+ *   1: the main pass stores dS in bf16 blocks of 32 x 32 and a separate pass
+ *     that owns each query tile sums dS K over the key tiles in a fixed
+ *     ascending order; workspace about B*Hq*N*N*2 bytes (one head's blocks
+ *     must stay below 4 GiB - 8 KiB, else FA_ERR_TOO_LARGE).
+ *   2: as 1, but the separate pass recomputes S, dP and dS instead of
+ *     reading them; workspace B*Hq*N*8 bytes.
+ *   Modes 1 and 2 give dq, dk and dv bit-identical across calls with the
+ *   same inputs on the same device.  Other values: FA_ERR_INVALID.
  * With Hq != Hkv, dk and dv sum over the query heads that share a K/V head.
  * dq, dk, dv must not overlap any input.
  */
@@ -117,13 +125,13 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
  * meaning given for fa_bwd; each stage checks the arguments it uses and
  * returns the same codes.
  *   fa_bwd_preprocess: Delta_i = rowsum(dO * O) and LSE_i * log2(e) into the
- *     workspace, and clears the workspace's fp32 dQ accumulator (and order
- *     counters).
+ *     workspace, and (mode 0) clears the workspace's fp32 dQ accumulator.
  *   fa_bwd_main: recomputes P tile by tile from q, k and the workspace's
- *     LSE * log2(e), and forms dK, dV (written to dk, dv); in atomic mode it
- *     also accumulates the unscaled dQ sums in the workspace.
- *   fa_bwd_dq: atomic mode: dq = bf16(scale * accumulated dQ) (q, k, v, dout
- *     unused but checked); fixed-order mode: the dQ pass described above.
+ *     LSE * log2(e), and forms dK, dV (written to dk, dv); in mode 0 it
+ *     also accumulates the unscaled dQ sums in the workspace, in mode 1 it
+ *     stores the dS blocks there.
+ *   fa_bwd_dq: mode 0: dq = bf16(scale * accumulated dQ) (q, k, v, dout
+ *     unused but checked); modes 1 and 2: the fixed-order dQ pass.
  */
 int fa_bwd_preprocess(const void* o, const void* dout, const float* lse, int B, int Hq, int Hkv,
                       int N, int D, void* workspace, size_t workspace_bytes, int deterministic,

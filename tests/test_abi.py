@@ -73,11 +73,20 @@ def test_workspace_size():
     B, H, N, D = 2, 16, 8192, 128
     s0 = fa.fa_bwd_workspace_size(B, H, H, N, D, 0)
     s1 = fa.fa_bwd_workspace_size(B, H, H, N, D, 1)
-    assert s0 >= B * H * N * D * 4 + 2 * B * H * N * 4   # atomic mode: fp32 dQ accumulator
-    assert s1 >= 2 * B * H * N * 4 and s1 < s0
-    assert s0 % 256 == 0 and s1 % 256 == 0
+    s2 = fa.fa_bwd_workspace_size(B, H, H, N, D, 2)
+    rows = 2 * B * H * N * 4                              # Delta and LSE * log2(e)
+    assert s0 >= B * H * N * D * 4 + rows                 # atomic mode: fp32 dQ accumulator
+    assert s1 >= B * H * N * N * 2 + rows                 # stored dS: bf16 32x32 blocks, N^2 per head
+    assert rows <= s2 < s0 < s1                           # recompute: row constants only
+    assert s0 % 256 == 0 and s1 % 256 == 0 and s2 % 256 == 0
     assert fa.fa_bwd_workspace_size(0, H, H, N, D, 0) == 0
     assert fa.fa_bwd_workspace_size(B, H, H, N, 80, 0) == 0
+    assert fa.fa_bwd_workspace_size(B, H, H, N, D, 3) == 0    # no such mode
+    assert fa.fa_bwd_workspace_size(B, H, H, N, D, -1) == 0
+    # Stored dS addresses one head's blocks with 32-bit offsets.
+    assert fa.fa_bwd_workspace_size(1, 1, 1, 46336, 64, 1) > 0
+    assert fa.fa_bwd_workspace_size(1, 1, 1, 46400, 64, 1) == 0
+    assert fa.fa_bwd_workspace_size(1, 1, 1, 46400, 64, 2) > 0
 
 
 def bwd(**kw):
@@ -96,6 +105,8 @@ def bwd(**kw):
     (dict(D=32), fa.FA_ERR_UNSUPPORTED), (dict(Hq=4, Hkv=3), fa.FA_ERR_INVALID),
     (dict(dq=Q), fa.FA_ERR_INVALID), (dict(dk=DV), fa.FA_ERR_INVALID),
     (dict(ws=DQ), fa.FA_ERR_INVALID), (dict(scale=float("nan")), fa.FA_ERR_INVALID),
+    (dict(det=3), fa.FA_ERR_INVALID), (dict(det=-1), fa.FA_ERR_INVALID),
+    (dict(N=46400, det=1), fa.FA_ERR_TOO_LARGE),
 ])
 def test_bwd_rejects(kw, code):
     assert bwd(**kw) == code
