@@ -382,7 +382,8 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
   // sv/dv hold S(i), dP(i); sn/dn receive S(i+1), dP(i+1).
   auto body = [&](int i, const char* cur, const char* nxt, char* ld, char* dsw,
                   const char* dsprev, f32x16 (&sv)[NQB], f32x16 (&dv)[NQB], f32x16 (&sn)[NQB],
-                  f32x16 (&dn)[NQB]) {
+                  f32x16 (&dn)[NQB], const f32x4 (&lc)[NQB][4], const f32x4 (&dc)[NQB][4],
+                  f32x4 (&ln)[NQB][4], f32x4 (&dln)[NQB][4]) {
     // Step i+1 must be in LDS; step i+2 may still be in flight.
     if (i + 2 < nsteps) wait_all_but_one_step();
     else wait_vmcnt<0>();
@@ -395,6 +396,14 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
     if (FUSED_DQ && i > 0) dq_step(prev_g, prev_qs, dsprev);
 
     const int q0 = cur_qs * QS;
+    // S(i) and dP(i) are read by the VALU below: move them to VGPRs here, so
+    // that the masked and unmasked paths join in VGPRs (otherwise the masked
+    // values go back to the accumulator registers and are read out again).
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      pin(sv[qb]);
+      pin(dv[qb]);
+    }
     // Causal mask of step i, only near the diagonal: S = -inf where key > query.
     // Register r of block qb holds query q0 + 32qb + 8(r/4) + 4h + r%4.
     // Padding keys (key >= N, rows read as zero) are masked too: their score 0
@@ -415,22 +424,32 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
     // Phase A: the 16 S(i+1)/dP(i+1) MFMAs (always computed, on a stale stage
     // after the last step, so the phase has no branch), each pair followed by
     // 2 NQB elements of P(i) = exp2(S c - LSE log2 e), dS(i) = P (dP - Delta).
-    // Phase B: the dV += P^T dO, dK += dS^T Q MFMAs with their transposing
-    // reads one pair ahead.
+    // Phase B: the dV += P^T dO, dK += dS^T Q MFMAs.  LDS operands of both
+    // phases form one stream read PD pairs ahead of their MFMAs; step i+1's
+    // LSE and Delta are read during phase B.
     constexpr int T = D / 16;
     constexpr int NPAIR = NQB * T;         // S/dP MFMA pairs (8 for D = 64, 128)
     constexpr int EPP = 16 * NQB / NPAIR;  // elements per lane per pair
+    constexpr int NB = NQB * ND * 2;       // dV/dK MFMA pairs
+    constexpr int PD = 2;                  // operand prefetch distance, in pairs
     const char* qs_l = cur;
     const char* dos_l = cur + TB;
-    const float* lse_l = (const float*)(cur + 2 * TB);
-    const float* dlt_l = (const float*)(cur + 2 * TB + 256);
-    f32x4 l4[NQB][4], d4[NQB][4];
+    // LSE * log2 e and Delta of step i: read by the previous step when one
+    // block per step (D = 128); read here when two (D = 64, where a second
+    // register set would not fit).
+    constexpr bool EARLY_ROWC = NQB == 1;
+    f32x4 lcur[NQB][4], dcur[NQB][4];
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        l4[qb][r4] = *(const f32x4*)(lse_l + 32 * qb + 8 * r4 + 4 * h);
-        d4[qb][r4] = *(const f32x4*)(dlt_l + 32 * qb + 8 * r4 + 4 * h);
+        if constexpr (EARLY_ROWC) {
+          lcur[qb][r4] = lc[qb][r4];
+          dcur[qb][r4] = dc[qb][r4];
+        } else {
+          lcur[qb][r4] = *(const f32x4*)((const float*)(cur + 2 * TB) + 32 * qb + 8 * r4 + 4 * h);
+          dcur[qb][r4] = *(const f32x4*)((const float*)(cur + 2 * TB + 256) + 32 * qb + 8 * r4 + 4 * h);
+        }
       }
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb)
@@ -439,26 +458,44 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
         sn[qb][r] = 0.f;
         dn[qb][r] = 0.f;
       }
-    bf16x8 qa = as_bf16x8(*(const u32x4*)(nxt + a_off[0]));
-    bf16x8 da = as_bf16x8(*(const u32x4*)(nxt + TB + a_off[0]));
+    // Operand stream: c < NPAIR is phase A pair c (row reads of Q, dO of step
+    // i+1); c >= NPAIR is phase B pair c - NPAIR = (qb, u, db), db fastest so
+    // that consecutive MFMAs never accumulate into the same registers
+    // (transposing reads of dO, Q of step i).
+    bf16x8 opA[NPAIR + NB], opB[NPAIR + NB];
+    auto fetch = [&](int c) {
+      if (c < NPAIR) {
+        const int qb1 = c / T, t1 = c % T;
+        opA[c] = as_bf16x8(*(const u32x4*)(nxt + qb1 * 32 * RB + a_off[t1]));
+        opB[c] = as_bf16x8(*(const u32x4*)(nxt + TB + qb1 * 32 * RB + a_off[t1]));
+      } else if (c < NPAIR + NB) {
+        const int jb = c - NPAIR;
+        const int qb = jb / (2 * ND), u = (jb / ND) & 1, db = jb % ND;
+        const int roff = (32 * qb + 16 * u) * RB;
+        const u32x2 olo = lds_read_tr16((const lds_void*)(dos_l + roff + tr_off[db][0]));
+        const u32x2 ohi = lds_read_tr16((const lds_void*)(dos_l + roff + tr_off[db][1]));
+        const u32x2 qlo = lds_read_tr16((const lds_void*)(qs_l + roff + tr_off[db][0]));
+        const u32x2 qhi = lds_read_tr16((const lds_void*)(qs_l + roff + tr_off[db][1]));
+        opA[c] = as_bf16x8(u32x4{olo[0], olo[1], ohi[0], ohi[1]});
+        opB[c] = as_bf16x8(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]});
+      }
+    };
+#pragma unroll
+    for (int c = 0; c < PD; ++c) fetch(c);
     bf16x8 pa[NQB][2], dsa[NQB][2];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < NPAIR; ++j) {
       const int qb = j / T, t = j % T;
-      sn[qb] = mfma32(qa, kB[t], sn[qb]);
-      dn[qb] = mfma32(da, vB[t], dn[qb]);
-      if (j + 1 < NPAIR) {
-        const int qb1 = (j + 1) / T, t1 = (j + 1) % T;
-        qa = as_bf16x8(*(const u32x4*)(nxt + qb1 * 32 * RB + a_off[t1]));
-        da = as_bf16x8(*(const u32x4*)(nxt + TB + qb1 * 32 * RB + a_off[t1]));
-      }
+      fetch(j + PD);
+      sn[qb] = mfma32(opA[j], kB[t], sn[qb]);
+      dn[qb] = mfma32(opB[j], vB[t], dn[qb]);
 #pragma unroll
       for (int e = j * EPP; e < (j + 1) * EPP; ++e) {
         const int eq = e / 16, r = e % 16;
-        const float pv = exp2_hw(__builtin_fmaf(sv[eq][r], p.c, -l4[eq][r >> 2][r & 3]));
+        const float pv = exp2_hw(__builtin_fmaf(sv[eq][r], p.c, -lcur[eq][r >> 2][r & 3]));
         sv[eq][r] = pv;
-        dv[eq][r] = pv * (dv[eq][r] - d4[eq][r >> 2][r & 3]);
+        dv[eq][r] = pv * (dv[eq][r] - dcur[eq][r >> 2][r & 3]);
         if ((r & 7) == 7) {
           const int u = r >> 3;
           u32x4 w1, w2;
@@ -481,30 +518,21 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
         ds_keep[qb][1] = as_u32x4(dsa[qb][1]);
       }
 
-    // Phase B.  Pair index jb = (qb, u, db), db fastest so that consecutive
-    // MFMAs never accumulate into the same registers; operands of the next pair are read
-    // while the current pair runs.
-    constexpr int NB = NQB * ND * 2;
-    auto tr_operands = [&](int jb, u32x4& ob, u32x4& qbv) {
-      const int qb = jb / (2 * ND), u = (jb / ND) & 1, db = jb % ND;
-      const int roff = (32 * qb + 16 * u) * RB;
-      const u32x2 olo = lds_read_tr16((const lds_void*)(dos_l + roff + tr_off[db][0]));
-      const u32x2 ohi = lds_read_tr16((const lds_void*)(dos_l + roff + tr_off[db][1]));
-      const u32x2 qlo = lds_read_tr16((const lds_void*)(qs_l + roff + tr_off[db][0]));
-      const u32x2 qhi = lds_read_tr16((const lds_void*)(qs_l + roff + tr_off[db][1]));
-      ob = u32x4{olo[0], olo[1], ohi[0], ohi[1]};
-      qbv = u32x4{qlo[0], qlo[1], qhi[0], qhi[1]};
-    };
-    u32x4 ob, qbv;
-    tr_operands(0, ob, qbv);
-    __builtin_amdgcn_sched_barrier(0);
+    // Phase B.
+    const float* lse_n = (const float*)(nxt + 2 * TB);
+    const float* dlt_n = (const float*)(nxt + 2 * TB + 256);
 #pragma unroll
     for (int jb = 0; jb < NB; ++jb) {
       const int qb = jb / (2 * ND), u = (jb / ND) & 1, db = jb % ND;
-      const u32x4 obc = ob, qbc = qbv;
-      if (jb + 1 < NB) tr_operands(jb + 1, ob, qbv);
-      dv_acc[db] = mfma32(pa[qb][u], as_bf16x8(obc), dv_acc[db]);
-      dk_acc[db] = mfma32(dsa[qb][u], as_bf16x8(qbc), dk_acc[db]);
+      fetch(NPAIR + jb + PD);
+      dv_acc[db] = mfma32(pa[qb][u], opA[NPAIR + jb], dv_acc[db]);
+      dk_acc[db] = mfma32(dsa[qb][u], opB[NPAIR + jb], dk_acc[db]);
+      // Step i+1's LSE * log2 e and Delta for this lane's queries.
+      if (EARLY_ROWC && jb < NQB * 4) {
+        const int lq = jb / 4, r4 = jb % 4;
+        ln[lq][r4] = *(const f32x4*)(lse_n + 32 * lq + 8 * r4 + 4 * h);
+        dln[lq][r4] = *(const f32x4*)(dlt_n + 32 * lq + 8 * r4 + 4 * h);
+      }
       // dS^T -> LDS: lane (key 32 wave + n) writes queries 32qb + 8g + 4h .. +4.
       if constexpr (FUSED_DQ) {
         if (db == 0 && u == 0) {
@@ -525,6 +553,9 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
   };
 
   f32x16 sA[NQB], dA[NQB], sB[NQB], dB[NQB];
+  // LSE * log2 e and Delta of the step being finished (set A or B, alternating
+  // like the S/dP sets; each body reads the next step's into the other set).
+  f32x4 lA[NQB][4], dlA[NQB][4], lB[NQB][4], dlB[NQB][4];
   if (nsteps > 0) {
     issue_next(stage0);
     if (nsteps > 1) issue_next(stage1);
@@ -538,20 +569,30 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
     }
     __syncthreads();
     compute_sdp(stage0, sA, dA);
+    if constexpr (NQB == 1)
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        lA[qb][r4] = *(const f32x4*)((const float*)(stage0 + 2 * TB) + 32 * qb + 8 * r4 + 4 * h);
+        dlA[qb][r4] = *(const f32x4*)((const float*)(stage0 + 2 * TB + 256) + 32 * qb + 8 * r4 + 4 * h);
+      }
   }
   // Stages rotate with period 4, S/dP register sets and dS^T buffers with
   // period 2.  The main loop has no bounds checks between bodies, so the
   // register sets keep their places; the tail checks each step.
   int i = 0;
   for (; i + 4 <= nsteps; i += 4) {
-    body(i, stage0, stage1, stage3, dsbuf0, dsbuf1, sA, dA, sB, dB);
-    body(i + 1, stage1, stage2, stage0, dsbuf1, dsbuf0, sB, dB, sA, dA);
-    body(i + 2, stage2, stage3, stage1, dsbuf0, dsbuf1, sA, dA, sB, dB);
-    body(i + 3, stage3, stage0, stage2, dsbuf1, dsbuf0, sB, dB, sA, dA);
+    body(i, stage0, stage1, stage3, dsbuf0, dsbuf1, sA, dA, sB, dB, lA, dlA, lB, dlB);
+    body(i + 1, stage1, stage2, stage0, dsbuf1, dsbuf0, sB, dB, sA, dA, lB, dlB, lA, dlA);
+    body(i + 2, stage2, stage3, stage1, dsbuf0, dsbuf1, sA, dA, sB, dB, lA, dlA, lB, dlB);
+    body(i + 3, stage3, stage0, stage2, dsbuf1, dsbuf0, sB, dB, sA, dA, lB, dlB, lA, dlA);
   }
-  if (i < nsteps) body(i, stage0, stage1, stage3, dsbuf0, dsbuf1, sA, dA, sB, dB);
-  if (i + 1 < nsteps) body(i + 1, stage1, stage2, stage0, dsbuf1, dsbuf0, sB, dB, sA, dA);
-  if (i + 2 < nsteps) body(i + 2, stage2, stage3, stage1, dsbuf0, dsbuf1, sA, dA, sB, dB);
+  if (i < nsteps) body(i, stage0, stage1, stage3, dsbuf0, dsbuf1, sA, dA, sB, dB, lA, dlA, lB, dlB);
+  if (i + 1 < nsteps)
+    body(i + 1, stage1, stage2, stage0, dsbuf1, dsbuf0, sB, dB, sA, dA, lB, dlB, lA, dlA);
+  if (i + 2 < nsteps)
+    body(i + 2, stage2, stage3, stage1, dsbuf0, dsbuf1, sA, dA, sB, dB, lA, dlA, lB, dlB);
   if (STORE_DS && nsteps > 0) store_ds(prev_g, prev_qs);
   if (FUSED_DQ && nsteps > 0) {
     __syncthreads();

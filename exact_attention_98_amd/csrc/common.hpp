@@ -78,6 +78,7 @@ __device__ __forceinline__ rsrc_t make_rsrc_uniform(const void* base, uint32_t b
 // before here and cannot be moved past or re-associated across this point.
 __device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(u32x4& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(f32x16& x) { asm volatile("" : "+v"(x)); }
 // Keeps the compiler from turning the guarded block into selects that run on
 // every path (used for rare, wave-uniform branches).
 __device__ __forceinline__ void keep_branch() { asm volatile("" ::: "memory"); }
