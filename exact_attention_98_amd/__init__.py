@@ -15,8 +15,9 @@ import ctypes
 import os
 
 __all__ = ["fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_workspace_size", "fa_bwd_preprocess",
-           "fa_bwd_main", "fa_bwd_dq", "fa_strerror", "forward", "backward", "FaError",
-           "library_path", "load"]
+           "fa_bwd_main", "fa_bwd_dq", "fa_fwd_varlen", "fa_fwd_varlen_workspace_size",
+           "fa_varlen_max_seqlen", "fa_strerror", "forward", "backward", "forward_varlen",
+           "FaError", "library_path", "load"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libfa.so")
@@ -31,7 +32,8 @@ FA_ERR_HIP = -5
 FA_ERR_TOO_LARGE = -6
 
 EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_workspace_size", "fa_bwd_preprocess",
-            "fa_bwd_main", "fa_bwd_dq", "fa_strerror")
+            "fa_bwd_main", "fa_bwd_dq", "fa_fwd_varlen", "fa_fwd_varlen_workspace_size",
+            "fa_varlen_max_seqlen", "fa_strerror")
 
 
 class FaError(RuntimeError):
@@ -69,6 +71,13 @@ def load():
     lib.fa_bwd_main.restype = ci
     lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp, sz, ci, vp]
     lib.fa_bwd_dq.restype = ci
+    lib.fa_fwd_varlen_workspace_size.argtypes = [ci, ci]
+    lib.fa_fwd_varlen_workspace_size.restype = sz
+    lib.fa_varlen_max_seqlen.argtypes = []
+    lib.fa_varlen_max_seqlen.restype = ci
+    lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, vp, sz,
+                                  vp]
+    lib.fa_fwd_varlen.restype = ci
     lib.fa_strerror.argtypes = [ci]
     lib.fa_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -111,6 +120,20 @@ def fa_bwd_dq(q, k, v, dout, dq, B, Hq, Hkv, N, D, causal, scale, workspace, wor
               deterministic, stream) -> int:
     return load().fa_bwd_dq(q, k, v, dout, dq, B, Hq, Hkv, N, D, int(causal), float(scale),
                             workspace, workspace_bytes, int(deterministic), stream)
+
+
+def fa_fwd_varlen_workspace_size(B, total) -> int:
+    return int(load().fa_fwd_varlen_workspace_size(B, total))
+
+
+def fa_varlen_max_seqlen() -> int:
+    return int(load().fa_varlen_max_seqlen())
+
+
+def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, B, Hq, Hkv, total, max_seqlen, D, causal, scale,
+                  workspace, workspace_bytes, stream) -> int:
+    return load().fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, B, Hq, Hkv, total, max_seqlen, D,
+                                int(causal), float(scale), workspace, workspace_bytes, stream)
 
 
 def fa_strerror(status: int) -> str:
@@ -199,3 +222,42 @@ def backward(q, k, v, o, lse, dout, causal: bool, scale: float, *, deterministic
     if rc != FA_OK:
         raise FaError(rc, "fa_bwd")
     return dq, dk, dv
+
+
+def forward_varlen(q, k, v, cu_seqlens, max_seqlen: int, causal: bool, scale: float, *,
+                   out=None, lse=None, workspace=None):
+    """O (bf16) and LSE (fp32) of a variable-length batch.
+
+    q [Hq, total, D], k/v [Hkv, total, D] bf16 device tensors; cu_seqlens an
+    int32 device tensor of B + 1 cumulative sequence starts.  Sequence b is
+    rows cu_seqlens[b]:cu_seqlens[b+1] of every head.
+    """
+    import torch
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q, k, v must be [H, total, D]")
+    Hq, total, D = q.shape
+    Hkv = k.shape[0]
+    _check("q", q, torch.bfloat16, (Hq, total, D))
+    _check("k", k, torch.bfloat16, (Hkv, total, D))
+    _check("v", v, torch.bfloat16, (Hkv, total, D))
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must hold B + 1 >= 2 entries")
+    B = cu_seqlens.numel() - 1
+    _check("cu_seqlens", cu_seqlens, torch.int32, (B + 1,))
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((Hq, total), dtype=torch.float32, device=q.device)
+    _check("out", out, torch.bfloat16, (Hq, total, D))
+    _check("lse", lse, torch.float32, (Hq, total))
+    if total == 0:
+        return out, lse
+    ws_bytes = fa_fwd_varlen_workspace_size(B, total)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=q.device)
+    rc = fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                       cu_seqlens.data_ptr(), B, Hq, Hkv, total, int(max_seqlen), D, causal,
+                       scale, workspace.data_ptr(), workspace.numel(), _stream_handle(q.device))
+    if rc != FA_OK:
+        raise FaError(rc, "fa_fwd_varlen")
+    return out, lse

@@ -78,6 +78,47 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, 
   return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, N, D, causal, scale, exp_poly_quarters, stream);
 }
 
+size_t fa_fwd_varlen_workspace_size(int B, int total) {
+  if (B < 1 || total < 0) return 0;
+  return fa::varlen_workspace_bytes(B, total);
+}
+
+int fa_varlen_max_seqlen(void) { return fa::varlen_max_seqlen_limit(); }
+
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int* cu_seqlens, int B, int Hq, int Hkv, int total, int max_seqlen, int D,
+                  int causal, float scale, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  if (!q || !k || !v || !o || !lse || !cu_seqlens || !workspace) return FA_ERR_INVALID;
+  if (B < 1 || total < 0 || max_seqlen < 1 || max_seqlen > fa::varlen_max_seqlen_limit())
+    return FA_ERR_INVALID;
+  // Shape checks as for one sequence of total tokens (at least 1).
+  int rc = check_shape(1, Hq, Hkv, total > 0 ? total : 1, D, scale);
+  if (rc != FA_OK) return rc;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      !aligned16(cu_seqlens))
+    return FA_ERR_ALIGN;
+  if (((uintptr_t)workspace & 255u) != 0) return FA_ERR_ALIGN;
+  const size_t wbytes = fa::varlen_workspace_bytes(B, total);
+  if (workspace_bytes < wbytes) return FA_ERR_WORKSPACE;
+  const size_t qbytes = (size_t)Hq * total * D * 2, kvbytes = (size_t)Hkv * total * D * 2;
+  const size_t lbytes = (size_t)Hq * total * 4, cbytes = (size_t)(B + 1) * 4;
+  const void* outs[3] = {o, lse, workspace};
+  const size_t osz[3] = {qbytes, lbytes, wbytes};
+  const void* ins[4] = {q, k, v, cu_seqlens};
+  const size_t isz[4] = {qbytes, kvbytes, kvbytes, cbytes};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 4; ++j)
+      if (overlaps(outs[i], osz[i], ins[j], isz[j])) return FA_ERR_INVALID;
+    for (int j = 0; j < 3; ++j)
+      if (j != i && overlaps(outs[i], osz[i], outs[j], osz[j])) return FA_ERR_INVALID;
+  }
+  if (total == 0) return FA_OK;
+  fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, max_seqlen, D, causal ? 1 : 0, scale, 0};
+  const fa::VarlenArgs va{cu_seqlens, B, total, max_seqlen, workspace};
+  return fa::launch_fwd_varlen(a, va, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int D, int deterministic) {
   if (check_shape(B, Hq, Hkv, N, D, 1.0f) != FA_OK) return 0;
   if (check_mode(N, deterministic) != FA_OK) return 0;

@@ -41,7 +41,7 @@ constexpr int kFwdBM = 128;   // queries per workgroup
 constexpr int kFwdBN = 64;    // keys per K/V tile
 constexpr int kFwdWaves = 4;
 
-template <int D, bool CAUSAL, int POLYQ>
+template <int D, bool CAUSAL, int POLYQ, bool VARLEN>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict__ Q,
                                                      const uint16_t* __restrict__ K,
                                                      const uint16_t* __restrict__ V,
@@ -62,20 +62,49 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
   __shared__ __attribute__((aligned(1024))) char vbuf0[TB];
   __shared__ __attribute__((aligned(1024))) char vbuf1[TB];
 
-  // Grid order: consecutive workgroup ids walk heads first, so with B*Hq a
-  // multiple of 8 every tile of a head lands on the same XCD (ids are dealt to
-  // the 8 XCDs round-robin) and shares K/V in that XCD's L2; query tiles go
-  // from last to first so that, under the causal mask, the longest tiles
-  // start first.
+  // Work item of this workgroup: (sequence, query head, query tile).
+  // Dense grid order: consecutive workgroup ids walk heads first, so with
+  // B*Hq a multiple of 8 every tile of a head lands on the same XCD (ids are
+  // dealt to the 8 XCDs round-robin) and shares K/V in that XCD's L2; query
+  // tiles go from last to first so that, under the causal mask, the longest
+  // tiles start first.  Variable length: the ids walk heads first over a list
+  // of (sequence, query tile) items sorted by work, largest first (the
+  // longest-first scheduling of the danialwang explainer, section 06), and a
+  // sequence's rows start at cu_seqlens[b] in every head's [total][D] matrix.
   const int wg = blockIdx.x;
-  const int bh = wg % p.BH;
-  const int qb = p.nqb - 1 - wg / p.BH;
-  const int b = bh / p.Hq, hq = bh % p.Hq;
-  const int hk = hq / p.G;
-  const size_t head_elems = (size_t)p.N * D;
-  const uint16_t* Kh = K + ((size_t)b * (p.Hq / p.G) + hk) * head_elems;
-  const uint16_t* Vh = V + ((size_t)b * (p.Hq / p.G) + hk) * head_elems;
-  const uint32_t head_bytes = (uint32_t)(head_elems * 2);
+  int N, qb, hq;
+  const uint16_t *Qh, *Kh, *Vh;
+  uint16_t* Oh;
+  float* Lh;
+  if constexpr (VARLEN) {
+    const int item = wg / p.Hq;
+    hq = wg % p.Hq;
+    if (item >= *p.n_items) return;  // the grid is sized for the worst case
+    const int b = p.items[2 * item];
+    qb = p.items[2 * item + 1];
+    const int s0 = min(max(p.cu[b], 0), p.total);
+    N = min(max(p.cu[b + 1] - s0, 0), p.total - s0);
+    const int hk = hq / p.G;
+    Qh = Q + ((size_t)hq * p.total + s0) * D;
+    Oh = O + ((size_t)hq * p.total + s0) * D;
+    Kh = K + ((size_t)hk * p.total + s0) * D;
+    Vh = V + ((size_t)hk * p.total + s0) * D;
+    Lh = LSE + (size_t)hq * p.total + s0;
+  } else {
+    const int bh = wg % p.BH;
+    qb = p.nqb - 1 - wg / p.BH;
+    const int b = bh / p.Hq;
+    hq = bh % p.Hq;
+    const int hk = hq / p.G;
+    N = p.N;
+    const size_t he = (size_t)N * D;
+    Qh = Q + (size_t)bh * he;
+    Oh = O + (size_t)bh * he;
+    Kh = K + ((size_t)b * (p.Hq / p.G) + hk) * he;
+    Vh = V + ((size_t)b * (p.Hq / p.G) + hk) * he;
+    Lh = LSE + (size_t)bh * N;
+  }
+  const uint32_t head_bytes = (uint32_t)((size_t)N * D * 2);
 
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
@@ -86,7 +115,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
 
   // Q fragments (B operand of S^T = K Q^T): k-step t covers d in [16t, 16t+16),
   // lane half h holds d = 16t + 8h .. +8 of query qi (rows past N read as 0).
-  const rsrc_t qr = make_rsrc_uniform(Q + (size_t)bh * head_elems, head_bytes);
+  const rsrc_t qr = make_rsrc_uniform(Qh, head_bytes);
   bf16x8 qf[D / 16];
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) qf[t] = as_bf16x8(buf_load16(qr, (uint32_t)(qi * RB + 32 * t + 16 * h)));
@@ -102,7 +131,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
   // Every wave walks all tiles of the workgroup; a tile wholly above a wave's
   // diagonal is masked to -inf and adds exactly nothing (at most one such tile
   // per wave, kept so the pipeline has no per-wave branch).
-  const int kend = CAUSAL ? min(p.N, q0 + BM) : p.N;
+  const int kend = CAUSAL ? min(N, q0 + BM) : N;
   const int ntiles = (kend + BN - 1) / BN;
 
   // ---- direct HBM -> LDS staging -------------------------------------------
@@ -152,9 +181,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
   // k0 + 32 sb + 8 (r/4) + 4 h + r % 4.
   auto mask = [&](int kt, f32x16 (&sv)[2]) {
     const int k0 = kt * BN;
-    if ((k0 + BN > p.N) || (CAUSAL && (k0 + BN - 1 > qw))) {
+    if ((k0 + BN > N) || (CAUSAL && (k0 + BN - 1 > qw))) {
       keep_branch();
-      int lim = p.N - 1 - k0 - 4 * h;
+      int lim = N - 1 - k0 - 4 * h;
       if (CAUSAL) lim = min(lim, qi - k0 - 4 * h);
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
@@ -310,7 +339,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
   // dropped by the buffer range.
   const float l_tot = xhalf_sum(l_part);
   const float inv = 1.f / l_tot;
-  const rsrc_t orr = make_rsrc_uniform(O + (size_t)bh * head_elems, head_bytes);
+  const rsrc_t orr = make_rsrc_uniform(Oh, head_bytes);
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -320,7 +349,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
       w[1] = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
       buf_store8(orr, (uint32_t)(qi * RB + (32 * db + 8 * g + 4 * h) * 2), w);
     }
-  if (h == 0 && qi < p.N) LSE[(size_t)bh * p.N + qi] = (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2;
+  if (h == 0 && qi < N) Lh[qi] = (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2;
 }
 
 template <int D, bool CAUSAL, int POLYQ>
@@ -333,7 +362,7 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   p.nqb = (a.N + kFwdBM - 1) / kFwdBM;
   p.c = a.scale * kLog2e;
   const dim3 grid((unsigned)(p.BH * p.nqb));
-  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, POLYQ>), grid, dim3(64 * kFwdWaves), 0, stream,
+  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, POLYQ, false>), grid, dim3(64 * kFwdWaves), 0, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (uint16_t*)a.o, a.lse, p);
   return hipGetLastError();
@@ -348,7 +377,116 @@ hipError_t launch_fwd_c(const FwdArgs& a, hipStream_t s) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Work list of a variable-length batch: every (sequence b, query tile qb), in
+// decreasing order of its number of K/V tiles (the work it does), so that the
+// longest items start first and no long one is left running alone at the end
+// (danialwang explainer, section 06).  One workgroup: a counting sort over the
+// cost in LDS.  Equal costs come out in any order; each item writes its own
+// rows, so the result does not depend on it.  cu_seqlens entries are clamped
+// into [0, total], so no item can address outside the tensors.
+constexpr int kSchedThreads = 1024;
+constexpr int kSchedMaxCost = 16384 - kSchedThreads - 1;  // histogram + chunk sums <= 64 KiB
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(const int* __restrict__ cu,
+                                                                      int B, int total,
+                                                                      int max_cost,
+                                                                      int* __restrict__ n_items,
+                                                                      int* __restrict__ items) {
+  extern __shared__ int sm[];
+  int* hist = sm;                    // max_cost + 1 counters, then start offsets
+  int* csum = sm + max_cost + 1;     // per-thread chunk sums
+  const int tid = threadIdx.x;
+  const int ncost = max_cost + 1;
+  for (int c = tid; c < ncost; c += kSchedThreads) hist[c] = 0;
+  __syncthreads();
+  auto seq_len = [&](int b) {
+    const int s0 = min(max(cu[b], 0), total);
+    return min(max(cu[b + 1] - s0, 0), total - s0);
+  };
+  auto cost = [&](int len, int qb) {
+    const int kend = CAUSAL ? min(len, (qb + 1) * kFwdBM) : len;
+    return min((kend + kFwdBN - 1) / kFwdBN, max_cost);
+  };
+  for (int b = tid; b < B; b += kSchedThreads) {
+    const int len = seq_len(b);
+    for (int qb = 0; qb * kFwdBM < len; ++qb) atomicAdd(&hist[cost(len, qb)], 1);
+  }
+  __syncthreads();
+  // Exclusive scan in decreasing cost: slot r = max_cost - c.  Thread t owns
+  // slots [t CH, (t+1) CH).
+  const int CH = (ncost + kSchedThreads - 1) / kSchedThreads;
+  int mine = 0;
+  for (int r = tid * CH; r < min((tid + 1) * CH, ncost); ++r) mine += hist[max_cost - r];
+  csum[tid] = mine;
+  __syncthreads();
+  for (int off = 1; off < kSchedThreads; off <<= 1) {  // inclusive scan of the chunk sums
+    const int v = tid >= off ? csum[tid - off] : 0;
+    __syncthreads();
+    csum[tid] += v;
+    __syncthreads();
+  }
+  int run = csum[tid] - mine;
+  for (int r = tid * CH; r < min((tid + 1) * CH, ncost); ++r) {
+    const int c = max_cost - r;
+    const int cnt = hist[c];
+    hist[c] = run;
+    run += cnt;
+  }
+  if (tid == kSchedThreads - 1) *n_items = csum[tid];
+  __syncthreads();
+  for (int b = tid; b < B; b += kSchedThreads) {
+    const int len = seq_len(b);
+    for (int qb = 0; qb * kFwdBM < len; ++qb) {
+      const int pos = atomicAdd(&hist[cost(len, qb)], 1);
+      items[2 * pos] = b;
+      items[2 * pos + 1] = qb;
+    }
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_fwd_varlen_t(const FwdArgs& a, const VarlenArgs& v, hipStream_t s) {
+  const size_t items_max = (size_t)v.total / kFwdBM + v.B;
+  char* ws = (char*)v.workspace;
+  int* n_items = (int*)ws;
+  int* items = (int*)(ws + 256);
+  const int max_cost = (v.max_seqlen + kFwdBN - 1) / kFwdBN;
+  const size_t shm = (size_t)(max_cost + 1 + kSchedThreads) * sizeof(int);
+  hipLaunchKernelGGL((varlen_schedule_kernel<CAUSAL>), dim3(1), dim3(kSchedThreads), shm, s, v.cu,
+                     v.B, v.total, max_cost, n_items, items);
+  FwdParams p;
+  p.BH = 0;
+  p.Hq = a.Hq;
+  p.G = a.Hq / a.Hkv;
+  p.N = 0;
+  p.nqb = 0;
+  p.c = a.scale * kLog2e;
+  p.cu = v.cu;
+  p.items = items;
+  p.n_items = n_items;
+  p.total = v.total;
+  const dim3 grid((unsigned)(items_max * a.Hq));
+  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, 0, true>), grid, dim3(64 * kFwdWaves), 0, s,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     (uint16_t*)a.o, a.lse, p);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+size_t varlen_workspace_bytes(int B, int total) {
+  return 256 + ((size_t)total / kFwdBM + B) * 2 * sizeof(int);
+}
+
+int varlen_max_seqlen_limit() { return kSchedMaxCost * kFwdBN; }
+
+hipError_t launch_fwd_varlen(const FwdArgs& a, const VarlenArgs& v, hipStream_t s) {
+  if (a.D == 64)
+    return a.causal ? launch_fwd_varlen_t<64, true>(a, v, s) : launch_fwd_varlen_t<64, false>(a, v, s);
+  return a.causal ? launch_fwd_varlen_t<128, true>(a, v, s) : launch_fwd_varlen_t<128, false>(a, v, s);
+}
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {
   if (a.D == 64) return a.causal ? launch_fwd_c<64, true>(a, s) : launch_fwd_c<64, false>(a, s);

@@ -26,9 +26,29 @@ struct FwdParams {
   int N;
   int nqb;    // query tiles per head
   float c;    // scale * log2(e)
+  // Variable length only: cumulative sequence starts (B + 1), the work list
+  // of (sequence, query tile) pairs and its length, and the token count.
+  const int* cu;
+  const int* items;
+  const int* n_items;
+  int total;
 };
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+
+// Variable-length forward.  Layout: q, o [Hq][total][D]; k, v [Hkv][total][D];
+// lse [Hq][total]; sequence b is rows cu[b] .. cu[b+1] of every head.
+struct VarlenArgs {
+  const int* cu;       // device, B + 1 entries
+  int B;
+  int total;
+  int max_seqlen;
+  void* workspace;     // varlen_workspace_bytes(B, total)
+};
+size_t varlen_workspace_bytes(int B, int total);
+// Largest max_seqlen the work-list builder supports (its histogram lives in LDS).
+int varlen_max_seqlen_limit();
+hipError_t launch_fwd_varlen(const FwdArgs& a, const VarlenArgs& v, hipStream_t stream);
 
 struct BwdArgs {
   const void* q;

@@ -143,6 +143,38 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, voi
               int Hq, int Hkv, int N, int D, int causal, float scale, void* workspace,
               size_t workspace_bytes, int deterministic, void* stream);
 
+/*
+ * Variable-length batches (forward).  B sequences of lengths len_b are packed
+ * along one token axis of total = sum_b len_b tokens:
+ *   q, o [Hq][total][D], k, v [Hkv][total][D] (bf16), lse [Hq][total] (fp32);
+ *   sequence b is rows cu_seqlens[b] .. cu_seqlens[b+1] - 1 of every head's
+ *   [total][D] matrix, and attends only within itself (causal: key j <= query
+ *   i, positions counted from the sequence start).
+ *   cu_seqlens: device int32[B + 1], nondecreasing, cu_seqlens[0] = 0,
+ *     cu_seqlens[B] = total (read on the device only; entries outside
+ *     [0, total] are clamped, so a malformed array cannot make a kernel
+ *     address outside the tensors, but its results are unspecified).
+ *     Sequences of length 0 are allowed.
+ *   max_seqlen: an upper bound of every len_b, 1 <= max_seqlen <=
+ *     fa_varlen_max_seqlen() (sizes the scheduler; a sequence longer than it
+ *     is still computed correctly, only scheduled as if it were max_seqlen).
+ *   workspace: device memory of fa_fwd_varlen_workspace_size(B, total)
+ *     bytes, 256-byte aligned, caller-owned scratch for the work list.
+ * The work is scheduled on the device, without a host round trip: a first
+ * kernel lists every (sequence, 128-query tile) and sorts the list by the
+ * number of K/V tiles each item processes, largest first (danialwang
+ * explainer, section 06, starting the longest work first); the attention
+ * kernel takes items in that order.  total = 0 is valid and writes nothing.
+ * Errors as fa_fwd, plus FA_ERR_WORKSPACE, and FA_ERR_INVALID for B < 1,
+ * total < 0 or max_seqlen outside its range.
+ */
+size_t fa_fwd_varlen_workspace_size(int B, int total);
+int fa_varlen_max_seqlen(void);
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int* cu_seqlens, int B, int Hq, int Hkv, int total, int max_seqlen,
+                  int D, int causal, float scale, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
 /* Static text for a status code. */
 const char* fa_strerror(int status);
 

@@ -96,3 +96,49 @@ def generate_workload(w: Workload, seed: int = 0):
 
 def sha256(t: torch.Tensor) -> str:
     return hashlib.sha256(t.contiguous().view(torch.int16).numpy().tobytes()).hexdigest()
+
+
+def varlen_lengths(n_seqs: int, total: int, lo: int, hi: int, *, seed: int = 0) -> list:
+    """A seeded mix of sequence lengths: log-uniform in [lo, hi], rescaled so
+    they sum to exactly `total` (each kept >= 1)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    u = torch.rand(n_seqs, generator=g, dtype=torch.float64)
+    raw = torch.exp(torch.log(torch.tensor(float(lo))) +
+                    u * (torch.log(torch.tensor(float(hi))) - torch.log(torch.tensor(float(lo)))))
+    lens = [max(1, int(x)) for x in (raw * (total / raw.sum())).tolist()]
+    lens[-1] += total - sum(lens)
+    if lens[-1] < 1:
+        raise ValueError("lengths do not fit the total")
+    return lens
+
+
+def generate_varlen(lens, Hq: int, Hkv: int, D: int, *, seed: int = 0, with_dout: bool = False):
+    """Packed variable-length inputs: q [Hq,total,D], k/v [Hkv,total,D] (and
+    dout [Hq,total,D]) bf16 CPU tensors plus cu_seqlens int32 [B+1].  Values:
+    fp32 randn in the order Q, K, V, dO, rounded to bf16, as for the dense
+    workloads."""
+    total = int(sum(lens))
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    q = torch.randn((Hq, total, D), generator=g, dtype=torch.float32)
+    k = torch.randn((Hkv, total, D), generator=g, dtype=torch.float32)
+    v = torch.randn((Hkv, total, D), generator=g, dtype=torch.float32)
+    out = [q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)]
+    if with_dout:
+        out.append(torch.randn((Hq, total, D), generator=g, dtype=torch.float32).to(torch.bfloat16))
+    cu = torch.zeros(len(lens) + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(torch.tensor(lens, dtype=torch.int64), 0).to(torch.int32)
+    return tuple(out) + (cu,)
+
+
+# Variable-length forward workload: 64 sequences, 65536 tokens in total,
+# lengths log-uniform in [128, 8192] (seed 0), 16 heads, D = 128, causal.
+VARLEN = {"n_seqs": 64, "total": 65536, "lo": 128, "hi": 8192, "Hq": 16, "Hkv": 16, "D": 128,
+          "causal": True}
+
+
+def varlen_flops_fwd(lens, Hq: int, D: int, causal: bool) -> float:
+    """4 Hq len^2 D per sequence, halved under the causal mask."""
+    f = sum(4.0 * Hq * n * n * D for n in lens)
+    return f / 2 if causal else f

@@ -131,3 +131,40 @@ def test_bwd_stages_reject():
         fa.FA_ERR_ALIGN
     assert fa.fa_bwd_dq(Q, K, V, DO, Q, 1, 2, 2, 64, 64, 1, 0.1, WS, ws, 1, None) == \
         fa.FA_ERR_INVALID
+
+
+def fwdv(**kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, cu=DQ, B=3, Hq=2, Hkv=1, total=500, max_seqlen=300, D=128,
+             causal=1, scale=0.1, ws=WS, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return fa.fa_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cu"], a["B"], a["Hq"],
+                            a["Hkv"], a["total"], a["max_seqlen"], a["D"], a["causal"], a["scale"],
+                            a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), fa.FA_ERR_INVALID), (dict(cu=None), fa.FA_ERR_INVALID),
+    (dict(ws=None), fa.FA_ERR_INVALID), (dict(B=0), fa.FA_ERR_INVALID),
+    (dict(total=-1), fa.FA_ERR_INVALID), (dict(max_seqlen=0), fa.FA_ERR_INVALID),
+    (dict(max_seqlen=1 << 30), fa.FA_ERR_INVALID), (dict(D=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(Hq=3, Hkv=2), fa.FA_ERR_INVALID), (dict(scale=float("nan")), fa.FA_ERR_INVALID),
+    (dict(cu=DQ + 2), fa.FA_ERR_ALIGN), (dict(ws=WS + 16), fa.FA_ERR_ALIGN),
+    (dict(wsb=64), fa.FA_ERR_WORKSPACE), (dict(o=Q), fa.FA_ERR_INVALID),
+    (dict(ws=L), fa.FA_ERR_INVALID), (dict(cu=O + 64), fa.FA_ERR_INVALID),
+    (dict(Hq=1 << 10, Hkv=1 << 10, total=1 << 14), fa.FA_ERR_TOO_LARGE),
+])
+def test_fwd_varlen_rejects(kw, code):
+    assert fwdv(**kw) == code
+
+
+def test_fwd_varlen_empty_batch_is_a_no_op():
+    # total = 0: every check passes and nothing is launched (fake pointers).
+    assert fwdv(total=0, max_seqlen=1) == fa.FA_OK
+
+
+def test_varlen_workspace_size():
+    assert fa.fa_fwd_varlen_workspace_size(0, 10) == 0
+    assert fa.fa_fwd_varlen_workspace_size(2, -1) == 0
+    # One (sequence, 128-query tile) pair of int32 per possible item, plus a header.
+    assert fa.fa_fwd_varlen_workspace_size(4, 1000) >= (1000 // 128 + 4) * 8
+    assert fa.fa_varlen_max_seqlen() >= 1 << 19
