@@ -15,6 +15,7 @@ Prints ONE JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import math
 import hashlib
 import json
 import os
@@ -90,6 +91,48 @@ def cpu_baseline(w, n_heads: int):
                       f"slices (N={w.N}, D={w.D}, causal), {dt:.1f} s wall"}
 
 
+def bench_varlen(fa, torch, dev, stream, reps: int = 20) -> dict:
+    """Variable-length forward on the packed workload of synth.VARLEN (the
+    work-list kernel included in the timed call)."""
+    import synth
+    w = synth.VARLEN
+    lens = synth.varlen_lengths(w["n_seqs"], w["total"], w["lo"], w["hi"])
+    q, k, v, cu = (t.to(dev) for t in synth.generate_varlen(lens, w["Hq"], w["Hkv"], w["D"]))
+    scale = 1.0 / math.sqrt(w["D"])
+    o = torch.empty_like(q)
+    lse = torch.empty((w["Hq"], w["total"]), dtype=torch.float32, device=dev)
+    wsb = fa.fa_fwd_varlen_workspace_size(len(lens), w["total"])
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    sh = stream.cuda_stream
+
+    def call():
+        rc = fa.fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              lse.data_ptr(), cu.data_ptr(), len(lens), w["Hq"], w["Hkv"],
+                              w["total"], max(lens), w["D"], w["causal"], scale, ws.data_ptr(),
+                              wsb, sh)
+        if rc != 0:
+            raise RuntimeError(f"fa_fwd_varlen: {fa.fa_strerror(rc)}")
+
+    for _ in range(3):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    flops = synth.varlen_flops_fwd(lens, w["Hq"], w["D"], w["causal"])
+    tf = flops / (us * 1e-6) / 1e12
+    return {"workload": f"{len(lens)} causal sequences, {w['total']} tokens "
+                        f"(lengths {min(lens)}..{max(lens)}, log-uniform mix), "
+                        f"H{w['Hq']} D{w['D']}",
+            "us": round(us, 1), "tflops": round(tf, 1),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -100,6 +143,8 @@ def main() -> int:
                          "default), fixed order recomputing dS (deterministic, small "
                          "workspace), or atomic adds")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the variable-length forward measurement")
     ap.add_argument("--cpu-heads", type=int, default=16)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device-to-device copy of MIB MiB (read MIB, write MIB) "
@@ -268,6 +313,8 @@ def main() -> int:
                                        "workspace_bytes": ows_bytes})
         del ows
     out["bwd"]["workspace_bytes"] = ws_bytes
+    if not args.no_extras:
+        out["extras"] = {"varlen_fwd": bench_varlen(fa, torch, dev, stream)}
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_heads} heads")
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)

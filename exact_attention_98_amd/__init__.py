@@ -16,8 +16,9 @@ import os
 
 __all__ = ["fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_workspace_size", "fa_bwd_preprocess",
            "fa_bwd_main", "fa_bwd_dq", "fa_fwd_varlen", "fa_fwd_varlen_workspace_size",
-           "fa_varlen_max_seqlen", "fa_strerror", "forward", "backward", "forward_varlen",
-           "FaError", "library_path", "load"]
+           "fa_varlen_max_seqlen", "fa_fwd_splitkv", "fa_fwd_splitkv_num_splits",
+           "fa_fwd_splitkv_workspace_size", "fa_strerror", "forward", "backward",
+           "forward_varlen", "forward_splitkv", "FaError", "library_path", "load"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libfa.so")
@@ -33,7 +34,8 @@ FA_ERR_TOO_LARGE = -6
 
 EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_workspace_size", "fa_bwd_preprocess",
             "fa_bwd_main", "fa_bwd_dq", "fa_fwd_varlen", "fa_fwd_varlen_workspace_size",
-            "fa_varlen_max_seqlen", "fa_strerror")
+            "fa_varlen_max_seqlen", "fa_fwd_splitkv", "fa_fwd_splitkv_num_splits",
+            "fa_fwd_splitkv_workspace_size", "fa_strerror")
 
 
 class FaError(RuntimeError):
@@ -78,6 +80,13 @@ def load():
     lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, vp, sz,
                                   vp]
     lib.fa_fwd_varlen.restype = ci
+    lib.fa_fwd_splitkv_num_splits.argtypes = [ci] * 6
+    lib.fa_fwd_splitkv_num_splits.restype = ci
+    lib.fa_fwd_splitkv_workspace_size.argtypes = [ci] * 7
+    lib.fa_fwd_splitkv_workspace_size.restype = sz
+    lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, ci, vp, sz,
+                                   vp]
+    lib.fa_fwd_splitkv.restype = ci
     lib.fa_strerror.argtypes = [ci]
     lib.fa_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -134,6 +143,21 @@ def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, B, Hq, Hkv, total, max_seqlen, D,
                   workspace, workspace_bytes, stream) -> int:
     return load().fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, B, Hq, Hkv, total, max_seqlen, D,
                                 int(causal), float(scale), workspace, workspace_bytes, stream)
+
+
+def fa_fwd_splitkv_num_splits(B, Hq, Hkv, Nq, Nk, D) -> int:
+    return int(load().fa_fwd_splitkv_num_splits(B, Hq, Hkv, Nq, Nk, D))
+
+
+def fa_fwd_splitkv_workspace_size(B, Hq, Hkv, Nq, Nk, D, num_splits) -> int:
+    return int(load().fa_fwd_splitkv_workspace_size(B, Hq, Hkv, Nq, Nk, D, num_splits))
+
+
+def fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, D, causal, scale, num_splits, workspace,
+                   workspace_bytes, stream) -> int:
+    return load().fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, D, int(causal),
+                                 float(scale), int(num_splits), workspace, workspace_bytes,
+                                 stream)
 
 
 def fa_strerror(status: int) -> str:
@@ -260,4 +284,36 @@ def forward_varlen(q, k, v, cu_seqlens, max_seqlen: int, causal: bool, scale: fl
                        scale, workspace.data_ptr(), workspace.numel(), _stream_handle(q.device))
     if rc != FA_OK:
         raise FaError(rc, "fa_fwd_varlen")
+    return out, lse
+
+
+def forward_splitkv(q, k, v, causal: bool, scale: float, *, num_splits: int = 0, out=None,
+                    lse=None, workspace=None):
+    """Decode-shaped forward: q [B,Hq,Nq,D] over k/v [B,Hkv,Nk,D] (bf16 device
+    tensors), keys split into num_splits ranges (0: automatic) and merged.
+    Causal aligns the queries with the last Nq key positions."""
+    import torch
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, D]")
+    B, Hq, Nq, D = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    _check("q", q, torch.bfloat16, (B, Hq, Nq, D))
+    _check("k", k, torch.bfloat16, (B, Hkv, Nk, D))
+    _check("v", v, torch.bfloat16, (B, Hkv, Nk, D))
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    _check("out", out, torch.bfloat16, (B, Hq, Nq, D))
+    _check("lse", lse, torch.float32, (B, Hq, Nq))
+    ws_bytes = fa_fwd_splitkv_workspace_size(B, Hq, Hkv, Nq, Nk, D, num_splits)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    wptr = workspace.data_ptr() if workspace is not None else None
+    wn = workspace.numel() if workspace is not None else 0
+    rc = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                        B, Hq, Hkv, Nq, Nk, D, causal, scale, num_splits, wptr, wn,
+                        _stream_handle(q.device))
+    if rc != FA_OK:
+        raise FaError(rc, "fa_fwd_splitkv")
     return out, lse

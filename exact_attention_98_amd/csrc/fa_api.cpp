@@ -119,6 +119,76 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
   return fa::launch_fwd_varlen(a, va, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Shape checks of the split-KV forward (q and k checked as their own
+// tensors, which may differ in length).
+int check_split(int B, int Hq, int Hkv, int Nq, int Nk, int D, int causal, float scale) {
+  if (Nq < 1 || Nk < 1) return FA_ERR_INVALID;
+  if (causal && Nq > Nk) return FA_ERR_INVALID;
+  int rc = check_shape(B, Hq, Hkv, Nq, D, scale);
+  if (rc != FA_OK) return rc;
+  return check_shape(B, Hkv, Hkv, Nk, D, scale);
+}
+
+int resolve_splits(int B, int Hq, int Hkv, int Nq, int Nk, int num_splits) {
+  if (num_splits == 0) return fa::split_auto(B, Hq, Hkv, Nq, Nk);
+  if (num_splits < 0 || num_splits > fa::split_max(Nk)) return -1;
+  return num_splits;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd_splitkv_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int D) {
+  if (check_split(B, Hq, Hkv, Nq, Nk, D, 0, 1.0f) != FA_OK) return 0;
+  return fa::split_auto(B, Hq, Hkv, Nq, Nk);
+}
+
+size_t fa_fwd_splitkv_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int D,
+                                     int num_splits) {
+  if (check_split(B, Hq, Hkv, Nq, Nk, D, 0, 1.0f) != FA_OK) return 0;
+  const int sp = resolve_splits(B, Hq, Hkv, Nq, Nk, num_splits);
+  if (sp < 1) return 0;
+  return fa::split_workspace_bytes(B, Hq, Nq, D, sp);
+}
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                   int Hq, int Hkv, int Nq, int Nk, int D, int causal, float scale,
+                   int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID;
+  int rc = check_split(B, Hq, Hkv, Nq, Nk, D, causal, scale);
+  if (rc != FA_OK) return rc;
+  const int sp = resolve_splits(B, Hq, Hkv, Nq, Nk, num_splits);
+  if (sp < 1) return FA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  const size_t wbytes = fa::split_workspace_bytes(B, Hq, Nq, D, sp);
+  if (wbytes > 0) {
+    if (!workspace || workspace_bytes < wbytes) return FA_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255u) != 0) return FA_ERR_ALIGN;
+  }
+  const size_t qb = (size_t)B * Hq * Nq * D * 2, kb = (size_t)B * Hkv * Nk * D * 2;
+  const size_t lb = (size_t)B * Hq * Nq * 4;
+  const void* outs[3] = {o, lse, workspace};
+  const size_t osz[3] = {qb, lb, wbytes};
+  const void* ins[3] = {q, k, v};
+  const size_t isz[3] = {qb, kb, kb};
+  for (int i = 0; i < 3; ++i) {
+    if (osz[i] == 0) continue;
+    for (int j = 0; j < 3; ++j)
+      if (overlaps(outs[i], osz[i], ins[j], isz[j])) return FA_ERR_INVALID;
+    for (int j = 0; j < 3; ++j)
+      if (j != i && osz[j] > 0 && overlaps(outs[i], osz[i], outs[j], osz[j])) return FA_ERR_INVALID;
+  }
+  fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Nq, D, causal ? 1 : 0, scale, 0};
+  const fa::SplitArgs sa{Nq, Nk, sp, workspace};
+  return fa::launch_fwd_split(a, sa, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int D, int deterministic) {
   if (check_shape(B, Hq, Hkv, N, D, 1.0f) != FA_OK) return 0;
   if (check_mode(N, deterministic) != FA_OK) return 0;

@@ -41,7 +41,12 @@ constexpr int kFwdBM = 128;   // queries per workgroup
 constexpr int kFwdBN = 64;    // keys per K/V tile
 constexpr int kFwdWaves = 4;
 
-template <int D, bool CAUSAL, int POLYQ, bool VARLEN>
+// Addressing modes of the forward kernel.
+constexpr int kModeDense = 0;   // [B][H][N][D], one workgroup per (b, hq, query tile)
+constexpr int kModeVarlen = 1;  // packed sequences, work list sorted longest first
+constexpr int kModeSplit = 2;   // query rows of a K/V group, one key range per workgroup
+
+template <int D, bool CAUSAL, int POLYQ, int MODE>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict__ Q,
                                                      const uint16_t* __restrict__ K,
                                                      const uint16_t* __restrict__ V,
@@ -71,12 +76,35 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
   // of (sequence, query tile) items sorted by work, largest first (the
   // longest-first scheduling of the danialwang explainer, section 06), and a
   // sequence's rows start at cu_seqlens[b] in every head's [total][D] matrix.
+  // Split-KV (decode-shaped queries): the rows of one workgroup are the
+  // G * Nq query rows of the G query heads that share K/V head hk (contiguous
+  // in [B][Hq][Nq][D]), and the keys are one range of the Nk keys; partial
+  // results (O / l and LSE per row) are merged by a second kernel.
   const int wg = blockIdx.x;
-  int N, qb, hq;
+  int N, Nkv, qb, hq;   // N: query rows; Nkv: keys this workgroup walks
+  int koff = 0;         // index of its first key (split-KV)
+  int split = 0;
   const uint16_t *Qh, *Kh, *Vh;
   uint16_t* Oh;
   float* Lh;
-  if constexpr (VARLEN) {
+  if constexpr (MODE == kModeSplit) {
+    int idx = wg;
+    const int bhk = idx % p.BH;  // BH = B * Hkv here
+    idx /= p.BH;
+    qb = idx % p.nqb;            // row block
+    split = idx / p.nqb;
+    const int b = bhk / (p.Hq / p.G), hk = bhk % (p.Hq / p.G);
+    hq = hk * p.G;
+    N = p.G * p.Nq;
+    koff = split * p.tiles_per_split * kFwdBN;
+    Nkv = max(min(p.Nk - koff, p.tiles_per_split * kFwdBN), 0);
+    const size_t row0 = ((size_t)b * p.Hq + hq) * p.Nq;
+    Qh = Q + row0 * D;
+    Oh = O + row0 * D;
+    Lh = LSE + row0;
+    Kh = K + ((size_t)bhk * p.Nk + koff) * D;
+    Vh = V + ((size_t)bhk * p.Nk + koff) * D;
+  } else if constexpr (MODE == kModeVarlen) {
     const int item = wg / p.Hq;
     hq = wg % p.Hq;
     if (item >= *p.n_items) return;  // the grid is sized for the worst case
@@ -84,6 +112,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
     qb = p.items[2 * item + 1];
     const int s0 = min(max(p.cu[b], 0), p.total);
     N = min(max(p.cu[b + 1] - s0, 0), p.total - s0);
+    Nkv = N;
     const int hk = hq / p.G;
     Qh = Q + ((size_t)hq * p.total + s0) * D;
     Oh = O + ((size_t)hq * p.total + s0) * D;
@@ -97,6 +126,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
     hq = bh % p.Hq;
     const int hk = hq / p.G;
     N = p.N;
+    Nkv = N;
     const size_t he = (size_t)N * D;
     Qh = Q + (size_t)bh * he;
     Oh = O + (size_t)bh * he;
@@ -104,7 +134,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
     Vh = V + ((size_t)b * (p.Hq / p.G) + hk) * he;
     Lh = LSE + (size_t)bh * N;
   }
-  const uint32_t head_bytes = (uint32_t)((size_t)N * D * 2);
+  const uint32_t head_bytes = (uint32_t)((size_t)N * D * 2);  // query rows
+  const uint32_t kv_bytes = (uint32_t)((size_t)Nkv * D * 2);
 
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
@@ -131,7 +162,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
   // Every wave walks all tiles of the workgroup; a tile wholly above a wave's
   // diagonal is masked to -inf and adds exactly nothing (at most one such tile
   // per wave, kept so the pipeline has no per-wave branch).
-  const int kend = CAUSAL ? min(N, q0 + BM) : N;
+  // Split-KV causal rows see keys up to Nk - Nq + (row mod Nq): no tile-level
+  // cut, the mask handles it.
+  const int kend = (CAUSAL && MODE != kModeSplit) ? min(N, q0 + BM) : Nkv;
   const int ntiles = (kend + BN - 1) / BN;
 
   // ---- direct HBM -> LDS staging -------------------------------------------
@@ -147,7 +180,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
   }
   auto issue = [&](const uint16_t* src, int kt, char* dst) {
     const uint32_t base = (uint32_t)kt * TB;
-    const uint32_t left = head_bytes > base ? head_bytes - base : 0u;
+    const uint32_t left = kv_bytes > base ? kv_bytes - base : 0u;
     const rsrc_t r = make_rsrc_uniform((const char*)src + base, left);
 #pragma unroll
     for (int s = 0; s < NLD; ++s) lds_dma16(r, (lds_void*)(dst + (s * kFwdWaves + wave) * 1024), ld_off[s]);
@@ -179,12 +212,20 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
   // Mask keys past the end and, under causal, keys after the query, on the
   // tiles that need it.  Register r of half sb holds key
   // k0 + 32 sb + 8 (r/4) + 4 h + r % 4.
+  // Last key each lane's query may see, in this workgroup's key numbering,
+  // and the smallest such key over the wave (which decides whether a tile
+  // needs the mask).
+  int qlast = qi, wave_qlast = qw;
+  if constexpr (MODE == kModeSplit) {
+    qlast = p.Nk - p.Nq + qi % p.Nq - koff;
+    wave_qlast = p.Nk - p.Nq - koff;
+  }
   auto mask = [&](int kt, f32x16 (&sv)[2]) {
     const int k0 = kt * BN;
-    if ((k0 + BN > N) || (CAUSAL && (k0 + BN - 1 > qw))) {
+    if ((k0 + BN > Nkv) || (CAUSAL && (k0 + BN - 1 > wave_qlast))) {
       keep_branch();
-      int lim = N - 1 - k0 - 4 * h;
-      if (CAUSAL) lim = min(lim, qi - k0 - 4 * h);
+      int lim = Nkv - 1 - k0 - 4 * h;
+      if (CAUSAL) lim = min(lim, qlast - k0 - 4 * h);
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
@@ -338,6 +379,28 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict_
   // Final correction: O = O / l, LSE = (m_ref + log2 l) ln 2.  Rows past N are
   // dropped by the buffer range.
   const float l_tot = xhalf_sum(l_part);
+  if constexpr (MODE == kModeSplit) {
+    if (p.splits > 1) {
+      // Partial result of this key range, fp32: O / l and LSE; a row that sees
+      // no key of the range gives O = 0 and LSE = -inf (weight 0 in the merge).
+      const bool none = !(l_tot > 0.f);
+      const float pinv = none ? 0.f : 1.f / l_tot;
+      const size_t prow = ((size_t)(wg % p.BH) * p.splits + split) * N;
+      const rsrc_t por = make_rsrc_uniform(p.o_part + prow * D, (uint32_t)((size_t)N * D * 4));
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          u32x4 w;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) w[j] = __builtin_bit_cast(uint32_t, oacc[db][4 * g + j] * pinv);
+          __builtin_amdgcn_raw_buffer_store_b128(w, por, (uint32_t)((qi * D + 32 * db + 8 * g + 4 * h) * 4), 0, 0);
+        }
+      if (h == 0 && qi < N)
+        p.l_part[prow + qi] = none ? -__builtin_inff() : (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2;
+      return;
+    }
+  }
   const float inv = 1.f / l_tot;
   const rsrc_t orr = make_rsrc_uniform(Oh, head_bytes);
 #pragma unroll
@@ -362,7 +425,7 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   p.nqb = (a.N + kFwdBM - 1) / kFwdBM;
   p.c = a.scale * kLog2e;
   const dim3 grid((unsigned)(p.BH * p.nqb));
-  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, POLYQ, false>), grid, dim3(64 * kFwdWaves), 0, stream,
+  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, POLYQ, kModeDense>), grid, dim3(64 * kFwdWaves), 0, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (uint16_t*)a.o, a.lse, p);
   return hipGetLastError();
@@ -468,13 +531,117 @@ hipError_t launch_fwd_varlen_t(const FwdArgs& a, const VarlenArgs& v, hipStream_
   p.n_items = n_items;
   p.total = v.total;
   const dim3 grid((unsigned)(items_max * a.Hq));
-  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, 0, true>), grid, dim3(64 * kFwdWaves), 0, s,
+  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, 0, kModeVarlen>), grid, dim3(64 * kFwdWaves), 0, s,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (uint16_t*)a.o, a.lse, p);
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Merge of the split-KV partial results of one query row: with L_s the
+// natural-log LSE of key range s and O_s its normalised output,
+// LSE = log sum_s exp(L_s) and O = sum_s exp(L_s - LSE) O_s (an exact
+// re-weighting; ranges a row cannot see have L_s = -inf and weight 0).  One
+// wave per row, D / 64 elements per lane.
+template <int D>
+__global__ __launch_bounds__(256) void split_merge_kernel(const float* __restrict__ o_part,
+                                                          const float* __restrict__ l_part,
+                                                          uint16_t* __restrict__ O,
+                                                          float* __restrict__ LSE, int rows_grp,
+                                                          int splits, int rows) {
+  constexpr int EPL = D / 64;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int grp = row / rows_grp, r = row % rows_grp;
+  const size_t base = (size_t)grp * splits * rows_grp + r;   // partial row of split 0
+  float mx = -__builtin_inff();
+  for (int s = 0; s < splits; ++s) mx = fmaxf(mx, l_part[base + (size_t)s * rows_grp]);
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  float sum = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const float ls = l_part[base + (size_t)s * rows_grp];
+    const float wgt = (ls == -__builtin_inff()) ? 0.f : __expf(ls - mx);
+    sum += wgt;
+    const float* op = o_part + (base + (size_t)s * rows_grp) * D + lane * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] += wgt * op[e];
+  }
+  const float inv = 1.f / sum;
+  uint16_t* orow = O + (size_t)row * D + lane * EPL;
+  if constexpr (EPL == 2) {
+    *(uint32_t*)orow = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  } else {
+    orow[0] = (uint16_t)(pack_bf16x2(acc[0] * inv, 0.f) & 0xffffu);
+  }
+  if (lane == 0) LSE[row] = mx + __logf(sum);
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_fwd_split_t(const FwdArgs& a, const SplitArgs& sa, hipStream_t s) {
+  const int G = a.Hq / a.Hkv;
+  const int M = G * sa.Nq;
+  const int ntiles = (sa.Nk + kFwdBN - 1) / kFwdBN;
+  FwdParams p;
+  p.BH = a.B * a.Hkv;
+  p.Hq = a.Hq;
+  p.G = G;
+  p.N = 0;
+  p.nqb = (M + kFwdBM - 1) / kFwdBM;
+  p.c = a.scale * kLog2e;
+  p.cu = nullptr;
+  p.items = nullptr;
+  p.n_items = nullptr;
+  p.total = 0;
+  p.Nq = sa.Nq;
+  p.Nk = sa.Nk;
+  p.splits = sa.splits;
+  p.tiles_per_split = (ntiles + sa.splits - 1) / sa.splits;
+  char* ws = (char*)sa.workspace;
+  const size_t rows = (size_t)a.B * a.Hq * sa.Nq;
+  p.o_part = (float*)ws;
+  p.l_part = (float*)(ws + ((rows * sa.splits * D * 4 + 255) & ~(size_t)255));
+  const dim3 grid((unsigned)(p.BH * p.nqb * sa.splits));
+  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, 0, kModeSplit>), grid, dim3(64 * kFwdWaves), 0, s,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     (uint16_t*)a.o, a.lse, p);
+  if (sa.splits > 1)
+    hipLaunchKernelGGL((split_merge_kernel<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s,
+                       (const float*)p.o_part, (const float*)p.l_part, (uint16_t*)a.o, a.lse, M,
+                       sa.splits, (int)rows);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+// Splits for a decode-shaped problem: enough workgroups for two per CU
+// (512 on the 256 CUs of an MI355X), without ranges shorter than 4 tiles.
+int split_auto(int B, int Hq, int Hkv, int Nq, int Nk) {
+  const int M = (Hq / Hkv) * Nq;
+  const long base = (long)B * Hkv * ((M + kFwdBM - 1) / kFwdBM);
+  const int ntiles = (Nk + kFwdBN - 1) / kFwdBN;
+  long want = (512 + base - 1) / base;
+  const long cap = (ntiles + 3) / 4;
+  if (want > cap) want = cap;
+  if (want < 1) want = 1;
+  return (int)want;
+}
+
+int split_max(int Nk) { return (Nk + kFwdBN - 1) / kFwdBN; }
+
+size_t split_workspace_bytes(int B, int Hq, int Nq, int D, int splits) {
+  if (splits <= 1) return 0;
+  const size_t rows = (size_t)B * Hq * Nq;
+  return ((rows * splits * D * 4 + 255) & ~(size_t)255) + ((rows * splits * 4 + 255) & ~(size_t)255);
+}
+
+hipError_t launch_fwd_split(const FwdArgs& a, const SplitArgs& sa, hipStream_t s) {
+  if (a.D == 64)
+    return a.causal ? launch_fwd_split_t<64, true>(a, sa, s) : launch_fwd_split_t<64, false>(a, sa, s);
+  return a.causal ? launch_fwd_split_t<128, true>(a, sa, s) : launch_fwd_split_t<128, false>(a, sa, s);
+}
 
 size_t varlen_workspace_bytes(int B, int total) {
   return 256 + ((size_t)total / kFwdBM + B) * 2 * sizeof(int);

@@ -32,6 +32,12 @@ struct FwdParams {
   const int* items;
   const int* n_items;
   int total;
+  // Split-KV only: query and key lengths, the key-range split, and the fp32
+  // partial results [B*Hkv][splits][G*Nq][D] and [B*Hkv][splits][G*Nq].
+  int Nq, Nk;
+  int splits, tiles_per_split;
+  float* o_part;
+  float* l_part;
 };
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
@@ -49,6 +55,19 @@ size_t varlen_workspace_bytes(int B, int total);
 // Largest max_seqlen the work-list builder supports (its histogram lives in LDS).
 int varlen_max_seqlen_limit();
 hipError_t launch_fwd_varlen(const FwdArgs& a, const VarlenArgs& v, hipStream_t stream);
+
+// Split-KV forward for decode-shaped problems: q, o [B][Hq][Nq][D], k, v
+// [B][Hkv][Nk][D], lse [B][Hq][Nq]; causal rows are aligned to the end of the
+// keys (query i sees keys j <= Nk - Nq + i).
+struct SplitArgs {
+  int Nq, Nk;
+  int splits;        // >= 1 (already resolved)
+  void* workspace;   // split_workspace_bytes(...)
+};
+int split_auto(int B, int Hq, int Hkv, int Nq, int Nk);
+int split_max(int Nk);
+size_t split_workspace_bytes(int B, int Hq, int Nq, int D, int splits);
+hipError_t launch_fwd_split(const FwdArgs& a, const SplitArgs& s, hipStream_t stream);
 
 struct BwdArgs {
   const void* q;

@@ -175,6 +175,33 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
                   int D, int causal, float scale, void* workspace, size_t workspace_bytes,
                   void* stream);
 
+/*
+ * Decode-shaped forward with the keys split across workgroups (split-KV).
+ * For few queries over long keys, typically G = Hq / Hkv query heads
+ * sharing one K/V head (multi-query / grouped attention, hotdry article,
+ * kernel-fusion section):
+ *   q, o [B][Hq][Nq][D], k, v [B][Hkv][Nk][D] (bf16), lse [B][Hq][Nq] (fp32),
+ *   1 <= Nq, 1 <= Nk, and Nq <= Nk when causal.
+ * causal != 0 aligns the queries with the end of the keys: query i sees keys
+ * j <= Nk - Nq + i (the Nq queries are the newest Nq positions).
+ * The G * Nq query rows of a K/V group are processed together against one
+ * range of keys per workgroup; with more than one range, each range writes
+ * an fp32 partial (O_s normalised, LSE_s) to the workspace and a second
+ * kernel merges them: LSE = log sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s.
+ *   num_splits: number of key ranges, 1 .. ceil(Nk / 64); 0 picks
+ *     fa_fwd_splitkv_num_splits() (enough workgroups to fill the GPU).
+ *   workspace: fa_fwd_splitkv_workspace_size() bytes (0 when one range:
+ *     workspace may then be NULL), 256-byte aligned, caller-owned scratch.
+ * Errors as fa_fwd, plus FA_ERR_INVALID for Nq < 1, Nk < 1, causal with
+ * Nq > Nk, or num_splits out of range, and FA_ERR_WORKSPACE.
+ */
+int fa_fwd_splitkv_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int D);
+size_t fa_fwd_splitkv_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int D,
+                                     int num_splits);
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                   int Hq, int Hkv, int Nq, int Nk, int D, int causal, float scale,
+                   int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* fa_strerror(int status);
 

@@ -168,3 +168,39 @@ def test_varlen_workspace_size():
     # One (sequence, 128-query tile) pair of int32 per possible item, plus a header.
     assert fa.fa_fwd_varlen_workspace_size(4, 1000) >= (1000 // 128 + 4) * 8
     assert fa.fa_varlen_max_seqlen() >= 1 << 19
+
+
+def fwds(**kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, B=2, Hq=8, Hkv=1, Nq=1, Nk=1000, D=128, causal=1,
+             scale=0.1, splits=4, ws=WS, wsb=1 << 24, stream=None)
+    a.update(kw)
+    return fa.fa_fwd_splitkv(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                             a["Nq"], a["Nk"], a["D"], a["causal"], a["scale"], a["splits"],
+                             a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), fa.FA_ERR_INVALID), (dict(Nq=0), fa.FA_ERR_INVALID),
+    (dict(Nk=0), fa.FA_ERR_INVALID), (dict(Nq=20, Nk=10), fa.FA_ERR_INVALID),
+    (dict(splits=-1), fa.FA_ERR_INVALID), (dict(splits=17), fa.FA_ERR_INVALID),
+    (dict(D=80), fa.FA_ERR_UNSUPPORTED), (dict(Hq=6, Hkv=4), fa.FA_ERR_INVALID),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID), (dict(k=K + 8), fa.FA_ERR_ALIGN),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE), (dict(wsb=100), fa.FA_ERR_WORKSPACE),
+    (dict(ws=WS + 64), fa.FA_ERR_ALIGN), (dict(o=K), fa.FA_ERR_INVALID),
+    (dict(ws=O), fa.FA_ERR_INVALID),
+    (dict(Hkv=1 << 8, Hq=1 << 8, Nk=1 << 17), fa.FA_ERR_TOO_LARGE),
+])
+def test_fwd_splitkv_rejects(kw, code):
+    assert fwds(**kw) == code
+
+
+def test_splitkv_sizes():
+    # Non-causal allows more queries than keys; one range needs no workspace.
+    assert fa.fa_fwd_splitkv_workspace_size(1, 8, 1, 20, 10, 64, 1) == 0
+    s = fa.fa_fwd_splitkv_num_splits(1, 32, 1, 1, 32768, 128)
+    assert 1 <= s <= 32768 // 64
+    rows = 1 * 32 * 1
+    assert fa.fa_fwd_splitkv_workspace_size(1, 32, 1, 1, 32768, 128, 8) >= rows * 8 * (128 + 1) * 4
+    assert fa.fa_fwd_splitkv_workspace_size(1, 32, 1, 1, 32768, 128, 0) == \
+        fa.fa_fwd_splitkv_workspace_size(1, 32, 1, 1, 32768, 128, s)
+    assert fa.fa_fwd_splitkv_workspace_size(1, 32, 1, 1, 100, 128, 3) == 0   # ceil(100/64) = 2 ranges max
