@@ -133,6 +133,51 @@ def bench_varlen(fa, torch, dev, stream, reps: int = 20) -> dict:
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
 
 
+def bench_decode(fa, torch, dev, stream, reps: int = 50) -> dict:
+    """Decode-shaped multi-query forward (split-KV + merge): one new query per
+    sequence and head over a long K/V cache; bound by reading K and V."""
+    import synth
+    B, Hq, Hkv, Nq, Nk, D = 16, 32, 1, 1, 32768, 128
+    g = torch.Generator(device="cpu")
+    g.manual_seed(0)
+    q = torch.randn((B, Hq, Nq, D), generator=g).to(torch.bfloat16).to(dev)
+    k = torch.randn((B, Hkv, Nk, D), generator=g).to(torch.bfloat16).to(dev)
+    v = torch.randn((B, Hkv, Nk, D), generator=g).to(torch.bfloat16).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev)
+    splits = fa.fa_fwd_splitkv_num_splits(B, Hq, Hkv, Nq, Nk, D)
+    wsb = fa.fa_fwd_splitkv_workspace_size(B, Hq, Hkv, Nq, Nk, D, splits)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(D)
+    sh = stream.cuda_stream
+
+    def call():
+        rc = fa.fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                               lse.data_ptr(), B, Hq, Hkv, Nq, Nk, D, 1, scale, splits,
+                               ws.data_ptr(), ws.numel(), sh)
+        if rc != 0:
+            raise RuntimeError(f"fa_fwd_splitkv: {fa.fa_strerror(rc)}")
+
+    for _ in range(3):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    # Algorithmic bytes: K and V once, Q and O once, LSE once.
+    nbytes = 2 * B * Hkv * Nk * D * 2 + 2 * B * Hq * Nq * D * 2 + B * Hq * Nq * 4
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"workload": f"B{B} Hq{Hq} Hkv{Hkv} Nq{Nq} Nk{Nk} D{D} causal, {splits} key ranges",
+            "us": round(us, 1), "tflops": round(4.0 * B * Hq * Nq * Nk * D / (us * 1e-6) / 1e12, 2),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "bytes": nbytes}}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -144,7 +189,7 @@ def main() -> int:
                          "workspace), or atomic adds")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the variable-length forward measurement")
+                    help="skip the variable-length and decode measurements")
     ap.add_argument("--cpu-heads", type=int, default=16)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device-to-device copy of MIB MiB (read MIB, write MIB) "
@@ -314,7 +359,8 @@ def main() -> int:
         del ows
     out["bwd"]["workspace_bytes"] = ws_bytes
     if not args.no_extras:
-        out["extras"] = {"varlen_fwd": bench_varlen(fa, torch, dev, stream)}
+        out["extras"] = {"varlen_fwd": bench_varlen(fa, torch, dev, stream),
+                         "decode_splitkv": bench_decode(fa, torch, dev, stream)}
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_heads} heads")
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
