@@ -17,8 +17,9 @@ import os
 __all__ = ["fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_workspace_size", "fa_bwd_preprocess",
            "fa_bwd_main", "fa_bwd_dq", "fa_fwd_varlen", "fa_fwd_varlen_workspace_size",
            "fa_varlen_max_seqlen", "fa_fwd_splitkv", "fa_fwd_splitkv_num_splits",
-           "fa_fwd_splitkv_workspace_size", "fa_strerror", "forward", "backward",
-           "forward_varlen", "forward_splitkv", "FaError", "library_path", "load"]
+           "fa_fwd_splitkv_workspace_size", "fa_bwd_varlen", "fa_bwd_varlen_workspace_size",
+           "fa_strerror", "forward", "backward", "forward_varlen", "backward_varlen",
+           "forward_splitkv", "FaError", "library_path", "load"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libfa.so")
@@ -35,7 +36,8 @@ FA_ERR_TOO_LARGE = -6
 EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_workspace_size", "fa_bwd_preprocess",
             "fa_bwd_main", "fa_bwd_dq", "fa_fwd_varlen", "fa_fwd_varlen_workspace_size",
             "fa_varlen_max_seqlen", "fa_fwd_splitkv", "fa_fwd_splitkv_num_splits",
-            "fa_fwd_splitkv_workspace_size", "fa_strerror")
+            "fa_fwd_splitkv_workspace_size", "fa_bwd_varlen", "fa_bwd_varlen_workspace_size",
+            "fa_strerror")
 
 
 class FaError(RuntimeError):
@@ -87,6 +89,10 @@ def load():
     lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, ci, vp, sz,
                                    vp]
     lib.fa_fwd_splitkv.restype = ci
+    lib.fa_bwd_varlen_workspace_size.argtypes = [ci] * 6
+    lib.fa_bwd_varlen_workspace_size.restype = sz
+    lib.fa_bwd_varlen.argtypes = [vp] * 10 + [ci] * 7 + [cf, vp, sz, ci, vp]
+    lib.fa_bwd_varlen.restype = ci
     lib.fa_strerror.argtypes = [ci]
     lib.fa_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -158,6 +164,17 @@ def fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, D, causal, scale, num_sp
     return load().fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, D, int(causal),
                                  float(scale), int(num_splits), workspace, workspace_bytes,
                                  stream)
+
+
+def fa_bwd_varlen_workspace_size(B, Hq, Hkv, total, D, deterministic) -> int:
+    return int(load().fa_bwd_varlen_workspace_size(B, Hq, Hkv, total, D, int(deterministic)))
+
+
+def fa_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens, B, Hq, Hkv, total, max_seqlen, D,
+                  causal, scale, workspace, workspace_bytes, deterministic, stream) -> int:
+    return load().fa_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens, B, Hq, Hkv, total,
+                                max_seqlen, D, int(causal), float(scale), workspace,
+                                workspace_bytes, int(deterministic), stream)
 
 
 def fa_strerror(status: int) -> str:
@@ -317,3 +334,35 @@ def forward_splitkv(q, k, v, causal: bool, scale: float, *, num_splits: int = 0,
     if rc != FA_OK:
         raise FaError(rc, "fa_fwd_splitkv")
     return out, lse
+
+
+def backward_varlen(q, k, v, o, lse, dout, cu_seqlens, max_seqlen: int, causal: bool,
+                    scale: float, *, deterministic: int = 0, workspace=None):
+    """dQ, dK, dV (bf16) of forward_varlen; deterministic is 0 (atomic) or 2
+    (fixed order, recomputing dS)."""
+    import torch
+    Hq, total, D = q.shape
+    Hkv = k.shape[0]
+    for name, t, shp in (("q", q, (Hq, total, D)), ("k", k, (Hkv, total, D)),
+                         ("v", v, (Hkv, total, D)), ("o", o, (Hq, total, D)),
+                         ("dout", dout, (Hq, total, D))):
+        _check(name, t, torch.bfloat16, shp)
+    _check("lse", lse, torch.float32, (Hq, total))
+    B = cu_seqlens.numel() - 1
+    _check("cu_seqlens", cu_seqlens, torch.int32, (B + 1,))
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if total == 0:
+        return dq, dk, dv
+    ws_bytes = fa_bwd_varlen_workspace_size(B, Hq, Hkv, total, D, deterministic)
+    if ws_bytes == 0:
+        raise FaError(FA_ERR_INVALID, "fa_bwd_varlen_workspace_size")
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    rc = fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                       dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                       cu_seqlens.data_ptr(), B, Hq, Hkv, total, int(max_seqlen), D, causal, scale,
+                       workspace.data_ptr(), workspace.numel(), deterministic,
+                       _stream_handle(q.device))
+    if rc != FA_OK:
+        raise FaError(rc, "fa_bwd_varlen")
+    return dq, dk, dv

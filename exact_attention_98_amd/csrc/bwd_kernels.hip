@@ -54,6 +54,20 @@ struct BwdParams {
   char* ds;        // dS^T blocks (stored-dS mode), ds_head bytes per (b, hq)
   uint32_t ds_head;
   int nb32;        // 32-row blocks per head, ceil(N / 32)
+  // Variable length: cumulative sequence starts, the token count, and the
+  // work list of this kernel (2 ints per item) with its length.
+  const int* cu;
+  int total;
+  const int* items;
+  const int* n_items;
+};
+
+// Geometry of one workgroup's sequence: its length, where its rows start in
+// one head's matrix, and the distance between two heads (in rows).
+struct SeqGeom {
+  int N;
+  size_t row0;   // first row of this sequence within a head
+  size_t hstride;  // rows per head: N (dense) or total (variable length)
 };
 
 // dQ modes (the deterministic argument of the C ABI).
@@ -111,7 +125,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
 // tile.  Query steps of QS = 4096 / D queries (32 for D = 128, 64 for D = 64)
 // are walked from the last one down to the first that meets the tile's
 // diagonal, for each of the G query heads.
-template <int D, bool CAUSAL, int DQM>
+template <int D, bool CAUSAL, int DQM, bool VARLEN>
 __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
@@ -149,9 +163,33 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
 
   const int Hkv = p.Hq / p.G;
   const int wg = blockIdx.x;
-  const int bhk = wg % (p.B * Hkv);
-  const int kb = wg / (p.B * Hkv);
-  const int b = bhk / Hkv, hk = bhk % Hkv;
+  int b, hk, kb;
+  SeqGeom sg;
+  if constexpr (VARLEN) {
+    // Work list of (sequence, 128-key block), largest first; heads fastest.
+    const int item = wg / Hkv;
+    hk = wg % Hkv;
+    if (item >= *p.n_items) return;
+    b = p.items[2 * item];
+    kb = p.items[2 * item + 1];
+    const int s0 = min(max(p.cu[b], 0), p.total);
+    sg.N = min(max(p.cu[b + 1] - s0, 0), p.total - s0);
+    sg.row0 = (size_t)s0;
+    sg.hstride = (size_t)p.total;
+  } else {
+    const int bhk = wg % (p.B * Hkv);
+    kb = wg / (p.B * Hkv);
+    b = bhk / Hkv;
+    hk = bhk % Hkv;
+    sg.N = p.N;
+    sg.row0 = 0;
+    sg.hstride = (size_t)p.N;
+  }
+  // Head h of batch b starts at row (b H + h) hstride + row0 (dense: b is the
+  // batch; variable length: b = 0 in the head index, the sequence is row0).
+  const int bq = VARLEN ? 0 : b;
+  const int N = sg.N;
+  const int nqs = (N + QS - 1) / QS;
   const int k0 = kb * BN;
 
   const int lane = threadIdx.x & 63;
@@ -160,9 +198,8 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
   const int kw = k0 + 32 * wave;     // this wave's first key (uniform)
   const int key = kw + n;            // key this lane carries as MFMA column
 
-  const size_t head_elems = (size_t)p.N * D;
-  const uint32_t head_bytes = (uint32_t)(head_elems * 2);
-  const size_t kv_head = ((size_t)b * Hkv + hk) * head_elems;
+  const uint32_t head_bytes = (uint32_t)((size_t)N * D * 2);   // one head's rows of this sequence
+  const size_t kv_head = (((size_t)bq * Hkv + hk) * sg.hstride + sg.row0) * D;
   const rsrc_t kr = make_rsrc_uniform(K + kv_head, head_bytes);
   const rsrc_t vr = make_rsrc_uniform(V + kv_head, head_bytes);
 
@@ -188,8 +225,8 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r0 = k0 + 16 * t + 8 * (j >> 1) + 4 * h + 2 * (j & 1);
-        const uint32_t lo = (r0 < p.N) ? Kh[(size_t)r0 * D + d] : 0u;
-        const uint32_t hi = (r0 + 1 < p.N) ? Kh[(size_t)(r0 + 1) * D + d] : 0u;
+        const uint32_t lo = (r0 < N) ? Kh[(size_t)r0 * D + d] : 0u;
+        const uint32_t hi = (r0 + 1 < N) ? Kh[(size_t)(r0 + 1) * D + d] : 0u;
         w[j] = lo | (hi << 16);
       }
       kT[t] = as_bf16x8(w);
@@ -255,17 +292,20 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
   // query heads.  Two cursors follow it with scalar increments only: the next
   // step to copy in and the step being finished.
   const int qs_first = CAUSAL ? (k0 / QS) : 0;
-  const int per_head = max(p.nqs - qs_first, 0);
+  const int per_head = max(nqs - qs_first, 0);
   const int nsteps = p.G * per_head;
   const int hq0 = hk * p.G;
-  const uint32_t lse_head_bytes = (uint32_t)p.N * 4u;
+  const uint32_t lse_head_bytes = (uint32_t)N * 4u;       // range of one head's row constants
+  const size_t q_hstride = sg.hstride * D * 2;             // bytes between two query heads
+  const size_t l_hstride = sg.hstride * 4;
+  const size_t qrow0 = ((size_t)bq * p.Hq + hq0) * sg.hstride + sg.row0;  // row of head hq0
 
   // Copy cursor: query step and the per-head base addresses of Q, dO, LSE, Delta.
-  int iss_qs = p.nqs - 1;
-  const char* iss_q = (const char*)(Q + ((size_t)b * p.Hq + hq0) * head_elems);
-  const char* iss_do = (const char*)(dO + ((size_t)b * p.Hq + hq0) * head_elems);
-  const char* iss_l = (const char*)(p.lse2 + ((size_t)b * p.Hq + hq0) * p.N);
-  const char* iss_d = (const char*)(p.delta + ((size_t)b * p.Hq + hq0) * p.N);
+  int iss_qs = nqs - 1;
+  const char* iss_q = (const char*)(Q + qrow0 * D);
+  const char* iss_do = (const char*)(dO + qrow0 * D);
+  const char* iss_l = (const char*)(p.lse2 + qrow0);
+  const char* iss_d = (const char*)(p.delta + qrow0);
   auto issue_next = [&](char* st) {
     const uint32_t base = (uint32_t)iss_qs * (uint32_t)TB;
     const uint32_t left = head_bytes - base;  // qs < nqs, so base < head_bytes
@@ -281,21 +321,21 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
     if (wave == 0) lds_dma4(make_rsrc_uniform(iss_l + rbase, rleft), (lds_void*)(st + 2 * TB), lane * 4);
     if (wave == 1) lds_dma4(make_rsrc_uniform(iss_d + rbase, rleft), (lds_void*)(st + 2 * TB + 256), lane * 4);
     if (--iss_qs < qs_first) {
-      iss_qs = p.nqs - 1;
-      iss_q += head_bytes;
-      iss_do += head_bytes;
-      iss_l += lse_head_bytes;
-      iss_d += lse_head_bytes;
+      iss_qs = nqs - 1;
+      iss_q += q_hstride;
+      iss_do += q_hstride;
+      iss_l += l_hstride;
+      iss_d += l_hstride;
     }
   };
   // Cursor of the step being finished (query step and head offset g).
-  int cur_qs = p.nqs - 1, cur_g = 0;
+  int cur_qs = nqs - 1, cur_g = 0;
   int prev_qs = 0, prev_g = 0;  // the step before it (atomic dQ)
   auto advance_cur = [&]() {
     prev_qs = cur_qs;
     prev_g = cur_g;
     if (--cur_qs < qs_first) {
-      cur_qs = p.nqs - 1;
+      cur_qs = nqs - 1;
       ++cur_g;
     }
   };
@@ -323,11 +363,11 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
       acc = mfma32(as_bf16x8(a), kT[t], acc);
     }
     // acc register r: query q0 + 32 dq_qb + 8(r/4) + 4h + r%4, d = 32 dq_db + n.
-    const size_t qh = ((size_t)b * p.Hq + hq) * p.N;
+    const size_t qh = ((size_t)bq * p.Hq + hq) * sg.hstride + sg.row0;
     float* dqh = p.dq_acc + qh * D;
     const int qrow0 = q0 + 32 * dq_qb + 4 * h;
     const int d = 32 * dq_db + n;
-    const rsrc_t dqr = make_rsrc_uniform(dqh, (uint32_t)(head_elems * 4));
+    const rsrc_t dqr = make_rsrc_uniform(dqh, (uint32_t)((size_t)N * D * 4));
 #pragma unroll
     for (int r = 0; r < 16; ++r)
       buf_atomic_add(dqr, (uint32_t)(((qrow0 + 8 * (r >> 2) + (r & 3)) * D + d) * 4), acc[r]);
@@ -408,9 +448,9 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
     // Register r of block qb holds query q0 + 32qb + 8(r/4) + 4h + r%4.
     // Padding keys (key >= N, rows read as zero) are masked too: their score 0
     // can exceed every real score and overflow P.
-    if ((CAUSAL && (q0 < kw + 31)) || (kw + 32 > p.N)) {
+    if ((CAUSAL && (q0 < kw + 31)) || (kw + 32 > N)) {
       keep_branch();
-      const int lim = (key >= p.N) ? 1 << 30 : (CAUSAL ? key - q0 - 4 * h : -1);
+      const int lim = (key >= N) ? 1 << 30 : (CAUSAL ? key - q0 - 4 * h : -1);
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
@@ -608,7 +648,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int krow = kw + 8 * (r >> 2) + 4 * h + (r & 3);
-      if (krow < p.N) {
+      if (krow < N) {
         const size_t off = (size_t)krow * D + 32 * db + n;
         dKh[off] = (uint16_t)(pack_bf16x2(dk_acc[db][r] * p.scale, 0.f) & 0xffffu);
         dVh[off] = (uint16_t)(pack_bf16x2(dv_acc[db][r], 0.f) & 0xffffu);
@@ -625,7 +665,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
 //   dQ^T += K^T dS^T                  (K^T by transposing reads of the K tile,
 //                                      dS^T straight from the accumulators)
 // and dQ = scale * dQ^T is written once, so the sum order is fixed.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t* __restrict__ Q,
                                                         const uint16_t* __restrict__ K,
                                                         const uint16_t* __restrict__ V,
@@ -642,16 +682,34 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t* __restri
   __shared__ __attribute__((aligned(1024))) char kv0[2 * TB];
   __shared__ __attribute__((aligned(1024))) char kv1[2 * TB];
 
-  const int BH = p.B * p.Hq;
+  // Work item: (batch or sequence, query head, 128-query tile); variable
+  // length takes (sequence, tile) pairs from a list sorted largest first.
   const int wg = blockIdx.x;
-  const int bh = wg % BH;
-  const int qb = nqb - 1 - wg / BH;
-  const int b = bh / p.Hq, hq = bh % p.Hq;
-  const int hk = hq / p.G;
-  const size_t head_elems = (size_t)p.N * D;
-  const uint32_t head_bytes = (uint32_t)(head_elems * 2);
-  const uint16_t* Kh = K + ((size_t)b * (p.Hq / p.G) + hk) * head_elems;
-  const uint16_t* Vh = V + ((size_t)b * (p.Hq / p.G) + hk) * head_elems;
+  int qb, hq, N;
+  size_t qrow, kvrow;   // first row of this (sequence, head) in Q/dO/dQ and in K/V
+  if constexpr (VARLEN) {
+    const int item = wg / p.Hq;
+    hq = wg % p.Hq;
+    if (item >= *p.n_items) return;
+    const int b = p.items[2 * item];
+    qb = p.items[2 * item + 1];
+    const int s0 = min(max(p.cu[b], 0), p.total);
+    N = min(max(p.cu[b + 1] - s0, 0), p.total - s0);
+    qrow = (size_t)hq * p.total + s0;
+    kvrow = (size_t)(hq / p.G) * p.total + s0;
+  } else {
+    const int BH = p.B * p.Hq;
+    const int bh = wg % BH;
+    qb = nqb - 1 - wg / BH;
+    const int b = bh / p.Hq;
+    hq = bh % p.Hq;
+    N = p.N;
+    qrow = (size_t)bh * N;
+    kvrow = ((size_t)b * (p.Hq / p.G) + hq / p.G) * N;
+  }
+  const uint32_t head_bytes = (uint32_t)((size_t)N * D * 2);
+  const uint16_t* Kh = K + kvrow * D;
+  const uint16_t* Vh = V + kvrow * D;
 
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
@@ -661,8 +719,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t* __restri
   const int qi = qw + n;
 
   // Q and dO fragments (B operands; k-step t: d = 16t + 8h .. +8 of query qi).
-  const rsrc_t qr = make_rsrc_uniform(Q + (size_t)bh * head_elems, head_bytes);
-  const rsrc_t dr = make_rsrc_uniform(dO + (size_t)bh * head_elems, head_bytes);
+  const rsrc_t qr = make_rsrc_uniform(Q + qrow * D, head_bytes);
+  const rsrc_t dr = make_rsrc_uniform(dO + qrow * D, head_bytes);
   bf16x8 qf[D / 16], df[D / 16];
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) {
@@ -671,8 +729,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t* __restri
   }
   // Row constants of this lane's query (rows past N read as 0; their results
   // are dropped at the store).
-  const rsrc_t lr = make_rsrc_uniform(p.lse2 + (size_t)bh * p.N, (uint32_t)p.N * 4u);
-  const rsrc_t er = make_rsrc_uniform(p.delta + (size_t)bh * p.N, (uint32_t)p.N * 4u);
+  const rsrc_t lr = make_rsrc_uniform(p.lse2 + qrow, (uint32_t)N * 4u);
+  const rsrc_t er = make_rsrc_uniform(p.delta + qrow, (uint32_t)N * 4u);
   const float lse2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lr, (uint32_t)qi * 4u, 0, 0));
   const float dlt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(er, (uint32_t)qi * 4u, 0, 0));
 
@@ -682,7 +740,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t* __restri
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
 
-  const int kend = CAUSAL ? min(p.N, q0 + BM) : p.N;
+  const int kend = CAUSAL ? min(N, q0 + BM) : N;
   const int ntiles = (kend + BN - 1) / BN;
 
   uint32_t ld_off[NLD];
@@ -750,8 +808,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t* __restri
     // Register r of half sb holds key k0 + 32 sb + 8 (r/4) + 4 h + r % 4.
     // Causal mask, and padding keys (key >= N, rows read as zero, whose score
     // 0 can exceed every real score).
-    const bool need_mask = (CAUSAL && (k0 + BN - 1 > qw)) || (k0 + BN > p.N);
-    const int lim = CAUSAL ? min(qi, p.N - 1) - k0 - 4 * h : p.N - 1 - k0 - 4 * h;
+    const bool need_mask = (CAUSAL && (k0 + BN - 1 > qw)) || (k0 + BN > N);
+    const int lim = CAUSAL ? min(qi, N - 1) - k0 - 4 * h : N - 1 - k0 - 4 * h;
     bf16x8 dsb[2][2];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
@@ -791,7 +849,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t* __restri
   }
 
   // dQ = scale * dQ^T; register r of block db is d = 32 db + 8 (r/4) + 4 h + r % 4.
-  const rsrc_t out = make_rsrc_uniform(dQ + (size_t)bh * head_elems, head_bytes);
+  const rsrc_t out = make_rsrc_uniform(dQ + qrow * D, head_bytes);
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -959,10 +1017,10 @@ __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(const float* __rest
   ((u32x4*)dq)[i] = w;
 }
 
-template <int D, bool CAUSAL, int DQM>
-hipError_t launch_bwd_t(const BwdArgs& a, const BwdParams& p, hipStream_t s) {
-  const dim3 grid((unsigned)(a.B * a.Hkv * p.nkb));
-  hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL, DQM>), grid, dim3(64 * kBwdWaves), 0, s,
+template <int D, bool CAUSAL, int DQM, bool VARLEN = false>
+hipError_t launch_bwd_t(const BwdArgs& a, const BwdParams& p, hipStream_t s, unsigned items = 0) {
+  const dim3 grid(VARLEN ? items * (unsigned)a.Hkv : (unsigned)(a.B * a.Hkv * p.nkb));
+  hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL, DQM, VARLEN>), grid, dim3(64 * kBwdWaves), 0, s,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, (uint16_t*)a.dk, (uint16_t*)a.dv, p);
   return hipGetLastError();
@@ -987,6 +1045,10 @@ BwdParams make_params(const BwdArgs& a) {
   p.nb32 = (a.N + 31) / 32;
   p.ds_head = (uint32_t)ds_head_bytes(a.N);
   p.ds = a.deterministic == kDqStored ? ws + lay.ds : nullptr;
+  p.cu = nullptr;
+  p.total = 0;
+  p.items = nullptr;
+  p.n_items = nullptr;
   return p;
 }
 
@@ -1035,17 +1097,71 @@ hipError_t launch_dq_d(const BwdArgs& a, hipStream_t s) {
   const int nqb = (a.N + 127) / 128;
   const dim3 grid((unsigned)(a.B * a.Hq * nqb));
   if (a.causal)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, true>), grid, dim3(256), 0, s, (const uint16_t*)a.q,
+    hipLaunchKernelGGL((bwd_dq_kernel<D, true, false>), grid, dim3(256), 0, s, (const uint16_t*)a.q,
                        (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
                        (uint16_t*)a.dq, p, nqb);
   else
-    hipLaunchKernelGGL((bwd_dq_kernel<D, false>), grid, dim3(256), 0, s, (const uint16_t*)a.q,
+    hipLaunchKernelGGL((bwd_dq_kernel<D, false, false>), grid, dim3(256), 0, s, (const uint16_t*)a.q,
                        (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
                        (uint16_t*)a.dq, p, nqb);
   return hipGetLastError();
 }
 
+// Variable-length backward (dQ modes 0 and 2).  The BwdArgs describe the
+// packed tensors as one batch of total rows (a.B = 1, a.N = total), so the
+// preprocess and the atomic-mode convert run over every row unchanged.
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_varlen_t(const BwdArgs& a, const VarlenArgs& v, hipStream_t s) {
+  const BwdLayout lay = bwd_layout(1, a.Hq, v.total, D, a.deterministic);
+  char* lists = (char*)a.workspace + lay.total;
+  const size_t lbytes = varlen_workspace_bytes(v.B, v.total);
+  int* main_n = (int*)lists;
+  int* main_items = (int*)(lists + 256);
+  int* dq_n = (int*)(lists + lbytes);
+  int* dq_items = (int*)(lists + lbytes + 256);
+  const unsigned items_max = (unsigned)(v.total / 128 + v.B);
+  constexpr int QS = 4096 / D;
+  hipError_t e = launch_varlen_schedule(v, CAUSAL, 1, QS, main_n, main_items, s);
+  if (e != hipSuccess) return e;
+  if (a.deterministic == kDqRecompute) {
+    e = launch_varlen_schedule(v, CAUSAL, 0, QS, dq_n, dq_items, s);
+    if (e != hipSuccess) return e;
+  }
+  e = launch_pre_d<D>(a, s);
+  if (e != hipSuccess) return e;
+  BwdParams p = make_params(a);
+  p.cu = v.cu;
+  p.total = v.total;
+  p.items = main_items;
+  p.n_items = main_n;
+  e = a.deterministic == kDqAtomic ? launch_bwd_t<D, CAUSAL, kDqAtomic, true>(a, p, s, items_max)
+                                   : launch_bwd_t<D, CAUSAL, kDqRecompute, true>(a, p, s, items_max);
+  if (e != hipSuccess) return e;
+  if (a.deterministic == kDqAtomic) {
+    const size_t n8 = (size_t)a.Hq * v.total * D / 8;
+    hipLaunchKernelGGL(bwd_dq_convert_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s,
+                       (const float*)p.dq_acc, (uint16_t*)a.dq, n8, a.scale);
+    return hipGetLastError();
+  }
+  p.items = dq_items;
+  p.n_items = dq_n;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, true>), dim3(items_max * (unsigned)a.Hq), dim3(256), 0,
+                     s, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     (const uint16_t*)a.dout, (uint16_t*)a.dq, p, 0);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+size_t bwd_varlen_workspace_bytes(int B, int Hq, int total, int D, int deterministic) {
+  return bwd_layout(1, Hq, total, D, deterministic).total + 2 * varlen_workspace_bytes(B, total);
+}
+
+hipError_t launch_bwd_varlen(const BwdArgs& a, const VarlenArgs& v, hipStream_t s) {
+  if (a.D == 64)
+    return a.causal ? launch_bwd_varlen_t<64, true>(a, v, s) : launch_bwd_varlen_t<64, false>(a, v, s);
+  return a.causal ? launch_bwd_varlen_t<128, true>(a, v, s) : launch_bwd_varlen_t<128, false>(a, v, s);
+}
 
 size_t ds_head_bytes(int N) {
   const size_t nb = ((size_t)N + 31) / 32;

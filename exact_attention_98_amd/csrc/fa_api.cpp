@@ -143,6 +143,52 @@ int resolve_splits(int B, int Hq, int Hkv, int Nq, int Nk, int num_splits) {
 
 extern "C" {
 
+size_t fa_bwd_varlen_workspace_size(int B, int Hq, int Hkv, int total, int D,
+                                    int deterministic) {
+  if (B < 1 || total < 0) return 0;
+  if (check_shape(1, Hq, Hkv, total > 0 ? total : 1, D, 1.0f) != FA_OK) return 0;
+  if (deterministic != 0 && deterministic != 2) return 0;
+  return fa::bwd_varlen_workspace_bytes(B, Hq, total, D, deterministic);
+}
+
+int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                  const void* dout, void* dq, void* dk, void* dv, const int* cu_seqlens,
+                  int B, int Hq, int Hkv, int total, int max_seqlen, int D, int causal,
+                  float scale, void* workspace, size_t workspace_bytes, int deterministic,
+                  void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !cu_seqlens || !workspace)
+    return FA_ERR_INVALID;
+  if (B < 1 || total < 0 || max_seqlen < 1 || max_seqlen > fa::varlen_max_seqlen_limit() / 2)
+    return FA_ERR_INVALID;
+  int rc = check_shape(1, Hq, Hkv, total > 0 ? total : 1, D, scale);
+  if (rc != FA_OK) return rc;
+  if (deterministic == 1) return FA_ERR_UNSUPPORTED;
+  if (deterministic != 0 && deterministic != 2) return FA_ERR_INVALID;
+  const void* all[11] = {q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens, workspace};
+  for (int i = 0; i < 10; ++i)
+    if (!aligned16(all[i])) return FA_ERR_ALIGN;
+  if (((uintptr_t)workspace & 255u) != 0) return FA_ERR_ALIGN;
+  const size_t wbytes = fa::bwd_varlen_workspace_bytes(B, Hq, total, D, deterministic);
+  if (workspace_bytes < wbytes) return FA_ERR_WORKSPACE;
+  const size_t qb = (size_t)Hq * total * D * 2, kb = (size_t)Hkv * total * D * 2;
+  const size_t lb = (size_t)Hq * total * 4, cb = (size_t)(B + 1) * 4;
+  const void* ins[7] = {q, k, v, o, lse, dout, cu_seqlens};
+  const size_t isz[7] = {qb, kb, kb, qb, lb, qb, cb};
+  const void* outs[4] = {dq, dk, dv, workspace};
+  const size_t osz[4] = {qb, kb, kb, wbytes};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 7; ++j)
+      if (overlaps(outs[i], osz[i], ins[j], isz[j])) return FA_ERR_INVALID;
+    for (int j = 0; j < 4; ++j)
+      if (j != i && overlaps(outs[i], osz[i], outs[j], osz[j])) return FA_ERR_INVALID;
+  }
+  if (total == 0) return FA_OK;
+  const fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, 1, Hq, Hkv, total, D, causal ? 1 : 0,
+                      scale, deterministic, workspace};
+  const fa::VarlenArgs va{cu_seqlens, B, total, max_seqlen, workspace};
+  return fa::launch_bwd_varlen(a, va, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 int fa_fwd_splitkv_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int D) {
   if (check_split(B, Hq, Hkv, Nq, Nk, D, 0, 1.0f) != FA_OK) return 0;
   return fa::split_auto(B, Hq, Hkv, Nq, Nk);

@@ -451,10 +451,14 @@ hipError_t launch_fwd_c(const FwdArgs& a, hipStream_t s) {
 constexpr int kSchedThreads = 1024;
 constexpr int kSchedMaxCost = 16384 - kSchedThreads - 1;  // histogram + chunk sums <= 64 KiB
 
-template <bool CAUSAL>
+// KIND 0 lists (sequence, 128-query tile) items costed by the 64-key tiles
+// they walk (forward, fixed-order dQ pass); KIND 1 lists (sequence, 128-key
+// block) items costed by the query steps of qstep queries they walk (main
+// backward kernel).
+template <bool CAUSAL, int KIND>
 __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(const int* __restrict__ cu,
                                                                       int B, int total,
-                                                                      int max_cost,
+                                                                      int max_cost, int qstep,
                                                                       int* __restrict__ n_items,
                                                                       int* __restrict__ items) {
   extern __shared__ int sm[];
@@ -469,8 +473,14 @@ __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(const in
     return min(max(cu[b + 1] - s0, 0), total - s0);
   };
   auto cost = [&](int len, int qb) {
-    const int kend = CAUSAL ? min(len, (qb + 1) * kFwdBM) : len;
-    return min((kend + kFwdBN - 1) / kFwdBN, max_cost);
+    if constexpr (KIND == 0) {
+      const int kend = CAUSAL ? min(len, (qb + 1) * kFwdBM) : len;
+      return min((kend + kFwdBN - 1) / kFwdBN, max_cost);
+    } else {
+      const int nsteps = (len + qstep - 1) / qstep;
+      const int first = CAUSAL ? (qb * kFwdBM) / qstep : 0;
+      return min(max(nsteps - first, 0), max_cost);
+    }
   };
   for (int b = tid; b < B; b += kSchedThreads) {
     const int len = seq_len(b);
@@ -517,8 +527,8 @@ hipError_t launch_fwd_varlen_t(const FwdArgs& a, const VarlenArgs& v, hipStream_
   int* items = (int*)(ws + 256);
   const int max_cost = (v.max_seqlen + kFwdBN - 1) / kFwdBN;
   const size_t shm = (size_t)(max_cost + 1 + kSchedThreads) * sizeof(int);
-  hipLaunchKernelGGL((varlen_schedule_kernel<CAUSAL>), dim3(1), dim3(kSchedThreads), shm, s, v.cu,
-                     v.B, v.total, max_cost, n_items, items);
+  hipLaunchKernelGGL((varlen_schedule_kernel<CAUSAL, 0>), dim3(1), dim3(kSchedThreads), shm, s,
+                     v.cu, v.B, v.total, max_cost, 0, n_items, items);
   FwdParams p;
   p.BH = 0;
   p.Hq = a.Hq;
@@ -641,6 +651,31 @@ hipError_t launch_fwd_split(const FwdArgs& a, const SplitArgs& sa, hipStream_t s
   if (a.D == 64)
     return a.causal ? launch_fwd_split_t<64, true>(a, sa, s) : launch_fwd_split_t<64, false>(a, sa, s);
   return a.causal ? launch_fwd_split_t<128, true>(a, sa, s) : launch_fwd_split_t<128, false>(a, sa, s);
+}
+
+hipError_t launch_varlen_schedule(const VarlenArgs& v, int causal, int kind, int qstep,
+                                  int* n_items, int* items, hipStream_t s) {
+  // Largest cost: 64-key tiles of the longest sequence (kind 0) or its query
+  // steps (kind 1, qstep >= 32 so never more than twice the tiles).
+  const int max_cost = kind == 0 ? (v.max_seqlen + kFwdBN - 1) / kFwdBN
+                                 : (v.max_seqlen + qstep - 1) / qstep;
+  const size_t shm = (size_t)(max_cost + 1 + kSchedThreads) * sizeof(int);
+  if (kind == 0) {
+    if (causal)
+      hipLaunchKernelGGL((varlen_schedule_kernel<true, 0>), dim3(1), dim3(kSchedThreads), shm, s,
+                         v.cu, v.B, v.total, max_cost, qstep, n_items, items);
+    else
+      hipLaunchKernelGGL((varlen_schedule_kernel<false, 0>), dim3(1), dim3(kSchedThreads), shm, s,
+                         v.cu, v.B, v.total, max_cost, qstep, n_items, items);
+  } else {
+    if (causal)
+      hipLaunchKernelGGL((varlen_schedule_kernel<true, 1>), dim3(1), dim3(kSchedThreads), shm, s,
+                         v.cu, v.B, v.total, max_cost, qstep, n_items, items);
+    else
+      hipLaunchKernelGGL((varlen_schedule_kernel<false, 1>), dim3(1), dim3(kSchedThreads), shm, s,
+                         v.cu, v.B, v.total, max_cost, qstep, n_items, items);
+  }
+  return hipGetLastError();
 }
 
 size_t varlen_workspace_bytes(int B, int total) {

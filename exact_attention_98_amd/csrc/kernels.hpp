@@ -55,6 +55,12 @@ size_t varlen_workspace_bytes(int B, int total);
 // Largest max_seqlen the work-list builder supports (its histogram lives in LDS).
 int varlen_max_seqlen_limit();
 hipError_t launch_fwd_varlen(const FwdArgs& a, const VarlenArgs& v, hipStream_t stream);
+// Work list of a variable-length batch into n_items / items (2 ints per item,
+// room for varlen_workspace_bytes(B, total) - 256 bytes): kind 0 = (sequence,
+// 128-query tile) by 64-key tiles walked; kind 1 = (sequence, 128-key block) by
+// query steps of qstep walked; largest first.
+hipError_t launch_varlen_schedule(const VarlenArgs& v, int causal, int kind, int qstep,
+                                  int* n_items, int* items, hipStream_t stream);
 
 // Split-KV forward for decode-shaped problems: q, o [B][Hq][Nq][D], k, v
 // [B][Hkv][Nk][D], lse [B][Hq][Nq]; causal rows are aligned to the end of the
@@ -106,5 +112,11 @@ hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t stream);
 // accumulated dQ); 1 stored dS, the fixed-order dS K pass; 2 recompute, the
 // fixed-order pass that recomputes S, dP and dS.
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
+
+// Variable-length backward, dQ modes 0 (atomic) and 2 (recompute): a holds
+// the packed tensors as B = 1, N = total; v the sequences.  Workspace layout:
+// the dense layout for (1, Hq, total), then two work lists.
+size_t bwd_varlen_workspace_bytes(int B, int Hq, int total, int D, int deterministic);
+hipError_t launch_bwd_varlen(const BwdArgs& a, const VarlenArgs& v, hipStream_t stream);
 
 }  // namespace fa

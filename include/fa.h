@@ -176,6 +176,28 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
                   void* stream);
 
 /*
+ * Variable-length backward: the gradients of fa_fwd_varlen, same packing:
+ *   q, o, dout, dq [Hq][total][D], k, v, dk, dv [Hkv][total][D], lse
+ *   [Hq][total]; cu_seqlens, B, total, max_seqlen as for fa_fwd_varlen, with
+ *   max_seqlen <= fa_varlen_max_seqlen() / 2.
+ *   deterministic: 0 (atomic dQ) or 2 (fixed-order dQ recomputing dS); the
+ *     stored-dS mode 1 is not available for variable length
+ *     (FA_ERR_UNSUPPORTED).
+ *   workspace: fa_bwd_varlen_workspace_size() bytes, 256-byte aligned.
+ * Work lists are built on the device as for the forward: the dK/dV pass takes
+ * (sequence, 128-key block) items by decreasing number of query steps, the
+ * dQ pass (sequence, 128-query tile) items by decreasing number of key tiles.
+ * total = 0 is valid and writes nothing.
+ */
+size_t fa_bwd_varlen_workspace_size(int B, int Hq, int Hkv, int total, int D,
+                                    int deterministic);
+int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                  const void* dout, void* dq, void* dk, void* dv, const int* cu_seqlens,
+                  int B, int Hq, int Hkv, int total, int max_seqlen, int D, int causal,
+                  float scale, void* workspace, size_t workspace_bytes, int deterministic,
+                  void* stream);
+
+/*
  * Decode-shaped forward with the keys split across workgroups (split-KV).
  * For few queries over long keys, typically G = Hq / Hkv query heads
  * sharing one K/V head (multi-query / grouped attention, hotdry article,

@@ -204,3 +204,35 @@ def test_splitkv_sizes():
     assert fa.fa_fwd_splitkv_workspace_size(1, 32, 1, 1, 32768, 128, 0) == \
         fa.fa_fwd_splitkv_workspace_size(1, 32, 1, 1, 32768, 128, s)
     assert fa.fa_fwd_splitkv_workspace_size(1, 32, 1, 1, 100, 128, 3) == 0   # ceil(100/64) = 2 ranges max
+
+
+def bwdv(**kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, dout=DO, dq=DQ, dk=DK, dv=DV, cu=(11 << 36), B=3, Hq=2,
+             Hkv=1, total=500, max_seqlen=300, D=128, causal=1, scale=0.1, ws=WS, wsb=1 << 24,
+             det=2, stream=None)
+    a.update(kw)
+    return fa.fa_bwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dout"], a["dq"], a["dk"],
+                            a["dv"], a["cu"], a["B"], a["Hq"], a["Hkv"], a["total"],
+                            a["max_seqlen"], a["D"], a["causal"], a["scale"], a["ws"], a["wsb"],
+                            a["det"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dout=None), fa.FA_ERR_INVALID), (dict(cu=None), fa.FA_ERR_INVALID),
+    (dict(det=1), fa.FA_ERR_UNSUPPORTED), (dict(det=3), fa.FA_ERR_INVALID),
+    (dict(B=0), fa.FA_ERR_INVALID), (dict(max_seqlen=1 << 30), fa.FA_ERR_INVALID),
+    (dict(D=32), fa.FA_ERR_UNSUPPORTED), (dict(dq=DQ + 4), fa.FA_ERR_ALIGN),
+    (dict(wsb=64), fa.FA_ERR_WORKSPACE), (dict(dk=DQ), fa.FA_ERR_INVALID),
+    (dict(dv=K), fa.FA_ERR_INVALID), (dict(ws=L), fa.FA_ERR_INVALID),
+])
+def test_bwd_varlen_rejects(kw, code):
+    assert bwdv(**kw) == code
+
+
+def test_bwd_varlen_sizes_and_empty_batch():
+    assert bwdv(total=0, max_seqlen=1) == fa.FA_OK
+    assert bwdv(total=0, max_seqlen=1, det=0) == fa.FA_OK
+    assert fa.fa_bwd_varlen_workspace_size(3, 2, 1, 500, 128, 1) == 0
+    s0 = fa.fa_bwd_varlen_workspace_size(3, 2, 1, 500, 128, 0)
+    s2 = fa.fa_bwd_varlen_workspace_size(3, 2, 1, 500, 128, 2)
+    assert s0 >= 2 * 500 * 128 * 4 and s2 < s0
