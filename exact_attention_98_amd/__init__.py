@@ -18,8 +18,9 @@ __all__ = ["fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_workspace_size", "fa_bwd_pre
            "fa_bwd_main", "fa_bwd_dq", "fa_fwd_varlen", "fa_fwd_varlen_workspace_size",
            "fa_varlen_max_seqlen", "fa_fwd_splitkv", "fa_fwd_splitkv_num_splits",
            "fa_fwd_splitkv_workspace_size", "fa_bwd_varlen", "fa_bwd_varlen_workspace_size",
-           "fa_strerror", "forward", "backward", "forward_varlen", "backward_varlen",
-           "forward_splitkv", "FaError", "library_path", "load"]
+           "fa_fwd_fp8", "fa_fwd_fp8_workspace_size", "fa_strerror", "forward", "backward",
+           "forward_varlen", "backward_varlen", "forward_splitkv", "forward_fp8", "FaError",
+           "library_path", "load"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libfa.so")
@@ -37,7 +38,7 @@ EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_workspace_size", "fa_bwd_pr
             "fa_bwd_main", "fa_bwd_dq", "fa_fwd_varlen", "fa_fwd_varlen_workspace_size",
             "fa_varlen_max_seqlen", "fa_fwd_splitkv", "fa_fwd_splitkv_num_splits",
             "fa_fwd_splitkv_workspace_size", "fa_bwd_varlen", "fa_bwd_varlen_workspace_size",
-            "fa_strerror")
+            "fa_fwd_fp8", "fa_fwd_fp8_workspace_size", "fa_strerror")
 
 
 class FaError(RuntimeError):
@@ -93,6 +94,10 @@ def load():
     lib.fa_bwd_varlen_workspace_size.restype = sz
     lib.fa_bwd_varlen.argtypes = [vp] * 10 + [ci] * 7 + [cf, vp, sz, ci, vp]
     lib.fa_bwd_varlen.restype = ci
+    lib.fa_fwd_fp8_workspace_size.argtypes = [ci] * 5
+    lib.fa_fwd_fp8_workspace_size.restype = sz
+    lib.fa_fwd_fp8.argtypes = [vp] * 5 + [ci] * 6 + [cf, vp, vp, sz, vp]
+    lib.fa_fwd_fp8.restype = ci
     lib.fa_strerror.argtypes = [ci]
     lib.fa_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -175,6 +180,16 @@ def fa_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens, B, Hq, Hkv, tot
     return load().fa_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens, B, Hq, Hkv, total,
                                 max_seqlen, D, int(causal), float(scale), workspace,
                                 workspace_bytes, int(deterministic), stream)
+
+
+def fa_fwd_fp8_workspace_size(B, Hq, Hkv, N, D) -> int:
+    return int(load().fa_fwd_fp8_workspace_size(B, Hq, Hkv, N, D))
+
+
+def fa_fwd_fp8(q, k, v, o, lse, B, Hq, Hkv, N, D, causal, scale, signs, workspace,
+               workspace_bytes, stream) -> int:
+    return load().fa_fwd_fp8(q, k, v, o, lse, B, Hq, Hkv, N, D, int(causal), float(scale), signs,
+                             workspace, workspace_bytes, stream)
 
 
 def fa_strerror(status: int) -> str:
@@ -366,3 +381,29 @@ def backward_varlen(q, k, v, o, lse, dout, cu_seqlens, max_seqlen: int, causal: 
     if rc != FA_OK:
         raise FaError(rc, "fa_bwd_varlen")
     return dq, dk, dv
+
+
+def forward_fp8(q, k, v, causal: bool, scale: float, signs=None, *, out=None, lse=None,
+                workspace=None):
+    """FP8 forward: O (bf16), LSE (fp32) for q [B,Hq,N,D], k/v [B,Hkv,N,D] bf16
+    device tensors; signs an optional float32 device tensor of D values +-1
+    (the Hadamard rotation's random signs)."""
+    import torch
+    B, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    _check("q", q, torch.bfloat16, (B, Hq, N, D))
+    _check("k", k, torch.bfloat16, (B, Hkv, N, D))
+    _check("v", v, torch.bfloat16, (B, Hkv, N, D))
+    if signs is not None:
+        _check("signs", signs, torch.float32, (D,))
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    ws_bytes = fa_fwd_fp8_workspace_size(B, Hq, Hkv, N, D)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    rc = fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq,
+                    Hkv, N, D, causal, scale, signs.data_ptr() if signs is not None else None,
+                    workspace.data_ptr(), workspace.numel(), _stream_handle(q.device))
+    if rc != FA_OK:
+        raise FaError(rc, "fa_fwd_fp8")
+    return out, lse

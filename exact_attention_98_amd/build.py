@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libfa.so")
 ARCH = "gfx950"
-SOURCES = ["fa_api.cpp", "fwd_kernel.hip", "bwd_kernels.hip"]
+SOURCES = ["fa_api.cpp", "fwd_kernel.hip", "bwd_kernels.hip", "fp8_kernel.hip"]
 
 
 def hipcc() -> str:

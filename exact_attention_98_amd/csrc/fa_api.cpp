@@ -189,6 +189,43 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, co
   return fa::launch_bwd_varlen(a, va, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+size_t fa_fwd_fp8_workspace_size(int B, int Hq, int Hkv, int N, int D) {
+  if (check_shape(B, Hq, Hkv, N, D, 1.0f) != FA_OK) return 0;
+  size_t total = 0;
+  fa::fp8_layout(B, Hq, Hkv, N, D, nullptr, &total);
+  return total;
+}
+
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+               int Hkv, int N, int D, int causal, float scale, const float* signs,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse || !workspace) return FA_ERR_INVALID;
+  int rc = check_shape(B, Hq, Hkv, N, D, scale);
+  if (rc != FA_OK) return rc;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      (signs && !aligned16(signs)))
+    return FA_ERR_ALIGN;
+  if (((uintptr_t)workspace & 255u) != 0) return FA_ERR_ALIGN;
+  size_t wbytes = 0;
+  fa::fp8_layout(B, Hq, Hkv, N, D, nullptr, &wbytes);
+  if (workspace_bytes < wbytes) return FA_ERR_WORKSPACE;
+  const size_t qb = (size_t)B * Hq * N * D * 2, kb = (size_t)B * Hkv * N * D * 2;
+  const size_t lb = (size_t)B * Hq * N * 4, sbytes = (size_t)D * 4;
+  const void* ins[4] = {q, k, v, signs};
+  const size_t isz[4] = {qb, kb, kb, signs ? sbytes : 0};
+  const void* outs[3] = {o, lse, workspace};
+  const size_t osz[3] = {qb, lb, wbytes};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 4; ++j)
+      if (isz[j] && overlaps(outs[i], osz[i], ins[j], isz[j])) return FA_ERR_INVALID;
+    for (int j = 0; j < 3; ++j)
+      if (j != i && overlaps(outs[i], osz[i], outs[j], osz[j])) return FA_ERR_INVALID;
+  }
+  fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, D, causal ? 1 : 0, scale, 0};
+  return fa::launch_fwd_fp8(a, signs, workspace, (hipStream_t)stream) == hipSuccess ? FA_OK
+                                                                                    : FA_ERR_HIP;
+}
+
 int fa_fwd_splitkv_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int D) {
   if (check_split(B, Hq, Hkv, Nq, Nk, D, 0, 1.0f) != FA_OK) return 0;
   return fa::split_auto(B, Hq, Hkv, Nq, Nk);

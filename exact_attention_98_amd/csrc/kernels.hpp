@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
 
 namespace fa {
 
@@ -74,6 +75,21 @@ int split_auto(int B, int Hq, int Hkv, int Nq, int Nk);
 int split_max(int Nk);
 size_t split_workspace_bytes(int B, int Hq, int Nq, int D, int splits);
 hipError_t launch_fwd_split(const FwdArgs& a, const SplitArgs& s, hipStream_t stream);
+
+// FP8 forward: quantized copies of Q, K (rotated) and V (transposed per
+// 64-key tile) and their per-tile scales, all in the caller's workspace.
+struct Fp8Layout {
+  int N, Np, nt;       // rows, rows padded to whole 64-row tiles, tiles per head
+  int BHq, BHkv;       // B * Hq, B * Hkv
+  uint8_t* q8;         // e4m3 [B*Hq][Np][D]
+  uint8_t* k8;         // e4m3 [B*Hkv][Np][D]
+  uint8_t* v8;         // e4m3 [B*Hkv][nt][D][64], keys in P-operand order
+  float* qs;           // dequantization factors [B*Hq][nt]
+  float* ks;           // [B*Hkv][nt]
+  int* ve;             // V factor exponents e (2^e) [B*Hkv][nt]
+};
+Fp8Layout fp8_layout(int B, int Hq, int Hkv, int N, int D, void* workspace, size_t* total);
+hipError_t launch_fwd_fp8(const FwdArgs& a, const float* signs, void* workspace, hipStream_t stream);
 
 struct BwdArgs {
   const void* q;

@@ -224,6 +224,29 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                    int Hq, int Hkv, int Nq, int Nk, int D, int causal, float scale,
                    int num_splits, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * FP8 forward (OCP e4m3 matrix products), for the same tensors and layout as
+ * fa_fwd.  Following the hotdry article's FP8 passage ("incoherent
+ * processing"): Q and K are rotated by x -> (x o signs) H / sqrt(D), H the
+ * Walsh-Hadamard matrix, which leaves Q K^T unchanged and spreads outlier
+ * channels; Q, K and V are quantized to e4m3 with one scale per 64 rows of
+ * each (batch, head) (Q, K: largest magnitude -> 448; V: a power of two);
+ * both products run on the FP8 matrix cores; P is rounded to e4m3 (as 256 P,
+ * kept <= 1 before scaling by rescaling whenever a row maximum grows).  O is
+ * bf16 and LSE fp32 as in fa_fwd.  The rounding to e4m3 costs accuracy
+ * (about 2^-4 relative per element of P and of the inputs); see the tests
+ * for the bounds used.
+ *   signs: device float[D] of +1 / -1 (drawn by the caller; NULL = no
+ *     rotation).
+ *   workspace: fa_fwd_fp8_workspace_size() bytes, 256-byte aligned: the
+ *     quantized copies and their scales.
+ * Errors as fa_fwd, plus FA_ERR_WORKSPACE.
+ */
+size_t fa_fwd_fp8_workspace_size(int B, int Hq, int Hkv, int N, int D);
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+               int Hkv, int N, int D, int causal, float scale, const float* signs,
+               void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* fa_strerror(int status);
 

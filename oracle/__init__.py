@@ -49,6 +49,9 @@ def _load():
         lib.oracle_fwd.argtypes = [u16p, u16p, u16p, f64p, f64p, ci, ci, ci, ci, ci, ci, ci,
                                    ctypes.c_double]
         lib.oracle_fwd.restype = ci
+        lib.oracle_fwd_f64.argtypes = [f64p, f64p, f64p, f64p, f64p, ci, ci, ci, ci, ci, ci, ci,
+                                       ctypes.c_double]
+        lib.oracle_fwd_f64.restype = ci
         lib.oracle_bwd.argtypes = [u16p, u16p, u16p, u16p, f64p, f64p, f64p, ci, ci, ci, ci, ci,
                                    ci, ci, ctypes.c_double]
         lib.oracle_bwd.restype = ci
@@ -97,6 +100,24 @@ def attention_fwd(q, k, v, causal: bool, scale: float):
                             float(scale))
     if rc != 0:
         raise RuntimeError(f"oracle_fwd failed ({rc})")
+    return torch.from_numpy(o), torch.from_numpy(lse)
+
+
+def attention_fwd_f64(q, k, v, causal: bool, scale: float):
+    """As attention_fwd, for fp64 inputs (any real values, e.g. dequantized
+    ones): O [B,Hq,Nq,D] and LSE [B,Hq,Nq], fp64."""
+    B, Hq, Hkv, Nq, Nk, D = _dims(q, k)
+    if tuple(v.shape) != tuple(k.shape):
+        raise ValueError("v must match k")
+    qa, ka, va = (np.ascontiguousarray(t.detach().cpu().double().numpy()) for t in (q, k, v))
+    o = np.zeros((B, Hq, Nq, D), dtype=np.float64)
+    lse = np.zeros((B, Hq, Nq), dtype=np.float64)
+    rc = _load().oracle_fwd_f64(_ptr(qa, ctypes.c_double), _ptr(ka, ctypes.c_double),
+                                _ptr(va, ctypes.c_double), _ptr(o, ctypes.c_double),
+                                _ptr(lse, ctypes.c_double), B, Hq, Hkv, Nq, Nk, D,
+                                int(bool(causal)), float(scale))
+    if rc != 0:
+        raise RuntimeError(f"oracle_fwd_f64 failed ({rc})")
     return torch.from_numpy(o), torch.from_numpy(lse)
 
 

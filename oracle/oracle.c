@@ -64,6 +64,21 @@ static void widen(const uint16_t* src, double* dst, long n) {
     for (long t = 0; t < n; ++t) dst[t] = bf16_to_f64(src[t]);
 }
 
+/* Element source of the forward: bf16 bit patterns or fp64 values. */
+typedef struct {
+    const void* p;
+    int is_f64;
+} src_t;
+
+static void load(src_t src, long off, double* dst, long n) {
+    if (src.is_f64) {
+        const double* d = (const double*)src.p + off;
+        for (long t = 0; t < n; ++t) dst[t] = d[t];
+    } else {
+        widen((const uint16_t*)src.p + off, dst, n);
+    }
+}
+
 static double dot(const double* a, const double* b, int D) {
     double s = 0.0;
     for (int d = 0; d < D; ++d) s += a[d] * b[d];
@@ -112,8 +127,8 @@ static void row_scores(const double* qi, const double* K, int nk, int D, double 
  * Forward: o [B][Hq][Nq][D], lse [B][Hq][Nq].
  * A row with no unmasked key gets O = 0 and LSE = -inf.
  */
-int oracle_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, double* o, double* lse,
-               int B, int Hq, int Hkv, int Nq, int Nk, int D, int causal, double scale) {
+static int fwd_impl(src_t q, src_t k, src_t v, double* o, double* lse,
+                    int B, int Hq, int Hkv, int Nq, int Nk, int D, int causal, double scale) {
     if (check_shape(B, Hq, Hkv, Nq, Nk, D)) return -1;
     const int G = Hq / Hkv;
     for (int b = 0; b < B; ++b) {
@@ -122,9 +137,9 @@ int oracle_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, double* 
             double* K = (double*)malloc(sizeof(double) * ((size_t)Nk * D + 1));
             double* V = (double*)malloc(sizeof(double) * ((size_t)Nk * D + 1));
             if (!K || !V) { free(K); free(V); return -2; }
-            widen(k + ((long)b * Hkv + hk) * Nk * D, K, (long)Nk * D);
-            widen(v + ((long)b * Hkv + hk) * Nk * D, V, (long)Nk * D);
-            const uint16_t* Qh = q + ((long)b * Hq + hq) * Nq * D;
+            load(k, ((long)b * Hkv + hk) * Nk * D, K, (long)Nk * D);
+            load(v, ((long)b * Hkv + hk) * Nk * D, V, (long)Nk * D);
+            const long qoff = ((long)b * Hq + hq) * Nq * D;
             double* Oh = o + ((long)b * Hq + hq) * Nq * D;
             double* Lh = lse + ((long)b * Hq + hq) * Nq;
             int fail = 0;
@@ -138,7 +153,7 @@ int oracle_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, double* 
                 } else {
 #pragma omp for schedule(dynamic, 16)
                     for (int i = 0; i < Nq; ++i) {
-                        widen(Qh + (long)i * D, qi, D);
+                        load(q, qoff + (long)i * D, qi, D);
                         const int nk = row_keys(i, Nk, causal);
                         double m, l;
                         row_scores(qi, K, nk, D, scale, s, &m, &l);
@@ -162,6 +177,19 @@ int oracle_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, double* 
         }
     }
     return 0;
+}
+
+int oracle_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, double* o, double* lse,
+               int B, int Hq, int Hkv, int Nq, int Nk, int D, int causal, double scale) {
+    const src_t sq = {q, 0}, sk = {k, 0}, sv = {v, 0};
+    return fwd_impl(sq, sk, sv, o, lse, B, Hq, Hkv, Nq, Nk, D, causal, scale);
+}
+
+/* The same definition on fp64 inputs (used on dequantized values). */
+int oracle_fwd_f64(const double* q, const double* k, const double* v, double* o, double* lse,
+                   int B, int Hq, int Hkv, int Nq, int Nk, int D, int causal, double scale) {
+    const src_t sq = {q, 1}, sk = {k, 1}, sv = {v, 1};
+    return fwd_impl(sq, sk, sv, o, lse, B, Hq, Hkv, Nq, Nk, D, causal, scale);
 }
 
 /*

@@ -142,3 +142,10 @@ def varlen_flops_fwd(lens, Hq: int, D: int, causal: bool) -> float:
     """4 Hq len^2 D per sequence, halved under the causal mask."""
     f = sum(4.0 * Hq * n * n * D for n in lens)
     return f / 2 if causal else f
+
+
+def hadamard_signs(D: int, *, seed: int = 0) -> torch.Tensor:
+    """Random +-1 signs of the FP8 path's Hadamard rotation (float32 [D])."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    return torch.where(torch.rand(D, generator=g) < 0.5, -1.0, 1.0).to(torch.float32)
