@@ -28,6 +28,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 METRIC = "attention fwd/bwd TFLOPS + % bf16 MFMA peak, B2 H16 N8K D128 causal"
 KERNEL_SOURCES = {
     "fwd_kernel": ["exact_attention_98_amd/csrc/fwd_kernel.hip",
@@ -133,6 +134,42 @@ def bench_varlen(fa, torch, dev, stream, reps: int = 20) -> dict:
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
 
 
+def bench_fp8(fa, torch, dev, stream, P, w, reps: int = 20) -> dict:
+    """FP8 forward on the headline shape (same inputs as the bf16 step),
+    rotation on; the timed call includes the quantize pass."""
+    import synth
+    B, Hq, Hkv, N, D = w.B, w.Hq, w.Hkv, w.N, w.D
+    signs = synth.hadamard_signs(D).to(dev)
+    wsb = fa.fa_fwd_fp8_workspace_size(B, Hq, Hkv, N, D)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    o = torch.empty((B, Hq, N, D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    sh = stream.cuda_stream
+
+    def call():
+        rc = fa.fa_fwd_fp8(P["q"], P["k"], P["v"], o.data_ptr(), lse.data_ptr(), B, Hq, Hkv, N, D,
+                           1, w.scale, signs.data_ptr(), ws.data_ptr(), wsb, sh)
+        if rc != 0:
+            raise RuntimeError(f"fa_fwd_fp8: {fa.fa_strerror(rc)}")
+
+    for _ in range(3):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    tf = w.flops_fwd() / (us * 1e-6) / 1e12
+    return {"workload": f"B{B} H{Hq} N{N} D{D} causal, e4m3, Hadamard rotation on "
+                        "(quantize pass included)",
+            "us": round(us, 1), "tflops": round(tf, 1),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_FP8_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4)}}
+
+
 def bench_decode(fa, torch, dev, stream, reps: int = 50) -> dict:
     """Decode-shaped multi-query forward (split-KV + merge): one new query per
     sequence and head over a long K/V cache; bound by reading K and V."""
@@ -189,7 +226,7 @@ def main() -> int:
                          "workspace), or atomic adds")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the variable-length and decode measurements")
+                    help="skip the variable-length, decode and FP8 measurements")
     ap.add_argument("--cpu-heads", type=int, default=16)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device-to-device copy of MIB MiB (read MIB, write MIB) "
@@ -360,7 +397,8 @@ def main() -> int:
     out["bwd"]["workspace_bytes"] = ws_bytes
     if not args.no_extras:
         out["extras"] = {"varlen_fwd": bench_varlen(fa, torch, dev, stream),
-                         "decode_splitkv": bench_decode(fa, torch, dev, stream)}
+                         "decode_splitkv": bench_decode(fa, torch, dev, stream),
+                         "fp8_fwd": bench_fp8(fa, torch, dev, stream, P, w)}
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_heads} heads")
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
