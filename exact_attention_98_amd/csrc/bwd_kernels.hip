@@ -1121,10 +1121,10 @@ hipError_t launch_bwd_varlen_t(const BwdArgs& a, const VarlenArgs& v, hipStream_
   int* dq_items = (int*)(lists + lbytes + 256);
   const unsigned items_max = (unsigned)(v.total / 128 + v.B);
   constexpr int QS = 4096 / D;
-  hipError_t e = launch_varlen_schedule(v, CAUSAL, 1, QS, main_n, main_items, s);
+  hipError_t e = launch_varlen_schedule(v, CAUSAL, 1, QS, kBwdBN, main_n, main_items, s);
   if (e != hipSuccess) return e;
   if (a.deterministic == kDqRecompute) {
-    e = launch_varlen_schedule(v, CAUSAL, 0, QS, dq_n, dq_items, s);
+    e = launch_varlen_schedule(v, CAUSAL, 0, QS, 128, dq_n, dq_items, s);
     if (e != hipSuccess) return e;
   }
   e = launch_pre_d<D>(a, s);

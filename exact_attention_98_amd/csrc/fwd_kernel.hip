@@ -1,7 +1,7 @@
 // Fused exact-attention forward for gfx950 (MI355X).
 //
-// One workgroup of 4 waves owns a tile of 128 queries of one (batch, head);
-// each wave owns 32 of them.  K/V tiles of 64 keys are copied from HBM
+// One workgroup of 8 waves (two per SIMD) owns a tile of 256 queries of one
+// (batch, head); each wave owns 32 of them, and all 8 share each K/V tile.  K/V tiles of 64 keys are copied from HBM
 // straight into LDS (buffer_load ... lds, double-buffered, one barrier per
 // tile) past the resident Q fragments, and each tile runs
 //   S^T = K Q^T          (bf16 MFMA 32x32x16, fp32 accumulate)
@@ -37,9 +37,9 @@
 namespace fa {
 namespace {
 
-constexpr int kFwdBM = 128;   // queries per workgroup
+constexpr int kFwdBM = 256;   // queries per workgroup (8 waves sharing each K/V tile)
 constexpr int kFwdBN = 64;    // keys per K/V tile
-constexpr int kFwdWaves = 4;
+constexpr int kFwdWaves = 8;
 
 // Addressing modes of the forward kernel.
 constexpr int kModeDense = 0;   // [B][H][N][D], one workgroup per (b, hq, query tile)
@@ -47,7 +47,7 @@ constexpr int kModeVarlen = 1;  // packed sequences, work list sorted longest fi
 constexpr int kModeSplit = 2;   // query rows of a K/V group, one key range per workgroup
 
 template <int D, bool CAUSAL, int POLYQ, int MODE>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(const uint16_t* __restrict__ Q,
+__global__ __launch_bounds__(512, 1) void fwd_kernel(const uint16_t* __restrict__ Q,
                                                      const uint16_t* __restrict__ K,
                                                      const uint16_t* __restrict__ V,
                                                      uint16_t* __restrict__ O,
@@ -451,14 +451,14 @@ hipError_t launch_fwd_c(const FwdArgs& a, hipStream_t s) {
 constexpr int kSchedThreads = 1024;
 constexpr int kSchedMaxCost = 16384 - kSchedThreads - 1;  // histogram + chunk sums <= 64 KiB
 
-// KIND 0 lists (sequence, 128-query tile) items costed by the 64-key tiles
-// they walk (forward, fixed-order dQ pass); KIND 1 lists (sequence, 128-key
-// block) items costed by the query steps of qstep queries they walk (main
-// backward kernel).
+// Items are (sequence, tile of `rows` rows).  KIND 0 costs a query tile by
+// the 64-key tiles it walks (forward, fixed-order dQ pass); KIND 1 costs a key
+// block by the query steps of qstep queries it walks (main backward kernel).
 template <bool CAUSAL, int KIND>
 __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(const int* __restrict__ cu,
                                                                       int B, int total,
                                                                       int max_cost, int qstep,
+                                                                      int rows,
                                                                       int* __restrict__ n_items,
                                                                       int* __restrict__ items) {
   extern __shared__ int sm[];
@@ -474,17 +474,17 @@ __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(const in
   };
   auto cost = [&](int len, int qb) {
     if constexpr (KIND == 0) {
-      const int kend = CAUSAL ? min(len, (qb + 1) * kFwdBM) : len;
+      const int kend = CAUSAL ? min(len, (qb + 1) * rows) : len;
       return min((kend + kFwdBN - 1) / kFwdBN, max_cost);
     } else {
       const int nsteps = (len + qstep - 1) / qstep;
-      const int first = CAUSAL ? (qb * kFwdBM) / qstep : 0;
+      const int first = CAUSAL ? (qb * rows) / qstep : 0;
       return min(max(nsteps - first, 0), max_cost);
     }
   };
   for (int b = tid; b < B; b += kSchedThreads) {
     const int len = seq_len(b);
-    for (int qb = 0; qb * kFwdBM < len; ++qb) atomicAdd(&hist[cost(len, qb)], 1);
+    for (int qb = 0; qb * rows < len; ++qb) atomicAdd(&hist[cost(len, qb)], 1);
   }
   __syncthreads();
   // Exclusive scan in decreasing cost: slot r = max_cost - c.  Thread t owns
@@ -511,7 +511,7 @@ __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(const in
   __syncthreads();
   for (int b = tid; b < B; b += kSchedThreads) {
     const int len = seq_len(b);
-    for (int qb = 0; qb * kFwdBM < len; ++qb) {
+    for (int qb = 0; qb * rows < len; ++qb) {
       const int pos = atomicAdd(&hist[cost(len, qb)], 1);
       items[2 * pos] = b;
       items[2 * pos + 1] = qb;
@@ -528,7 +528,7 @@ hipError_t launch_fwd_varlen_t(const FwdArgs& a, const VarlenArgs& v, hipStream_
   const int max_cost = (v.max_seqlen + kFwdBN - 1) / kFwdBN;
   const size_t shm = (size_t)(max_cost + 1 + kSchedThreads) * sizeof(int);
   hipLaunchKernelGGL((varlen_schedule_kernel<CAUSAL, 0>), dim3(1), dim3(kSchedThreads), shm, s,
-                     v.cu, v.B, v.total, max_cost, 0, n_items, items);
+                     v.cu, v.B, v.total, max_cost, 0, kFwdBM, n_items, items);
   FwdParams p;
   p.BH = 0;
   p.Hq = a.Hq;
@@ -653,7 +653,7 @@ hipError_t launch_fwd_split(const FwdArgs& a, const SplitArgs& sa, hipStream_t s
   return a.causal ? launch_fwd_split_t<128, true>(a, sa, s) : launch_fwd_split_t<128, false>(a, sa, s);
 }
 
-hipError_t launch_varlen_schedule(const VarlenArgs& v, int causal, int kind, int qstep,
+hipError_t launch_varlen_schedule(const VarlenArgs& v, int causal, int kind, int qstep, int rows,
                                   int* n_items, int* items, hipStream_t s) {
   // Largest cost: 64-key tiles of the longest sequence (kind 0) or its query
   // steps (kind 1, qstep >= 32 so never more than twice the tiles).
@@ -663,23 +663,25 @@ hipError_t launch_varlen_schedule(const VarlenArgs& v, int causal, int kind, int
   if (kind == 0) {
     if (causal)
       hipLaunchKernelGGL((varlen_schedule_kernel<true, 0>), dim3(1), dim3(kSchedThreads), shm, s,
-                         v.cu, v.B, v.total, max_cost, qstep, n_items, items);
+                         v.cu, v.B, v.total, max_cost, qstep, rows, n_items, items);
     else
       hipLaunchKernelGGL((varlen_schedule_kernel<false, 0>), dim3(1), dim3(kSchedThreads), shm, s,
-                         v.cu, v.B, v.total, max_cost, qstep, n_items, items);
+                         v.cu, v.B, v.total, max_cost, qstep, rows, n_items, items);
   } else {
     if (causal)
       hipLaunchKernelGGL((varlen_schedule_kernel<true, 1>), dim3(1), dim3(kSchedThreads), shm, s,
-                         v.cu, v.B, v.total, max_cost, qstep, n_items, items);
+                         v.cu, v.B, v.total, max_cost, qstep, rows, n_items, items);
     else
       hipLaunchKernelGGL((varlen_schedule_kernel<false, 1>), dim3(1), dim3(kSchedThreads), shm, s,
-                         v.cu, v.B, v.total, max_cost, qstep, n_items, items);
+                         v.cu, v.B, v.total, max_cost, qstep, rows, n_items, items);
   }
   return hipGetLastError();
 }
 
+// Room for one work list of tiles of at least 128 rows: at most
+// sum_b ceil(len_b / 128) <= total / 128 + B items.
 size_t varlen_workspace_bytes(int B, int total) {
-  return 256 + ((size_t)total / kFwdBM + B) * 2 * sizeof(int);
+  return 256 + ((size_t)total / 128 + B) * 2 * sizeof(int);
 }
 
 int varlen_max_seqlen_limit() { return kSchedMaxCost * kFwdBN; }

@@ -57,10 +57,11 @@ size_t varlen_workspace_bytes(int B, int total);
 int varlen_max_seqlen_limit();
 hipError_t launch_fwd_varlen(const FwdArgs& a, const VarlenArgs& v, hipStream_t stream);
 // Work list of a variable-length batch into n_items / items (2 ints per item,
-// room for varlen_workspace_bytes(B, total) - 256 bytes): kind 0 = (sequence,
-// 128-query tile) by 64-key tiles walked; kind 1 = (sequence, 128-key block) by
-// query steps of qstep walked; largest first.
-hipError_t launch_varlen_schedule(const VarlenArgs& v, int causal, int kind, int qstep,
+// room for varlen_workspace_bytes(B, total) - 256 bytes, enough for tiles of
+// rows >= 128): kind 0 = (sequence, query tile of `rows`) by 64-key tiles
+// walked; kind 1 = (sequence, key block of `rows`) by query steps of qstep
+// walked; largest first.
+hipError_t launch_varlen_schedule(const VarlenArgs& v, int causal, int kind, int qstep, int rows,
                                   int* n_items, int* items, hipStream_t stream);
 
 // Split-KV forward for decode-shaped problems: q, o [B][Hq][Nq][D], k, v
