@@ -1,7 +1,8 @@
 // Fused exact-attention forward for gfx950 (MI355X).
 //
-// One workgroup of 8 waves (two per SIMD) owns a tile of 256 queries of one
-// (batch, head); each wave owns 32 of them, and all 8 share each K/V tile.  K/V tiles of 64 keys are copied from HBM
+// One workgroup of NW waves owns a tile of 32 NW queries of one (batch, head);
+// each wave owns 32 of them, and all share each K/V tile (dense: 8 waves, two
+// per SIMD; split-KV: 4, two workgroups per CU).  K/V tiles of 64 keys are copied from HBM
 // straight into LDS (buffer_load ... lds, double-buffered, one barrier per
 // tile) past the resident Q fragments, and each tile runs
 //   S^T = K Q^T          (bf16 MFMA 32x32x16, fp32 accumulate)
@@ -37,26 +38,36 @@
 namespace fa {
 namespace {
 
-constexpr int kFwdBM = 256;   // queries per workgroup (8 waves sharing each K/V tile)
-constexpr int kFwdBN = 64;    // keys per K/V tile
-constexpr int kFwdWaves = 8;
+constexpr int kFwdWaves = 8;     // dense forward: 8 waves, 256 queries
+constexpr int kVarlenWaves = 4;  // variable-length forward: 4 waves, 128 queries (short sequences waste fewer rows)
+constexpr int kSplitWaves = 4;   // split-KV: 4 waves, 128 query rows, two workgroups per CU
+constexpr int kFwdBM = 32 * kFwdWaves;
+constexpr int kVarlenBM = 32 * kVarlenWaves;
+constexpr int kSplitBM = 32 * kSplitWaves;
+constexpr int kFwdBN = 64;       // keys per K/V tile
+
+template <bool V>
+struct Flag {
+  static constexpr bool value = V;
+};
 
 // Addressing modes of the forward kernel.
 constexpr int kModeDense = 0;   // [B][H][N][D], one workgroup per (b, hq, query tile)
 constexpr int kModeVarlen = 1;  // packed sequences, work list sorted longest first
 constexpr int kModeSplit = 2;   // query rows of a K/V group, one key range per workgroup
 
-template <int D, bool CAUSAL, int POLYQ, int MODE>
-__global__ __launch_bounds__(512, 1) void fwd_kernel(const uint16_t* __restrict__ Q,
+template <int D, bool CAUSAL, int POLYQ, int MODE, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(const uint16_t* __restrict__ Q,
                                                      const uint16_t* __restrict__ K,
                                                      const uint16_t* __restrict__ V,
                                                      uint16_t* __restrict__ O,
                                                      float* __restrict__ LSE, FwdParams p) {
-  constexpr int BM = kFwdBM, BN = kFwdBN;
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  constexpr int BM = 32 * NW, BN = kFwdBN;
   constexpr int RB = D * 2;             // bytes per K/V row
   constexpr int KCH = D / 8;            // 16-byte chunks per row
   constexpr int TB = BN * RB;           // bytes per K (or V) tile
-  constexpr int NLD = TB / 1024 / kFwdWaves;  // 1 KiB direct loads per wave per tensor
+  constexpr int NLD = TB / 1024 / NW;  // 1 KiB direct loads per wave per tensor
   static_assert(NLD >= 1, "tile too small");
   // K and V tiles double-buffered separately, each buffer its own array so the
   // compiler can tell an in-flight copy into one from reads of another.  While
@@ -66,6 +77,13 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(const uint16_t* __restrict_
   __shared__ __attribute__((aligned(1024))) char kbuf1[TB];
   __shared__ __attribute__((aligned(1024))) char vbuf0[TB];
   __shared__ __attribute__((aligned(1024))) char vbuf1[TB];
+  // Ping-pong of the two halves of an 8-wave workgroup (below): two more V
+  // buffers.
+  constexpr bool PING = NW == 8;
+  __shared__ __attribute__((aligned(1024))) char vbuf2_[PING ? TB : 1024];
+  __shared__ __attribute__((aligned(1024))) char vbuf3_[PING ? TB : 1024];
+  char* const vbuf2 = PING ? vbuf2_ : vbuf0;
+  char* const vbuf3 = PING ? vbuf3_ : vbuf1;
 
   // Work item of this workgroup: (sequence, query head, query tile).
   // Dense grid order: consecutive workgroup ids walk heads first, so with
@@ -143,6 +161,9 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(const uint16_t* __restrict_
   const int q0 = qb * BM;
   const int qw = q0 + wave * 32;   // first query of this wave (uniform)
   const int qi = qw + n;           // this lane's query
+  // Lagging half of the ping-pong: waves NW/2 .. NW-1 (wave w runs on SIMD
+  // w % 4, so every SIMD holds one wave of each half).
+  const bool lag = PING && wave >= NW / 2;
 
   // Q fragments (B operand of S^T = K Q^T): k-step t covers d in [16t, 16t+16),
   // lane half h holds d = 16t + 8h .. +8 of query qi (rows past N read as 0).
@@ -168,13 +189,13 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(const uint16_t* __restrict_
   const int ntiles = (kend + BN - 1) / BN;
 
   // ---- direct HBM -> LDS staging -------------------------------------------
-  // Load s of this wave fills LDS chunks g = (s*4 + wave)*64 + lane of the
+  // Load s of this wave fills LDS chunks g = (s*NW + wave)*64 + lane of the
   // tile: row g / KCH, physical chunk g % KCH, holding logical chunk
   // (g % KCH) ^ f(row).
   uint32_t ld_off[NLD];
 #pragma unroll
   for (int s = 0; s < NLD; ++s) {
-    const int g = (s * kFwdWaves + wave) * 64 + lane;
+    const int g = (s * NW + wave) * 64 + lane;
     const int row = g / KCH, pc = g % KCH;
     ld_off[s] = (uint32_t)(row * RB + ((pc ^ tile_swz<D>(row)) * 16));
   }
@@ -183,7 +204,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(const uint16_t* __restrict_
     const uint32_t left = kv_bytes > base ? kv_bytes - base : 0u;
     const rsrc_t r = make_rsrc_uniform((const char*)src + base, left);
 #pragma unroll
-    for (int s = 0; s < NLD; ++s) lds_dma16(r, (lds_void*)(dst + (s * kFwdWaves + wave) * 1024), ld_off[s]);
+    for (int s = 0; s < NLD; ++s) lds_dma16(r, (lds_void*)(dst + (s * NW + wave) * 1024), ld_off[s]);
   };
 
   // Per-lane LDS read offsets (buffer, sub-block and step offsets are constants).
@@ -209,6 +230,9 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(const uint16_t* __restrict_
   }
 
   constexpr int T = D / 16;
+  // LDS read distance: operand fragments are read this many MFMAs (phase A:
+  // k-steps) ahead of the instruction that consumes them.
+  constexpr int PDA = 1, PDB = 2;
   // Mask keys past the end and, under causal, keys after the query, on the
   // tiles that need it.  Register r of half sb holds key
   // k0 + 32 sb + 8 (r/4) + 4 h + r % 4.
@@ -258,16 +282,15 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(const uint16_t* __restrict_
     }
   };
 
-  // One tile kt.  sv holds S^T(kt), masked, with m_new its candidate max; sn
-  // receives S^T(kt+1).  Issue order is fixed by hand (sched_barrier fences):
-  // the MFMA unit runs one instruction at a time in program order, so each
-  // matrix instruction is followed by VALU work that runs under it.
-  auto body = [&](int kt, const char* kn, const char* vc, char* kld, char* vld, f32x16 (&sv)[2],
-                  f32x16 (&sn)[2], float& m_new) {
-    wait_vmcnt<0>();
-    __syncthreads();  // K(kt+1), V(kt) in LDS; tile kt-1's buffers are free
-    if (kt + 2 < ntiles) issue(Kh, kt + 2, kld);
-    if (kt + 1 < ntiles) issue(Vh, kt + 1, vld);
+  // One tile kt is two phases.  Phase A(kt): sv holds S^T(kt), masked, with
+  // m_new its candidate max; P^T(kt) goes to pb and S^T(kt+1) to sn.  Phase
+  // B(kt): O^T += V^T P^T(kt) and the candidate max of S^T(kt+1).  Issue order
+  // is fixed by hand (sched_barrier fences): the MFMA unit runs one
+  // instruction at a time in program order, so each matrix instruction is
+  // followed by VALU work that runs under it.
+  bf16x8 pb[2][2];
+  auto phase_a = [&](int kt, const char* kn, f32x16 (&sv)[2], f32x16 (&sn)[2],
+                     float m_new) __attribute__((always_inline)) {
     rescale(m_new);
     const float msub = (m_ref == -__builtin_inff()) ? 0.f : m_ref;
 
@@ -278,21 +301,23 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(const uint16_t* __restrict_
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sn[sb][r] = 0.f;
-    bf16x8 pb[2][2];
     // MFMA pair j = k-step t: sub-blocks 0 and 1 alternate, so consecutive
-    // MFMAs never accumulate into the same registers.
-    bf16x8 ka = as_bf16x8(*(const u32x4*)(kn + k_off[0]));
-    bf16x8 kb2 = as_bf16x8(*(const u32x4*)(kn + 32 * RB + k_off[0]));
+    // MFMAs never accumulate into the same registers.  The K fragments are
+    // read PDA k-steps ahead of their MFMAs.
+    auto kread = [&](int j, int sb) { return as_bf16x8(*(const u32x4*)(kn + sb * 32 * RB + k_off[j])); };
+    bf16x8 kq[PDA][2];
+#pragma unroll
+    for (int j = 0; j < PDA; ++j) {
+      kq[j][0] = kread(j, 0);
+      kq[j][1] = kread(j, 1);
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < T; ++j) {
-      sn[0] = mfma32(ka, qf[j], sn[0]);
-      const bf16x8 kc = kb2;
-      if (j + 1 < T) {
-        ka = as_bf16x8(*(const u32x4*)(kn + k_off[j + 1]));
-        kb2 = as_bf16x8(*(const u32x4*)(kn + 32 * RB + k_off[j + 1]));
-      }
-      sn[1] = mfma32(kc, qf[j], sn[1]);
+      sn[0] = mfma32(kq[j % PDA][0], qf[j], sn[0]);
+      if (j + PDA < T) kq[j % PDA][0] = kread(j + PDA, 0);
+      sn[1] = mfma32(kq[j % PDA][1], qf[j], sn[1]);
+      if (j + PDA < T) kq[j % PDA][1] = kread(j + PDA, 1);
 #pragma unroll
       for (int e = j * (32 / T); e < (j + 1) * (32 / T); ++e) {
         const int esb = e / 16, r = e % 16;
@@ -314,9 +339,12 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(const uint16_t* __restrict_
     }
 
     mask(kt + 1, sn);
+  };
 
+  auto phase_b = [&](const char* vc, const f32x16 (&sn)[2],
+                     float& m_new) __attribute__((always_inline)) {
     // Phase B: O^T += V^T P^T(kt), A operand = keys 32 sb + 16 u + 8 rd + 4 h
-    // (0..3) of column d = 32 db + n by two transposing reads, one MFMA ahead;
+    // (0..3) of column d = 32 db + n by two transposing reads, PDB MFMAs ahead;
     // the row max of S^T(kt+1) is spread over it.
     constexpr int NB = (D / 32) * 4;
     // MFMA jb: d block db = jb % (D/32) (fastest, so consecutive MFMAs never
@@ -328,15 +356,16 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(const uint16_t* __restrict_
       const u32x2 hi = lds_read_tr16((const lds_void*)(base + v_off[db][1]));
       return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
     };
-    bf16x8 va = vread(0);
+    bf16x8 vq[PDB];
+#pragma unroll
+    for (int jb = 0; jb < PDB; ++jb) vq[jb] = vread(jb);
     float mx = -__builtin_inff();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int jb = 0; jb < NB; ++jb) {
       const int db = jb % (D / 32), sb = (jb / (D / 32)) >> 1, u = (jb / (D / 32)) & 1;
-      const bf16x8 vcur = va;
-      if (jb + 1 < NB) va = vread(jb + 1);
-      oacc[db] = mfma32(vcur, pb[sb][u], oacc[db]);
+      oacc[db] = mfma32(vq[jb % PDB], pb[sb][u], oacc[db]);
+      if (jb + PDB < NB) vq[jb % PDB] = vread(jb + PDB);
 #pragma unroll
       for (int e = jb * (32 / NB); e < (jb + 1) * (32 / NB); ++e)
         mx = __builtin_fmaxf(mx, sn[e / 16][e % 16]);
@@ -367,14 +396,59 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(const uint16_t* __restrict_
     mask(0, sA);
     row_max(sA, m_new);
   }
-  // Buffers alternate with the tile parity: K(kt+1) in kbuf[(kt+1)&1], V(kt)
-  // in vbuf[kt&1]; the copies go to kbuf[kt&1] and vbuf[(kt+1)&1].
-  int kt = 0;
-  for (; kt + 2 <= ntiles; kt += 2) {
-    body(kt, kbuf1, vbuf0, kbuf0, vbuf1, sA, sB, m_new);
-    body(kt + 1, kbuf0, vbuf1, kbuf1, vbuf0, sB, sA, m_new);
-  }
-  if (kt < ntiles) body(kt, kbuf1, vbuf0, kbuf0, vbuf1, sA, sB, m_new);
+  // Tile kt between barrier kt and barrier kt+1.  At barrier kt, K(kt+1) and
+  // V(kt) are in LDS, and the copies of K(kt+2) and V(kt+1) are issued.  The
+  // leading waves run A(kt), B(kt); with PING the lagging half runs B(kt-1),
+  // A(kt), so on every SIMD one wave's exp2 work runs beside the other's
+  // P V products (their order within each wave is unchanged, so the results
+  // are too).  V(kt-1) is then still being read after barrier kt, which is
+  // why PING keeps four V buffers.
+  auto run = [&](auto lag_flag) __attribute__((always_inline)) {
+    constexpr bool LAG = decltype(lag_flag)::value;
+    auto step = [&](int kt, const char* kn, const char* vc, const char* vp, char* kld, char* vld,
+                    f32x16 (&sv)[2], f32x16 (&sn)[2]) __attribute__((always_inline)) {
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (kt + 2 < ntiles) issue(Kh, kt + 2, kld);
+      if (kt + 1 < ntiles) issue(Vh, kt + 1, vld);
+      // Split-KV: a wave whose 32 rows all lie past the workgroup's rows
+      // (decode groups have fewer rows than waves) only takes its share of
+      // the copies.
+      if constexpr (MODE == kModeSplit)
+        if (qw >= N) return;
+      if constexpr (LAG) {
+        if (kt > 0) phase_b(vp, sv, m_new);
+        phase_a(kt, kn, sv, sn, m_new);
+      } else {
+        phase_a(kt, kn, sv, sn, m_new);
+        phase_b(vc, sn, m_new);
+      }
+    };
+    // K(j) lives in kbuf[j % 2] and V(j) in vbuf[j % 4] (vbuf2, vbuf3 alias
+    // vbuf0, vbuf1 without PING).
+    int kt = 0;
+    for (; kt + 4 <= ntiles; kt += 4) {
+      step(kt, kbuf1, vbuf0, vbuf3, kbuf0, vbuf1, sA, sB);
+      step(kt + 1, kbuf0, vbuf1, vbuf0, kbuf1, vbuf2, sB, sA);
+      step(kt + 2, kbuf1, vbuf2, vbuf1, kbuf0, vbuf3, sA, sB);
+      step(kt + 3, kbuf0, vbuf3, vbuf2, kbuf1, vbuf0, sB, sA);
+    }
+    if (kt < ntiles) step(kt, kbuf1, vbuf0, vbuf3, kbuf0, vbuf1, sA, sB);
+    if (kt + 1 < ntiles) step(kt + 1, kbuf0, vbuf1, vbuf0, kbuf1, vbuf2, sB, sA);
+    if (kt + 2 < ntiles) step(kt + 2, kbuf1, vbuf2, vbuf1, kbuf0, vbuf3, sA, sB);
+    // The lagging waves still owe B(last); its max (of a tile past the end)
+    // is not used.
+    if constexpr (LAG) {
+      if (ntiles > 0) {
+        const int r = (ntiles - 1) & 3;
+        phase_b(r == 0 ? vbuf0 : r == 1 ? vbuf1 : r == 2 ? vbuf2 : vbuf3, sA, m_new);
+      }
+    }
+  };
+  if (lag)
+    run(Flag<true>{});
+  else
+    run(Flag<false>{});
 
   // Final correction: O = O / l, LSE = (m_ref + log2 l) ln 2.  Rows past N are
   // dropped by the buffer range.
@@ -425,7 +499,7 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   p.nqb = (a.N + kFwdBM - 1) / kFwdBM;
   p.c = a.scale * kLog2e;
   const dim3 grid((unsigned)(p.BH * p.nqb));
-  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, POLYQ, kModeDense>), grid, dim3(64 * kFwdWaves), 0, stream,
+  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, POLYQ, kModeDense, kFwdWaves>), grid, dim3(64 * kFwdWaves), 0, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (uint16_t*)a.o, a.lse, p);
   return hipGetLastError();
@@ -521,14 +595,14 @@ __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(const in
 
 template <int D, bool CAUSAL>
 hipError_t launch_fwd_varlen_t(const FwdArgs& a, const VarlenArgs& v, hipStream_t s) {
-  const size_t items_max = (size_t)v.total / kFwdBM + v.B;
+  const size_t items_max = (size_t)v.total / kVarlenBM + v.B;
   char* ws = (char*)v.workspace;
   int* n_items = (int*)ws;
   int* items = (int*)(ws + 256);
   const int max_cost = (v.max_seqlen + kFwdBN - 1) / kFwdBN;
   const size_t shm = (size_t)(max_cost + 1 + kSchedThreads) * sizeof(int);
   hipLaunchKernelGGL((varlen_schedule_kernel<CAUSAL, 0>), dim3(1), dim3(kSchedThreads), shm, s,
-                     v.cu, v.B, v.total, max_cost, 0, kFwdBM, n_items, items);
+                     v.cu, v.B, v.total, max_cost, 0, kVarlenBM, n_items, items);
   FwdParams p;
   p.BH = 0;
   p.Hq = a.Hq;
@@ -541,7 +615,7 @@ hipError_t launch_fwd_varlen_t(const FwdArgs& a, const VarlenArgs& v, hipStream_
   p.n_items = n_items;
   p.total = v.total;
   const dim3 grid((unsigned)(items_max * a.Hq));
-  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, 0, kModeVarlen>), grid, dim3(64 * kFwdWaves), 0, s,
+  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, 0, kModeVarlen, kVarlenWaves>), grid, dim3(64 * kVarlenWaves), 0, s,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (uint16_t*)a.o, a.lse, p);
   return hipGetLastError();
@@ -552,41 +626,73 @@ hipError_t launch_fwd_varlen_t(const FwdArgs& a, const VarlenArgs& v, hipStream_
 // natural-log LSE of key range s and O_s its normalised output,
 // LSE = log sum_s exp(L_s) and O = sum_s exp(L_s - LSE) O_s (an exact
 // re-weighting; ranges a row cannot see have L_s = -inf and weight 0).  One
-// wave per row, D / 64 elements per lane.
+// workgroup of 256 threads per row: thread t owns 4 consecutive elements
+// (t % (D/4)) of the splits s = t / (D/4) + k SG, so every split's row is read
+// by one coalesced sweep and each thread has only splits / SG loads in flight;
+// the SG partial sums meet in LDS.
+constexpr int kMergeThreads = 256;
 template <int D>
-__global__ __launch_bounds__(256) void split_merge_kernel(const float* __restrict__ o_part,
-                                                          const float* __restrict__ l_part,
-                                                          uint16_t* __restrict__ O,
-                                                          float* __restrict__ LSE, int rows_grp,
-                                                          int splits, int rows) {
-  constexpr int EPL = D / 64;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
+__global__ __launch_bounds__(kMergeThreads) void split_merge_kernel(const float* __restrict__ o_part,
+                                                                    const float* __restrict__ l_part,
+                                                                    uint16_t* __restrict__ O,
+                                                                    float* __restrict__ LSE,
+                                                                    int rows_grp, int splits) {
+  constexpr int E4 = D / 4;                  // float4 columns per row
+  constexpr int SG = kMergeThreads / E4;     // split groups
+  __shared__ float4 part[SG][E4];
+  __shared__ float red[kMergeThreads / 64];
+  __shared__ float gsum[SG];
+  const int row = blockIdx.x;
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int grp = row / rows_grp, r = row % rows_grp;
   const size_t base = (size_t)grp * splits * rows_grp + r;   // partial row of split 0
+  // Largest L_s over the splits (-inf if the row saw no key at all).
   float mx = -__builtin_inff();
-  for (int s = 0; s < splits; ++s) mx = fmaxf(mx, l_part[base + (size_t)s * rows_grp]);
-  float acc[EPL];
+  for (int sp = t; sp < splits; sp += kMergeThreads) mx = fmaxf(mx, l_part[base + (size_t)sp * rows_grp]);
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if (lane == 0) red[wv] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const int e4 = t % E4, sg = t / E4;
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
   float sum = 0.f;
-  for (int s = 0; s < splits; ++s) {
-    const float ls = l_part[base + (size_t)s * rows_grp];
+#pragma unroll 4
+  for (int sp = sg; sp < splits; sp += SG) {
+    const size_t pr = base + (size_t)sp * rows_grp;
+    const float ls = l_part[pr];
+    const float4 o = ((const float4*)(o_part + pr * D))[e4];
     const float wgt = (ls == -__builtin_inff()) ? 0.f : __expf(ls - mx);
     sum += wgt;
-    const float* op = o_part + (base + (size_t)s * rows_grp) * D + lane * EPL;
+    acc.x += wgt * o.x;
+    acc.y += wgt * o.y;
+    acc.z += wgt * o.z;
+    acc.w += wgt * o.w;
+  }
+  part[sg][e4] = acc;
+  // Every thread of a split group saw the same weights: the total weight is
+  // the sum of one thread's per group, added in a fixed order.
+  if (e4 == 0) gsum[sg] = sum;
+  __syncthreads();
+  if (sg == 0) {
+    float4 a = part[0][e4];
+    float tot = gsum[0];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] += wgt * op[e];
+    for (int g = 1; g < SG; ++g) {
+      const float4 b = part[g][e4];
+      a.x += b.x;
+      a.y += b.y;
+      a.z += b.z;
+      a.w += b.w;
+      tot += gsum[g];
+    }
+    const float inv = 1.f / tot;
+    u32x2 w;
+    w[0] = pack_bf16x2(a.x * inv, a.y * inv);
+    w[1] = pack_bf16x2(a.z * inv, a.w * inv);
+    *(u32x2*)(O + (size_t)row * D + 4 * e4) = w;
+    if (e4 == 0) LSE[row] = mx + __logf(tot);
   }
-  const float inv = 1.f / sum;
-  uint16_t* orow = O + (size_t)row * D + lane * EPL;
-  if constexpr (EPL == 2) {
-    *(uint32_t*)orow = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-  } else {
-    orow[0] = (uint16_t)(pack_bf16x2(acc[0] * inv, 0.f) & 0xffffu);
-  }
-  if (lane == 0) LSE[row] = mx + __logf(sum);
 }
 
 template <int D, bool CAUSAL>
@@ -599,7 +705,7 @@ hipError_t launch_fwd_split_t(const FwdArgs& a, const SplitArgs& sa, hipStream_t
   p.Hq = a.Hq;
   p.G = G;
   p.N = 0;
-  p.nqb = (M + kFwdBM - 1) / kFwdBM;
+  p.nqb = (M + kSplitBM - 1) / kSplitBM;
   p.c = a.scale * kLog2e;
   p.cu = nullptr;
   p.items = nullptr;
@@ -614,13 +720,13 @@ hipError_t launch_fwd_split_t(const FwdArgs& a, const SplitArgs& sa, hipStream_t
   p.o_part = (float*)ws;
   p.l_part = (float*)(ws + ((rows * sa.splits * D * 4 + 255) & ~(size_t)255));
   const dim3 grid((unsigned)(p.BH * p.nqb * sa.splits));
-  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, 0, kModeSplit>), grid, dim3(64 * kFwdWaves), 0, s,
+  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, 0, kModeSplit, kSplitWaves>), grid, dim3(64 * kSplitWaves), 0, s,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (uint16_t*)a.o, a.lse, p);
   if (sa.splits > 1)
-    hipLaunchKernelGGL((split_merge_kernel<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s,
+    hipLaunchKernelGGL((split_merge_kernel<D>), dim3((unsigned)rows), dim3(kMergeThreads), 0, s,
                        (const float*)p.o_part, (const float*)p.l_part, (uint16_t*)a.o, a.lse, M,
-                       sa.splits, (int)rows);
+                       sa.splits);
   return hipGetLastError();
 }
 
@@ -630,7 +736,7 @@ hipError_t launch_fwd_split_t(const FwdArgs& a, const SplitArgs& sa, hipStream_t
 // (512 on the 256 CUs of an MI355X), without ranges shorter than 4 tiles.
 int split_auto(int B, int Hq, int Hkv, int Nq, int Nk) {
   const int M = (Hq / Hkv) * Nq;
-  const long base = (long)B * Hkv * ((M + kFwdBM - 1) / kFwdBM);
+  const long base = (long)B * Hkv * ((M + kSplitBM - 1) / kSplitBM);
   const int ntiles = (Nk + kFwdBN - 1) / kFwdBN;
   long want = (512 + base - 1) / base;
   const long cap = (ntiles + 3) / 4;
