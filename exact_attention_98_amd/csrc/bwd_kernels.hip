@@ -657,6 +657,380 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Warp-specialized main backward kernel, D = 128 (dense; dQ modes stored and
+// recompute).  Same work item as bwd_main_kernel -- (batch, K/V head, 128-key
+// tile), every query step of every query head of the group -- with 8 waves in
+// two roles over the same step tiles:
+//   score waves 0..3 (keys 32 w): the MFMA unit forms S, dP of step i+1 while
+//     the VALU forms P(i) = exp2(S c - LSE log2 e) and dS(i) = P (dP - Delta);
+//     P(i) and dS(i) go to LDS in MFMA operand order (and, stored mode, dS(i)
+//     to the workspace);
+//   gradient waves 4..7 (keys 32 (w - 4)): dV += P^T dO and dK += dS^T Q of
+//     step i-1, P and dS from that LDS copy, dO^T and Q^T by transposing reads
+//     of the step tile.
+// Waves are dealt to the 4 SIMDs round-robin, so waves w and w + 4 share one:
+// the exp2-heavy score stream and the MFMA-only gradient stream run side by
+// side, and each role needs about half the registers of the single-role
+// kernel, which is what lets two waves live on a SIMD.  One barrier per step.
+// Step tiles rotate through five stages: step i-1 (transposing reads), i (its
+// LSE and Delta), i+1 (row reads), i+2 and i+3 (copies in flight).  Only the
+// gradient waves copy step tiles in; only the score waves store dS.
+template <bool CAUSAL, int DQM>
+__global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, BwdParams p) {
+  constexpr int D = 128;
+  constexpr int NW = 8;
+  constexpr int BN = kBwdBN;
+  constexpr int RB = D * 2;
+  constexpr int KCH = D / 8;
+  constexpr int QS = 32;              // queries per step
+  constexpr int ND = D / 32;          // 32-wide d blocks
+  constexpr int T = D / 16;           // k-steps of S and dP
+  constexpr int TB = QS * RB;         // bytes of one Q (or dO) step tile
+  constexpr int NLD = TB / 1024 / 4;  // 1 KiB direct loads per gradient wave and tensor
+  constexpr bool STORE_DS = DQM == kDqStored;
+  static_assert(NLD >= 1, "step tile too small");
+  static_assert(DQM != kDqAtomic, "atomic dQ uses bwd_main_kernel");
+  constexpr int STAGE = 2 * TB + 512;  // Q, dO, 256 B LSE * log2 e, 256 B Delta
+  constexpr int PSLOT = 4 * 4096;      // P, dS of the 4 score waves
+  __shared__ __attribute__((aligned(1024))) char st0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[STAGE];
+  __shared__ __attribute__((aligned(1024))) char st2[STAGE];
+  __shared__ __attribute__((aligned(1024))) char st3[STAGE];
+  __shared__ __attribute__((aligned(1024))) char st4[STAGE];
+  __shared__ __attribute__((aligned(1024))) char pb0[PSLOT];
+  __shared__ __attribute__((aligned(1024))) char pb1[PSLOT];
+
+  const int Hkv = p.Hq / p.G;
+  const int wg = blockIdx.x;
+  const int bhk = wg % (p.B * Hkv);
+  const int kb = wg / (p.B * Hkv);
+  const int b = bhk / Hkv, hk = bhk % Hkv;
+  const int N = p.N;
+  const int nqs = (N + QS - 1) / QS;
+  const int k0 = kb * BN;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const bool grad = wave >= 4;
+  const int kwave = wave & 3;
+  const int n = lane & 31, h = lane >> 5;
+  const int kw = k0 + 32 * kwave;    // first key of this wave's 32 (uniform)
+  const int key = kw + n;
+  const uint32_t head_bytes = (uint32_t)((size_t)N * D * 2);
+  const size_t kv_head = ((size_t)b * Hkv + hk) * (size_t)N * D;
+
+  // ---- step copies (gradient waves only) ----------------------------------
+  // The score waves issue no loads in the loop, so their only memory traffic,
+  // the stored-dS writes, never delays a wait for a copy: vmcnt counts loads
+  // and stores together, and a store can take long to be acknowledged.
+  // Load s of gradient wave k fills chunks g = (s*4 + k)*64 + lane of a step
+  // tile (row g / KCH, physical chunk g % KCH holding logical chunk
+  // (g % KCH) ^ f(row)).
+  uint32_t ld_off[NLD];
+#pragma unroll
+  for (int s = 0; s < NLD; ++s) {
+    const int g = (s * 4 + kwave) * 64 + lane;
+    const int row = g / KCH, pc = g % KCH;
+    ld_off[s] = (uint32_t)(row * RB + ((pc ^ tile_swz<D>(row)) * 16));
+  }
+  const int qs_first = CAUSAL ? (k0 / QS) : 0;
+  const int per_head = max(nqs - qs_first, 0);
+  const int nsteps = p.G * per_head;
+  const int hq0 = hk * p.G;
+  const uint32_t lse_head_bytes = (uint32_t)N * 4u;
+  const size_t q_hstride = (size_t)N * D * 2;
+  const size_t l_hstride = (size_t)N * 4;
+  const size_t qrow0 = ((size_t)b * p.Hq + hq0) * (size_t)N;
+  int iss_qs = nqs - 1;
+  const char* iss_q = (const char*)(Q + qrow0 * D);
+  const char* iss_do = (const char*)(dO + qrow0 * D);
+  const char* iss_l = (const char*)(p.lse2 + qrow0);
+  const char* iss_d = (const char*)(p.delta + qrow0);
+  auto issue_next = [&](char* st) {
+    const uint32_t base = (uint32_t)iss_qs * (uint32_t)TB;
+    const uint32_t left = head_bytes - base;
+    const rsrc_t qrr = make_rsrc_uniform(iss_q + base, left);
+    const rsrc_t dor = make_rsrc_uniform(iss_do + base, left);
+#pragma unroll
+    for (int s = 0; s < NLD; ++s) {
+      lds_dma16(qrr, (lds_void*)(st + (s * 4 + kwave) * 1024), ld_off[s]);
+      lds_dma16(dor, (lds_void*)(st + TB + (s * 4 + kwave) * 1024), ld_off[s]);
+    }
+    const uint32_t rbase = (uint32_t)iss_qs * (uint32_t)(QS * 4);
+    const uint32_t rleft = lse_head_bytes - rbase;
+    if (wave == 4) lds_dma4(make_rsrc_uniform(iss_l + rbase, rleft), (lds_void*)(st + 2 * TB), lane * 4);
+    if (wave == 5) lds_dma4(make_rsrc_uniform(iss_d + rbase, rleft), (lds_void*)(st + 2 * TB + 256), lane * 4);
+    if (--iss_qs < qs_first) {
+      iss_qs = nqs - 1;
+      iss_q += q_hstride;
+      iss_do += q_hstride;
+      iss_l += l_hstride;
+      iss_d += l_hstride;
+    }
+  };
+  // Gradient waves: at most the newest step's copies still in flight (waves 4
+  // and 5 issue one extra row-constant copy per step; loads complete in order).
+  auto wait_step = [&](bool all) {
+    if (all) {
+      wait_vmcnt<0>();
+    } else if (wave < 6) {
+      wait_vmcnt<2 * NLD + 1>();
+    } else {
+      wait_vmcnt<2 * NLD>();
+    }
+  };
+
+  // Score waves: resident B operands of S = Q K^T and dP = dO V^T (keys past
+  // N read as 0).
+  bf16x8 kB[T], vB[T];
+  if (!grad) {
+    const rsrc_t kr = make_rsrc_uniform(K + kv_head, head_bytes);
+    const rsrc_t vr = make_rsrc_uniform(V + kv_head, head_bytes);
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      kB[t] = as_bf16x8(buf_load16(kr, (uint32_t)(key * RB + 32 * t + 16 * h)));
+      vB[t] = as_bf16x8(buf_load16(vr, (uint32_t)(key * RB + 32 * t + 16 * h)));
+    }
+  }
+  if (nsteps > 0 && grad) {
+    issue_next(st0);
+    if (nsteps > 1) issue_next(st1);
+    if (nsteps > 2) issue_next(st2);
+    if (nsteps > 2) {
+      if (wave < 6) wait_vmcnt<4 * NLD + 2>();
+      else wait_vmcnt<4 * NLD>();
+    } else {
+      wait_vmcnt<0>();
+    }
+  }
+  __syncthreads();
+
+  if (!grad) {
+    // ======================= score waves =======================
+    // Row-major A operand (Q of S, dO of dP): row n, logical chunk 2t + h.
+    uint32_t a_off[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) a_off[t] = (uint32_t)(n * RB + (((2 * t + h) ^ tile_swz<D>(n)) * 16));
+
+    int cur_qs = nqs - 1, cur_g = 0;
+    int prev_qs = 0, prev_g = 0;
+    u32x4 ds_keep[2];
+    const int kb32 = kw / 32;
+    const uint32_t ds_lane = (uint32_t)(n * 64 + h * 16);
+    auto store_ds = [&](int g, int qs) {
+      if constexpr (STORE_DS) {
+        const rsrc_t r = make_rsrc_uniform(p.ds + ((size_t)b * p.Hq + hq0 + g) * p.ds_head, p.ds_head);
+        const bool ok = qs < p.nb32 && kb32 < p.nb32 && (!CAUSAL || kb32 <= qs);
+        const uint32_t off = ok ? (uint32_t)(qs * p.nb32 + kb32) * 2048u : 0xFFFFF000u;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          __builtin_amdgcn_raw_buffer_store_b128(ds_keep[u], r, off + ds_lane + 32u * u, 0, 0);
+      }
+    };
+
+    f32x16 sA, dA, sB, dB;
+    if (nsteps > 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sA[r] = 0.f;
+        dA[r] = 0.f;
+      }
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        sA = mfma32(as_bf16x8(*(const u32x4*)(st0 + a_off[t])), kB[t], sA);
+        dA = mfma32(as_bf16x8(*(const u32x4*)(st0 + TB + a_off[t])), vB[t], dA);
+      }
+    }
+
+    // Iteration i: S(i+1), dP(i+1) from stage `nxt`; P(i), dS(i) from sv, dv
+    // with step i's LSE and Delta in stage `cur`; P, dS to `pbw`.
+    auto body = [&](int i, const char* cur, const char* nxt, char* pbw, f32x16& sv, f32x16& dv,
+                    f32x16& sn, f32x16& dn) __attribute__((always_inline)) {
+      __syncthreads();
+      if (STORE_DS && i > 0 && i <= nsteps) store_ds(prev_g, prev_qs);
+      if (i >= nsteps) return;
+      const int q0 = cur_qs * QS;
+      pin(sv);
+      pin(dv);
+      // Causal mask near the diagonal (S = -inf where key > query) and
+      // padding keys (key >= N).  Register r holds query q0 + 8(r/4) + 4h + r%4.
+      if ((CAUSAL && (q0 < kw + 31)) || (kw + 32 > N)) {
+        keep_branch();
+        const int lim = (key >= N) ? 1 << 30 : (CAUSAL ? key - q0 - 4 * h : -1);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (8 * (r >> 2) + (r & 3) < lim) sv[r] = -__builtin_inff();
+      }
+      f32x4 lc[4], dc[4];
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        lc[r4] = *(const f32x4*)((const float*)(cur + 2 * TB) + 8 * r4 + 4 * h);
+        dc[r4] = *(const f32x4*)((const float*)(cur + 2 * TB + 256) + 8 * r4 + 4 * h);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sn[r] = 0.f;
+        dn[r] = 0.f;
+      }
+      constexpr int PD = 2;  // operand read distance, in MFMA pairs
+      bf16x8 opA[T], opB[T];
+      auto fetch = [&](int c) {
+        if (c < T) {
+          opA[c] = as_bf16x8(*(const u32x4*)(nxt + a_off[c]));
+          opB[c] = as_bf16x8(*(const u32x4*)(nxt + TB + a_off[c]));
+        }
+      };
+#pragma unroll
+      for (int c = 0; c < PD; ++c) fetch(c);
+      char* pw = pbw + kwave * 4096 + lane * 16;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < T; ++j) {
+        fetch(j + PD);
+        sn = mfma32(opA[j], kB[j], sn);
+        dn = mfma32(opB[j], vB[j], dn);
+#pragma unroll
+        for (int r = 2 * j; r < 2 * j + 2; ++r) {
+          const float pv = exp2_hw(__builtin_fmaf(sv[r], p.c, -lc[r >> 2][r & 3]));
+          sv[r] = pv;
+          dv[r] = pv * (dv[r] - dc[r >> 2][r & 3]);
+          if ((r & 7) == 7) {
+            const int u = r >> 3;
+            u32x4 w1, w2;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+              w1[m] = pack_bf16x2(sv[8 * u + 2 * m], sv[8 * u + 2 * m + 1]);
+              w2[m] = pack_bf16x2(dv[8 * u + 2 * m], dv[8 * u + 2 * m + 1]);
+            }
+            *(u32x4*)(pw + u * 1024) = w1;
+            *(u32x4*)(pw + (2 + u) * 1024) = w2;
+            if constexpr (STORE_DS) ds_keep[u] = w2;
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      prev_qs = cur_qs;
+      prev_g = cur_g;
+      if (--cur_qs < qs_first) {
+        cur_qs = nqs - 1;
+        ++cur_g;
+      }
+    };
+    // Stages rotate with period 5, P/dS slots and S/dP register sets with 2.
+    // Groups of 10 iterations run whole (iterations past nsteps only meet the
+    // barrier): conditional exits between bodies make the register allocator
+    // copy the accumulators.
+    for (int i = 0; i <= nsteps && nsteps > 0; i += 10) {
+      body(i, st0, st1, pb0, sA, dA, sB, dB);
+      body(i + 1, st1, st2, pb1, sB, dB, sA, dA);
+      body(i + 2, st2, st3, pb0, sA, dA, sB, dB);
+      body(i + 3, st3, st4, pb1, sB, dB, sA, dA);
+      body(i + 4, st4, st0, pb0, sA, dA, sB, dB);
+      body(i + 5, st0, st1, pb1, sB, dB, sA, dA);
+      body(i + 6, st1, st2, pb0, sA, dA, sB, dB);
+      body(i + 7, st2, st3, pb1, sB, dB, sA, dA);
+      body(i + 8, st3, st4, pb0, sA, dA, sB, dB);
+      body(i + 9, st4, st0, pb1, sB, dB, sA, dA);
+    }
+  } else {
+    // ======================= gradient waves =======================
+    f32x16 dk_acc[ND], dv_acc[ND];
+#pragma unroll
+    for (int i = 0; i < ND; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        dk_acc[i][r] = 0.f;
+        dv_acc[i][r] = 0.f;
+      }
+    // Transposing B-operand reads of dO / Q (queries 16 u + 8 rd + 4 h + 0..3
+    // of column d = 32 db + n): lane j of 16-lane group gq points at row
+    // 8 rd + 4 h + j/4 and d = 32 db + 16 (gq & 1) + 4 (j & 3).
+    const int tj = lane & 15, gq = lane >> 4;
+    uint32_t tr_off[ND][2];
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) {
+      const int row = 8 * rd + 4 * h + (tj >> 2);
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+        const int c = 4 * db + 2 * (gq & 1) + ((tj & 3) >> 1);
+        tr_off[db][rd] = (uint32_t)(row * RB + ((c ^ tile_swz<D>(row)) * 16) + (tj & 1) * 8);
+      }
+    }
+    // Iteration i: dV, dK of step i-1 (tile `prv`, P and dS in `pbr`).
+    auto body = [&](int i, const char* prv, const char* pbr, char* ld) __attribute__((always_inline)) {
+      wait_step(i + 2 >= nsteps);
+      __syncthreads();
+      if (i + 3 < nsteps) issue_next(ld);
+      if (i == 0 || i > nsteps) return;
+      const char* pr = pbr + kwave * 4096 + lane * 16;
+      bf16x8 pa[2], dsa[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        pa[u] = as_bf16x8(*(const u32x4*)(pr + u * 1024));
+        dsa[u] = as_bf16x8(*(const u32x4*)(pr + (2 + u) * 1024));
+      }
+      constexpr int NB = 2 * ND;  // MFMA pairs: (u, db), db fastest
+      constexpr int PD = 2;
+      bf16x8 opA[NB], opB[NB];
+      auto fetch = [&](int jb) {
+        if (jb < NB) {
+          const int u = jb / ND, db = jb % ND;
+          const int roff = 16 * u * RB;
+          const u32x2 olo = lds_read_tr16((const lds_void*)(prv + TB + roff + tr_off[db][0]));
+          const u32x2 ohi = lds_read_tr16((const lds_void*)(prv + TB + roff + tr_off[db][1]));
+          const u32x2 qlo = lds_read_tr16((const lds_void*)(prv + roff + tr_off[db][0]));
+          const u32x2 qhi = lds_read_tr16((const lds_void*)(prv + roff + tr_off[db][1]));
+          opA[jb] = as_bf16x8(u32x4{olo[0], olo[1], ohi[0], ohi[1]});
+          opB[jb] = as_bf16x8(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]});
+        }
+      };
+#pragma unroll
+      for (int c = 0; c < PD; ++c) fetch(c);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int jb = 0; jb < NB; ++jb) {
+        const int u = jb / ND, db = jb % ND;
+        fetch(jb + PD);
+        dv_acc[db] = mfma32(pa[u], opA[jb], dv_acc[db]);
+        dk_acc[db] = mfma32(dsa[u], opB[jb], dk_acc[db]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // Step i-1's tile is in stage (i-1) mod 5, its P and dS in slot (i-1) mod 2.
+    for (int i = 0; i <= nsteps && nsteps > 0; i += 10) {
+      body(i, st4, pb1, st3);
+      body(i + 1, st0, pb0, st4);
+      body(i + 2, st1, pb1, st0);
+      body(i + 3, st2, pb0, st1);
+      body(i + 4, st3, pb1, st2);
+      body(i + 5, st4, pb0, st3);
+      body(i + 6, st0, pb1, st4);
+      body(i + 7, st1, pb0, st0);
+      body(i + 8, st2, pb1, st1);
+      body(i + 9, st3, pb0, st2);
+    }
+    // dK (scaled) and dV of this wave's 32 keys.  Register r of d-block db:
+    // key kw + 8(r/4) + 4h + r%4, d = 32 db + n.
+    uint16_t* dKh = dK + kv_head;
+    uint16_t* dVh = dV + kv_head;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int krow = kw + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (krow < N) {
+          const size_t off = (size_t)krow * D + 32 * db + n;
+          dKh[off] = (uint16_t)(pack_bf16x2(dk_acc[db][r] * p.scale, 0.f) & 0xffffu);
+          dVh[off] = (uint16_t)(pack_bf16x2(dv_acc[db][r], 0.f) & 0xffffu);
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Fixed-order dQ kernel.  Workgroup = (batch, query head, 128 queries), 4
 // waves of 32 queries.  K/V tiles of 64 keys are copied straight into LDS
 // (double-buffered, one barrier per tile) and walked in ascending order:
@@ -1063,9 +1437,25 @@ hipError_t launch_pre_d(const BwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// D = 128 in the fixed-order dQ modes: the warp-specialized kernel.
+constexpr bool kBwdSplitRoles = true;
+template <bool CAUSAL, int DQM>
+hipError_t launch_ws_t(const BwdArgs& a, const BwdParams& p, hipStream_t s) {
+  const dim3 grid((unsigned)(a.B * a.Hkv * p.nkb));
+  hipLaunchKernelGGL((bwd_ws_kernel<CAUSAL, DQM>), grid, dim3(512), 0, s, (const uint16_t*)a.q,
+                     (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
+                     (uint16_t*)a.dk, (uint16_t*)a.dv, p);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_main_d(const BwdArgs& a, hipStream_t s) {
   const BwdParams p = make_params(a);
+  if (kBwdSplitRoles && D == 128 && a.deterministic != kDqAtomic) {
+    if (a.deterministic == kDqStored)
+      return a.causal ? launch_ws_t<true, kDqStored>(a, p, s) : launch_ws_t<false, kDqStored>(a, p, s);
+    return a.causal ? launch_ws_t<true, kDqRecompute>(a, p, s) : launch_ws_t<false, kDqRecompute>(a, p, s);
+  }
   switch (a.deterministic) {
     case kDqAtomic:
       return a.causal ? launch_bwd_t<D, true, kDqAtomic>(a, p, s) : launch_bwd_t<D, false, kDqAtomic>(a, p, s);

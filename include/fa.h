@@ -161,7 +161,7 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, voi
  *   workspace: device memory of fa_fwd_varlen_workspace_size(B, total)
  *     bytes, 256-byte aligned, caller-owned scratch for the work list.
  * The work is scheduled on the device, without a host round trip: a first
- * kernel lists every (sequence, 256-query tile) and sorts the list by the
+ * kernel lists every (sequence, 128-query tile) and sorts the list by the
  * number of K/V tiles each item processes, largest first (danialwang
  * explainer, section 06, starting the longest work first); the attention
  * kernel takes items in that order.  total = 0 is valid and writes nothing.
