@@ -672,9 +672,10 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
 // the exp2-heavy score stream and the MFMA-only gradient stream run side by
 // side, and each role needs about half the registers of the single-role
 // kernel, which is what lets two waves live on a SIMD.  One barrier per step.
-// Step tiles rotate through five stages: step i-1 (transposing reads), i (its
-// LSE and Delta), i+1 (row reads), i+2 and i+3 (copies in flight).  Only the
-// gradient waves copy step tiles in; only the score waves store dS.
+// Step tiles rotate through six stages: step i-1 (transposing reads), i (its
+// LSE and Delta), i+1 (row reads), i+2 .. i+4 (copies in flight, three steps
+// of latency hidden).  Only the gradient waves copy step tiles in; only the
+// score waves store dS.
 template <bool CAUSAL, int DQM>
 __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -700,6 +701,7 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
   __shared__ __attribute__((aligned(1024))) char st2[STAGE];
   __shared__ __attribute__((aligned(1024))) char st3[STAGE];
   __shared__ __attribute__((aligned(1024))) char st4[STAGE];
+  __shared__ __attribute__((aligned(1024))) char st5[STAGE];
   __shared__ __attribute__((aligned(1024))) char pb0[PSLOT];
   __shared__ __attribute__((aligned(1024))) char pb1[PSLOT];
 
@@ -771,15 +773,18 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
       iss_d += l_hstride;
     }
   };
-  // Gradient waves: at most the newest step's copies still in flight (waves 4
-  // and 5 issue one extra row-constant copy per step; loads complete in order).
-  auto wait_step = [&](bool all) {
-    if (all) {
-      wait_vmcnt<0>();
-    } else if (wave < 6) {
-      wait_vmcnt<2 * NLD + 1>();
+  // Gradient waves at iteration i: step i+1's copies complete, those of steps
+  // i+2 and i+3 may still be in flight (waves 4 and 5 issue one extra
+  // row-constant copy per step; loads complete in order).
+  auto wait_step = [&](int i) {
+    if (i + 3 < nsteps) {
+      if (wave < 6) wait_vmcnt<2 * (2 * NLD + 1)>();
+      else wait_vmcnt<2 * (2 * NLD)>();
+    } else if (i + 2 < nsteps) {
+      if (wave < 6) wait_vmcnt<2 * NLD + 1>();
+      else wait_vmcnt<2 * NLD>();
     } else {
-      wait_vmcnt<2 * NLD>();
+      wait_vmcnt<0>();
     }
   };
 
@@ -799,9 +804,11 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
     issue_next(st0);
     if (nsteps > 1) issue_next(st1);
     if (nsteps > 2) issue_next(st2);
-    if (nsteps > 2) {
-      if (wave < 6) wait_vmcnt<4 * NLD + 2>();
-      else wait_vmcnt<4 * NLD>();
+    if (nsteps > 3) issue_next(st3);
+    // Step 0 complete; steps 1..3 may be in flight.
+    if (nsteps > 3) {
+      if (wave < 6) wait_vmcnt<3 * (2 * NLD + 1)>();
+      else wait_vmcnt<3 * (2 * NLD)>();
     } else {
       wait_vmcnt<0>();
     }
@@ -919,21 +926,17 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
         ++cur_g;
       }
     };
-    // Stages rotate with period 5, P/dS slots and S/dP register sets with 2.
-    // Groups of 10 iterations run whole (iterations past nsteps only meet the
+    // Stages rotate with period 6, P/dS slots and S/dP register sets with 2.
+    // Groups of 6 iterations run whole (iterations past nsteps only meet the
     // barrier): conditional exits between bodies make the register allocator
     // copy the accumulators.
-    for (int i = 0; i <= nsteps && nsteps > 0; i += 10) {
+    for (int i = 0; i <= nsteps && nsteps > 0; i += 6) {
       body(i, st0, st1, pb0, sA, dA, sB, dB);
       body(i + 1, st1, st2, pb1, sB, dB, sA, dA);
       body(i + 2, st2, st3, pb0, sA, dA, sB, dB);
       body(i + 3, st3, st4, pb1, sB, dB, sA, dA);
-      body(i + 4, st4, st0, pb0, sA, dA, sB, dB);
-      body(i + 5, st0, st1, pb1, sB, dB, sA, dA);
-      body(i + 6, st1, st2, pb0, sA, dA, sB, dB);
-      body(i + 7, st2, st3, pb1, sB, dB, sA, dA);
-      body(i + 8, st3, st4, pb0, sA, dA, sB, dB);
-      body(i + 9, st4, st0, pb1, sB, dB, sA, dA);
+      body(i + 4, st4, st5, pb0, sA, dA, sB, dB);
+      body(i + 5, st5, st0, pb1, sB, dB, sA, dA);
     }
   } else {
     // ======================= gradient waves =======================
@@ -961,9 +964,9 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
     }
     // Iteration i: dV, dK of step i-1 (tile `prv`, P and dS in `pbr`).
     auto body = [&](int i, const char* prv, const char* pbr, char* ld) __attribute__((always_inline)) {
-      wait_step(i + 2 >= nsteps);
+      wait_step(i);
       __syncthreads();
-      if (i + 3 < nsteps) issue_next(ld);
+      if (i + 4 < nsteps) issue_next(ld);
       if (i == 0 || i > nsteps) return;
       const char* pr = pbr + kwave * 4096 + lane * 16;
       bf16x8 pa[2], dsa[2];
@@ -999,18 +1002,15 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    // Step i-1's tile is in stage (i-1) mod 5, its P and dS in slot (i-1) mod 2.
-    for (int i = 0; i <= nsteps && nsteps > 0; i += 10) {
-      body(i, st4, pb1, st3);
-      body(i + 1, st0, pb0, st4);
+    // Step i-1's tile is in stage (i-1) mod 6, its P and dS in slot (i-1) mod 2;
+    // step i+4 is copied into stage (i+4) mod 6.
+    for (int i = 0; i <= nsteps && nsteps > 0; i += 6) {
+      body(i, st5, pb1, st4);
+      body(i + 1, st0, pb0, st5);
       body(i + 2, st1, pb1, st0);
       body(i + 3, st2, pb0, st1);
       body(i + 4, st3, pb1, st2);
       body(i + 5, st4, pb0, st3);
-      body(i + 6, st0, pb1, st4);
-      body(i + 7, st1, pb0, st0);
-      body(i + 8, st2, pb1, st1);
-      body(i + 9, st3, pb0, st2);
     }
     // dK (scaled) and dV of this wave's 32 keys.  Register r of d-block db:
     // key kw + 8(r/4) + 4h + r%4, d = 32 db + n.
