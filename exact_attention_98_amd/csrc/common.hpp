@@ -170,4 +170,10 @@ __device__ __forceinline__ float exp2_poly(float x) {
   return x < -127.0f ? 0.0f : __builtin_bit_cast(float, bits);
 }
 
+// Compile-time bool for generic lambdas (one instantiation per value).
+template <bool V>
+struct Flag {
+  static constexpr bool value = V;
+};
+
 }  // namespace fa

@@ -29,7 +29,11 @@
 namespace fa {
 namespace {
 
-constexpr int kF8BM = 128, kF8BN = 64, kF8Waves = 4, kQT = 64;   // kQT: quantization tile rows
+constexpr int kF8BN = 64, kQT = 64;   // kQT: quantization tile rows
+// Waves per workgroup (32 queries each): 8 at D = 128 (two per SIMD, ping-pong
+// below), 4 at D = 64 (a tile copy then still has a 1 KiB share per wave).
+template <int D>
+constexpr int f8_waves() { return D == 128 ? 8 : 4; }
 constexpr float kE4M3Max = 448.f;
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -171,14 +175,16 @@ __global__ __launch_bounds__(64) void fp8_quant_kernel(const uint16_t* __restric
 // holds chunk c at c ^ ((r >> 2) & 3).  Both make the 16 lanes of a
 // 16-byte read hit 16 distinct bank groups.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(uint16_t* __restrict__ O,
-                                                         float* __restrict__ LSE, Fp8Layout L,
-                                                         int Hq, int G, int nqb, float c) {
-  constexpr int BM = kF8BM, BN = kF8BN;
+__global__ __launch_bounds__(64 * f8_waves<D>(), 8 / f8_waves<D>()) void fwd_fp8_kernel(
+    uint16_t* __restrict__ O, float* __restrict__ LSE, Fp8Layout L, int Hq, int G, int nqb,
+    float c) {
+  constexpr int NW = f8_waves<D>();
+  constexpr bool PING = NW == 8;
+  constexpr int BM = 32 * NW, BN = kF8BN;
   constexpr int CH = D / 16;                 // 16-byte chunks per K row
   constexpr int TBK = BN * D;                // bytes of a K tile
   constexpr int TBV = D * BN;                // bytes of a V^T tile
-  constexpr int NLD = TBK / 1024 / kF8Waves; // 1 KiB copies per wave per tile
+  constexpr int NLD = TBK / 1024 / NW;       // 1 KiB copies per wave per tile
   constexpr int KT = D / 64;                 // k-steps of S^T
   constexpr int ND = D / 32;                 // 32-row d blocks of O^T
   constexpr int SH = D == 128 ? 1 : 2;
@@ -187,7 +193,12 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(uint16_t* __restrict__ 
   __shared__ __attribute__((aligned(1024))) char kbuf1[TBK];
   __shared__ __attribute__((aligned(1024))) char vbuf0[TBV];
   __shared__ __attribute__((aligned(1024))) char vbuf1[TBV];
-  auto fk = [](int r) { return (r >> SH) & (CH - 1); };
+  // Ping-pong (8 waves): V(kt-1) is still read after barrier kt, so V is
+  // four-deep.
+  __shared__ __attribute__((aligned(1024))) char vbuf2_[PING ? TBV : 1024];
+  __shared__ __attribute__((aligned(1024))) char vbuf3_[PING ? TBV : 1024];
+  char* const vbuf2 = PING ? vbuf2_ : vbuf0;
+  char* const vbuf3 = PING ? vbuf3_ : vbuf1;  auto fk = [](int r) { return (r >> SH) & (CH - 1); };
   auto fv = [](int r) { return (r >> 2) & 3; };
 
   const int BH = L.BHq;
@@ -205,6 +216,8 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(uint16_t* __restrict__ 
   const int q0 = qb * BM;
   const int qw = q0 + wave * 32;
   const int qi = qw + n;
+  // Lagging half of the ping-pong: waves 4..7 (wave w runs on SIMD w % 4).
+  const bool lag = PING && wave >= NW / 2;
 
   // Q fragments: k-step t holds bytes 64t + 32h .. +32 of row qi (B operand).
   const rsrc_t qr = make_rsrc_uniform(L.q8 + (size_t)bh * L.Np * D, (uint32_t)((size_t)L.Np * D));
@@ -231,11 +244,11 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(uint16_t* __restrict__ 
   const int kend = CAUSAL ? min(N, q0 + BM) : N;
   const int ntiles = (kend + BN - 1) / BN;
 
-  // Copies: chunk g = (s*4 + wave)*64 + lane of a tile.
+  // Copies: chunk g = (s*NW + wave)*64 + lane of a tile.
   uint32_t kld_off[NLD], vld_off[NLD];
 #pragma unroll
   for (int s = 0; s < NLD; ++s) {
-    const int g = (s * kF8Waves + wave) * 64 + lane;
+    const int g = (s * NW + wave) * 64 + lane;
     kld_off[s] = (uint32_t)((g / CH) * D + (((g % CH) ^ fk(g / CH)) * 16));
     vld_off[s] = (uint32_t)((g / 4) * 64 + (((g % 4) ^ fv(g / 4)) * 16));
   }
@@ -244,12 +257,12 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(uint16_t* __restrict__ 
   auto issue_k = [&](int kt, char* dst) {
     const rsrc_t r = make_rsrc_uniform(k8h + (size_t)kt * TBK, (uint32_t)TBK);
 #pragma unroll
-    for (int s = 0; s < NLD; ++s) lds_dma16(r, (lds_void*)(dst + (s * kF8Waves + wave) * 1024), kld_off[s]);
+    for (int s = 0; s < NLD; ++s) lds_dma16(r, (lds_void*)(dst + (s * NW + wave) * 1024), kld_off[s]);
   };
   auto issue_v = [&](int kt, char* dst) {
     const rsrc_t r = make_rsrc_uniform(v8h + (size_t)kt * TBV, (uint32_t)TBV);
 #pragma unroll
-    for (int s = 0; s < NLD; ++s) lds_dma16(r, (lds_void*)(dst + (s * kF8Waves + wave) * 1024), vld_off[s]);
+    for (int s = 0; s < NLD; ++s) lds_dma16(r, (lds_void*)(dst + (s * NW + wave) * 1024), vld_off[s]);
   };
   // LDS read offsets.  K (A operand of S^T): row n (+32 sb), logical chunks
   // 4t + 2h + u.  V^T (A operand of O^T): row n (+32 db), chunks 2h + u.
@@ -301,23 +314,22 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(uint16_t* __restrict__ 
     }
   };
 
-  auto body = [&](int kt, const char* kn, const char* vc, char* kld, char* vld, f32x16 (&sv)[2],
-                  f32x16 (&sn)[2], float& m_new) {
-    wait_vmcnt<0>();
-    __syncthreads();  // K(kt+1), V(kt) in LDS; tile kt-1's buffers are free
-    if (kt + 2 < ntiles) issue_k(kt + 2, kld);
-    if (kt + 1 < ntiles) issue_v(kt + 1, vld);
+  // Phase A(kt): S^T(kt+1) on the MFMA unit while the VALU forms
+  // e4m3(256 P(kt)) into pb; phase B(kt): O^T += V^T P^T(kt) with the row max
+  // of S^T(kt+1).  The row sum l_part accumulates 256 P (exact power-of-two
+  // scale, undone at the end), so 256 is folded into the exp2 argument.
+  v8i pb;
+  auto phase_a = [&](int kt, const char* kn, f32x16 (&sv)[2], f32x16 (&sn)[2],
+                     float m_new) __attribute__((always_inline)) {
     rescale(m_new);
-    const float msub = (m_ref == -__builtin_inff()) ? 0.f : m_ref;
+    const float msub8 = 8.f - ((m_ref == -__builtin_inff()) ? 0.f : m_ref);
     const float ct = cq * ksc[kt];
-    const float cn = cq * ksc[min(kt + 1, ntiles - 1)];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sn[sb][r] = 0.f;
-    // Phase A: the 2 KT MFMAs of S^T(kt+1) (sub-blocks alternate), each with
-    // 16 / KT elements of P(kt): exp2, row sum, e4m3(256 P) into the B operand.
-    v8i pb;
+    // The 2 KT MFMAs of S^T(kt+1) (sub-blocks alternate), each with 16 / KT
+    // elements of P(kt): exp2, row sum, e4m3 into the B operand.
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < 2 * KT; ++j) {
@@ -331,18 +343,21 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(uint16_t* __restrict__ 
         float pv[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          pv[q] = exp2_hw(__builtin_fmaf(sv[esb][r + q], ct, -msub));
+          pv[q] = exp2_hw(__builtin_fmaf(sv[esb][r + q], ct, msub8));
           l_part += pv[q];
         }
-        pb[e >> 2] = (int)cvt_fp8x4(pv[0] * 256.f, pv[1] * 256.f, pv[2] * 256.f, pv[3] * 256.f);
+        pb[e >> 2] = (int)cvt_fp8x4(pv[0], pv[1], pv[2], pv[3]);
       }
       pin(l_part);
       __builtin_amdgcn_sched_barrier(0);
     }
     mask(kt + 1, sn);
-    // Phase B: O^T += V^T P^T (V block scale 2^e, P block scale 2^-8), with
-    // the row max of S^T(kt+1) spread over it.
+  };
+  auto phase_b = [&](int kt, const char* vc, const f32x16 (&sn)[2],
+                     float& m_new) __attribute__((always_inline)) {
+    // V block scale 2^e, P block scale 2^-8.
     const int sa = 127 + vex[kt];
+    const float cn = cq * ksc[min(kt + 1, ntiles - 1)];
     float mx = -__builtin_inff();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -380,16 +395,55 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(uint16_t* __restrict__ 
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sA[sb][r]);
     m_new = fmaxf(m_ref, xhalf_max(mx) * cq * ksc[0]);
   }
-  int kt = 0;
-  for (; kt + 2 <= ntiles; kt += 2) {
-    body(kt, kbuf1, vbuf0, kbuf0, vbuf1, sA, sB, m_new);
-    body(kt + 1, kbuf0, vbuf1, kbuf1, vbuf0, sB, sA, m_new);
-  }
-  if (kt < ntiles) body(kt, kbuf1, vbuf0, kbuf0, vbuf1, sA, sB, m_new);
+  // Tile kt between barrier kt and barrier kt+1: at barrier kt, K(kt+1) and
+  // V(kt) are in LDS and the copies of K(kt+2), V(kt+1) are issued.  Leading
+  // waves run A(kt), B(kt); with PING the lagging half runs B(kt-1), A(kt),
+  // so on each SIMD one wave's exp2 work runs beside the other's products
+  // (each wave's own order, and so its results, are unchanged).
+  auto run = [&](auto lag_flag) __attribute__((always_inline)) {
+    constexpr bool LAG = decltype(lag_flag)::value;
+    auto step = [&](int kt, const char* kn, const char* vc, const char* vp, char* kld, char* vld,
+                    f32x16 (&sv)[2], f32x16 (&sn)[2]) __attribute__((always_inline)) {
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (kt + 2 < ntiles) issue_k(kt + 2, kld);
+      if (kt + 1 < ntiles) issue_v(kt + 1, vld);
+      if constexpr (LAG) {
+        if (kt > 0) phase_b(kt - 1, vp, sv, m_new);
+        phase_a(kt, kn, sv, sn, m_new);
+      } else {
+        phase_a(kt, kn, sv, sn, m_new);
+        phase_b(kt, vc, sn, m_new);
+      }
+    };
+    // K(j) in kbuf[j % 2], V(j) in vbuf[j % 4] (vbuf2, vbuf3 alias vbuf0,
+    // vbuf1 without PING).
+    int kt = 0;
+    for (; kt + 4 <= ntiles; kt += 4) {
+      step(kt, kbuf1, vbuf0, vbuf3, kbuf0, vbuf1, sA, sB);
+      step(kt + 1, kbuf0, vbuf1, vbuf0, kbuf1, vbuf2, sB, sA);
+      step(kt + 2, kbuf1, vbuf2, vbuf1, kbuf0, vbuf3, sA, sB);
+      step(kt + 3, kbuf0, vbuf3, vbuf2, kbuf1, vbuf0, sB, sA);
+    }
+    if (kt < ntiles) step(kt, kbuf1, vbuf0, vbuf3, kbuf0, vbuf1, sA, sB);
+    if (kt + 1 < ntiles) step(kt + 1, kbuf0, vbuf1, vbuf0, kbuf1, vbuf2, sB, sA);
+    if (kt + 2 < ntiles) step(kt + 2, kbuf1, vbuf2, vbuf1, kbuf0, vbuf3, sA, sB);
+    // The lagging waves still owe B(last); its max is not used.
+    if constexpr (LAG) {
+      if (ntiles > 0) {
+        const int r = (ntiles - 1) & 3;
+        phase_b(ntiles - 1, r == 0 ? vbuf0 : r == 1 ? vbuf1 : r == 2 ? vbuf2 : vbuf3, sA, m_new);
+      }
+    }
+  };
+  if (lag)
+    run(Flag<true>{});
+  else
+    run(Flag<false>{});
 
-  // O = O / l (bf16), LSE = (m_ref + log2 l) ln 2.
+  // O = O / l (bf16), LSE = (m_ref + log2 l) ln 2, with l = l_part / 256.
   const float l_tot = xhalf_sum(l_part);
-  const float inv = 1.f / l_tot;
+  const float inv = 256.f / l_tot;
   const uint32_t head_bytes = (uint32_t)((size_t)N * D * 2);
   const rsrc_t orr = make_rsrc_uniform(O + (size_t)bh * N * D, head_bytes);
 #pragma unroll
@@ -401,7 +455,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(uint16_t* __restrict__ 
       w[1] = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
       buf_store8(orr, (uint32_t)(qi * D * 2 + (32 * db + 8 * g + 4 * h) * 2), w);
     }
-  if (h == 0 && qi < N) LSE[(size_t)bh * N + qi] = (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2;
+  if (h == 0 && qi < N) LSE[(size_t)bh * N + qi] = (m_ref + __builtin_amdgcn_logf(l_tot) - 8.f) * kLn2;
 }
 
 template <int D, bool CAUSAL>
@@ -409,9 +463,10 @@ hipError_t launch_fp8_t(const FwdArgs& a, const float* signs, const Fp8Layout& L
   const int items = (L.BHq + 2 * L.BHkv) * L.nt;
   hipLaunchKernelGGL((fp8_quant_kernel<D>), dim3((unsigned)items), dim3(64), 0, s,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, signs, L);
-  const int nqb = (a.N + kF8BM - 1) / kF8BM;
+  constexpr int BM = 32 * f8_waves<D>();
+  const int nqb = (a.N + BM - 1) / BM;
   hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL>), dim3((unsigned)(L.BHq * nqb)),
-                     dim3(64 * kF8Waves), 0, s, (uint16_t*)a.o, a.lse, L, a.Hq, a.Hq / a.Hkv, nqb,
+                     dim3(64 * f8_waves<D>()), 0, s, (uint16_t*)a.o, a.lse, L, a.Hq, a.Hq / a.Hkv, nqb,
                      a.scale * kLog2e);
   return hipGetLastError();
 }

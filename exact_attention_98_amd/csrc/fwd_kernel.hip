@@ -46,11 +46,6 @@ constexpr int kVarlenBM = 32 * kVarlenWaves;
 constexpr int kSplitBM = 32 * kSplitWaves;
 constexpr int kFwdBN = 64;       // keys per K/V tile
 
-template <bool V>
-struct Flag {
-  static constexpr bool value = V;
-};
-
 // Addressing modes of the forward kernel.
 constexpr int kModeDense = 0;   // [B][H][N][D], one workgroup per (b, hq, query tile)
 constexpr int kModeVarlen = 1;  // packed sequences, work list sorted longest first
