@@ -136,6 +136,107 @@ def bench_varlen(fa, torch, dev, stream, reps: int = 20) -> dict:
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
 
 
+def bench_varlen_bwd(fa, torch, dev, stream, det: int = 2, reps: int = 10) -> dict:
+    """Variable-length backward (fa_bwd_varlen: preprocess, both work lists,
+    dK/dV and dQ passes) on the packed workload of synth.VARLEN, dQ mode det
+    (2: fixed order, deterministic; the stored-dS mode has no variable-length
+    form)."""
+    import synth
+    w = synth.VARLEN
+    lens = synth.varlen_lengths(w["n_seqs"], w["total"], w["lo"], w["hi"])
+    q, k, v, cu = (t.to(dev) for t in synth.generate_varlen(lens, w["Hq"], w["Hkv"], w["D"]))
+    g = torch.Generator(device="cpu")
+    g.manual_seed(1)
+    do = torch.randn(q.shape, generator=g).to(torch.bfloat16).to(dev)
+    scale = 1.0 / math.sqrt(w["D"])
+    B, Hq, Hkv, total, D = len(lens), w["Hq"], w["Hkv"], w["total"], w["D"]
+    o = torch.empty_like(q)
+    lse = torch.empty((Hq, total), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fws = torch.empty(fa.fa_fwd_varlen_workspace_size(B, total), dtype=torch.uint8, device=dev)
+    wsb = fa.fa_bwd_varlen_workspace_size(B, Hq, Hkv, total, D, det)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    sh = stream.cuda_stream
+    rc = fa.fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                          cu.data_ptr(), B, Hq, Hkv, total, max(lens), D, w["causal"], scale,
+                          fws.data_ptr(), fws.numel(), sh)
+    if rc != 0:
+        raise RuntimeError(f"fa_fwd_varlen: {fa.fa_strerror(rc)}")
+
+    def call():
+        rc = fa.fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                              dv.data_ptr(), cu.data_ptr(), B, Hq, Hkv, total, max(lens), D,
+                              w["causal"], scale, ws.data_ptr(), wsb, det, sh)
+        if rc != 0:
+            raise RuntimeError(f"fa_bwd_varlen: {fa.fa_strerror(rc)}")
+
+    for _ in range(2):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    flops = 2.5 * synth.varlen_flops_fwd(lens, Hq, D, w["causal"])
+    tf = flops / (us * 1e-6) / 1e12
+    return {"workload": f"{B} causal sequences, {total} tokens (lengths {min(lens)}..{max(lens)}), "
+                        f"H{Hq} D{D}, dQ mode {det}",
+            "us": round(us, 1), "tflops": round(tf, 1),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
+
+
+def bench_grouped(fa, torch, dev, stream, Hkv: int = 2, reps: int = 5) -> dict:
+    """Grouped heads (Hq 16 over Hkv K/V heads) at the headline size: forward
+    plus backward (stored-dS dQ mode; dK and dV summed over each group inside
+    the main kernel)."""
+    B, Hq, N, D = 2, 16, 8192, 128
+    g = torch.Generator(device="cpu")
+    g.manual_seed(2)
+    q = torch.randn((B, Hq, N, D), generator=g).to(torch.bfloat16).to(dev)
+    k = torch.randn((B, Hkv, N, D), generator=g).to(torch.bfloat16).to(dev)
+    v = torch.randn((B, Hkv, N, D), generator=g).to(torch.bfloat16).to(dev)
+    do = torch.randn((B, Hq, N, D), generator=g).to(torch.bfloat16).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    det = 1
+    wsb = fa.fa_bwd_workspace_size(B, Hq, Hkv, N, D, det)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(D)
+    sh = stream.cuda_stream
+
+    def call():
+        rc = fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                       B, Hq, Hkv, N, D, 1, scale, sh)
+        if rc == 0:
+            rc = fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                           do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq,
+                           Hkv, N, D, 1, scale, ws.data_ptr(), wsb, det, sh)
+        if rc != 0:
+            raise RuntimeError(f"grouped fwd+bwd: {fa.fa_strerror(rc)}")
+
+    call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    flops = 3.5 * 4.0 * B * Hq * N * N * D / 2   # forward 2 products + backward 5, causal
+    tf = flops / (us * 1e-6) / 1e12
+    return {"workload": f"B{B} Hq{Hq} Hkv{Hkv} N{N} D{D} causal, forward + backward (stored dS)",
+            "us": round(us, 1), "tflops": round(tf, 1),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
+
+
 def bench_fp8(fa, torch, dev, stream, P, w, reps: int = 20) -> dict:
     """FP8 forward on the headline shape (same inputs as the bf16 step),
     rotation on; the timed call includes the quantize pass."""
@@ -401,6 +502,8 @@ def main() -> int:
     out["bwd"]["workspace_bytes"] = ws_bytes
     if not args.no_extras:
         out["extras"] = {"varlen_fwd": bench_varlen(fa, torch, dev, stream),
+                         "varlen_bwd": bench_varlen_bwd(fa, torch, dev, stream),
+                         "grouped_fwd_bwd": bench_grouped(fa, torch, dev, stream),
                          "decode_splitkv": bench_decode(fa, torch, dev, stream),
                          "fp8_fwd": bench_fp8(fa, torch, dev, stream, P, w)}
     if not args.no_cpu_baseline:

@@ -53,6 +53,8 @@ struct BwdParams {
   float* lse2;     // fp32 [B][Hq][N]
   char* ds;        // dS^T blocks (stored-dS mode), ds_head bytes per (b, hq)
   uint32_t ds_head;
+  int hsplit;      // query-head parts per K/V head (warp-specialized kernel)
+  float* kv_part;  // fp32 partial dK, dV when hsplit > 1
   int nb32;        // 32-row blocks per head, ceil(N / 32)
   // Variable length: cumulative sequence starts, the token count, and the
   // work list of this kernel (2 ints per item) with its length.
@@ -707,9 +709,14 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
 
   const int Hkv = p.Hq / p.G;
   const int wg = blockIdx.x;
-  const int bhk = wg % (p.B * Hkv);
-  const int kb = wg / (p.B * Hkv);
+  // Work item: (batch, K/V head, part hs of its G query heads, key tile);
+  // key tiles vary slowest so the longest causal items start first.
+  const int BHkv = p.B * Hkv;
+  const int bhk = wg % BHkv;
+  const int hs = (wg / BHkv) % p.hsplit;
+  const int kb = wg / BHkv / p.hsplit;
   const int b = bhk / Hkv, hk = bhk % Hkv;
+  const int gs = p.G / p.hsplit;       // query heads this workgroup walks
   const int N = p.N;
   const int nqs = (N + QS - 1) / QS;
   const int k0 = kb * BN;
@@ -740,8 +747,8 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
   }
   const int qs_first = CAUSAL ? (k0 / QS) : 0;
   const int per_head = max(nqs - qs_first, 0);
-  const int nsteps = p.G * per_head;
-  const int hq0 = hk * p.G;
+  const int nsteps = gs * per_head;
+  const int hq0 = hk * p.G + hs * gs;
   const uint32_t lse_head_bytes = (uint32_t)N * 4u;
   const size_t q_hstride = (size_t)N * D * 2;
   const size_t l_hstride = (size_t)N * 4;
@@ -1013,20 +1020,39 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
       body(i + 5, st4, pb0, st3);
     }
     // dK (scaled) and dV of this wave's 32 keys.  Register r of d-block db:
-    // key kw + 8(r/4) + 4h + r%4, d = 32 db + n.
-    uint16_t* dKh = dK + kv_head;
-    uint16_t* dVh = dV + kv_head;
+    // key kw + 8(r/4) + 4h + r%4, d = 32 db + n.  With the query heads cut
+    // into parts, each part writes fp32 partials that bwd_kv_reduce_kernel
+    // sums in part order.
+    if (p.hsplit > 1) {
+      const size_t plane = (size_t)BHkv * N * D;
+      float* pk = p.kv_part + (size_t)hs * 2 * plane + (size_t)bhk * N * D;
+      float* pv = pk + plane;
 #pragma unroll
-    for (int db = 0; db < ND; ++db)
+      for (int db = 0; db < ND; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int krow = kw + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (krow < N) {
-          const size_t off = (size_t)krow * D + 32 * db + n;
-          dKh[off] = (uint16_t)(pack_bf16x2(dk_acc[db][r] * p.scale, 0.f) & 0xffffu);
-          dVh[off] = (uint16_t)(pack_bf16x2(dv_acc[db][r], 0.f) & 0xffffu);
+        for (int r = 0; r < 16; ++r) {
+          const int krow = kw + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (krow < N) {
+            const size_t off = (size_t)krow * D + 32 * db + n;
+            pk[off] = dk_acc[db][r] * p.scale;
+            pv[off] = dv_acc[db][r];
+          }
         }
-      }
+    } else {
+      uint16_t* dKh = dK + kv_head;
+      uint16_t* dVh = dV + kv_head;
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int krow = kw + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (krow < N) {
+            const size_t off = (size_t)krow * D + 32 * db + n;
+            dKh[off] = (uint16_t)(pack_bf16x2(dk_acc[db][r] * p.scale, 0.f) & 0xffffu);
+            dVh[off] = (uint16_t)(pack_bf16x2(dv_acc[db][r], 0.f) & 0xffffu);
+          }
+        }
+    }
   }
 }
 
@@ -1402,7 +1428,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, const BwdParams& p, hipStream_t s, uns
 
 BwdParams make_params(const BwdArgs& a) {
   const int QS = 4096 / a.D;
-  const BwdLayout lay = bwd_layout(a.B, a.Hq, a.N, a.D, a.deterministic);
+  const BwdLayout lay = bwd_layout(a.B, a.Hq, a.Hkv, a.N, a.D, a.deterministic);
   char* ws = (char*)a.workspace;
   BwdParams p;
   p.B = a.B;
@@ -1419,6 +1445,8 @@ BwdParams make_params(const BwdArgs& a) {
   p.nb32 = (a.N + 31) / 32;
   p.ds_head = (uint32_t)ds_head_bytes(a.N);
   p.ds = a.deterministic == kDqStored ? ws + lay.ds : nullptr;
+  p.hsplit = lay.hsplit;
+  p.kv_part = lay.hsplit > 1 ? (float*)(ws + lay.kv_part) : nullptr;
   p.cu = nullptr;
   p.total = 0;
   p.items = nullptr;
@@ -1437,14 +1465,43 @@ hipError_t launch_pre_d(const BwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// dK, dV = bf16 of the sum of the parts' fp32 partials, in part order (4
+// elements per thread; n4 = B * Hkv * N * D / 4 per tensor).
+__global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(const float* __restrict__ part,
+                                                            uint16_t* __restrict__ dk,
+                                                            uint16_t* __restrict__ dv, size_t n4,
+                                                            int parts) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= 2 * n4) return;
+  const size_t which = i / n4, j = i % n4;
+  const float4* src = (const float4*)part + which * n4 + j;
+  float4 acc = src[0];
+  for (int s = 1; s < parts; ++s) {
+    const float4 x = src[(size_t)s * 2 * n4];
+    acc.x += x.x;
+    acc.y += x.y;
+    acc.z += x.z;
+    acc.w += x.w;
+  }
+  u32x2 w;
+  w[0] = pack_bf16x2(acc.x, acc.y);
+  w[1] = pack_bf16x2(acc.z, acc.w);
+  ((u32x2*)(which ? dv : dk))[j] = w;
+}
+
 // D = 128 in the fixed-order dQ modes: the warp-specialized kernel.
 constexpr bool kBwdSplitRoles = true;
 template <bool CAUSAL, int DQM>
 hipError_t launch_ws_t(const BwdArgs& a, const BwdParams& p, hipStream_t s) {
-  const dim3 grid((unsigned)(a.B * a.Hkv * p.nkb));
+  const dim3 grid((unsigned)(a.B * a.Hkv * p.nkb * p.hsplit));
   hipLaunchKernelGGL((bwd_ws_kernel<CAUSAL, DQM>), grid, dim3(512), 0, s, (const uint16_t*)a.q,
                      (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
                      (uint16_t*)a.dk, (uint16_t*)a.dv, p);
+  if (p.hsplit > 1) {
+    const size_t n4 = (size_t)a.B * a.Hkv * a.N * 128 / 4;
+    hipLaunchKernelGGL(bwd_kv_reduce_kernel, dim3((unsigned)((2 * n4 + 255) / 256)), dim3(256), 0,
+                       s, (const float*)p.kv_part, (uint16_t*)a.dk, (uint16_t*)a.dv, n4, p.hsplit);
+  }
   return hipGetLastError();
 }
 
@@ -1502,7 +1559,8 @@ hipError_t launch_dq_d(const BwdArgs& a, hipStream_t s) {
 // preprocess and the atomic-mode convert run over every row unchanged.
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_varlen_t(const BwdArgs& a, const VarlenArgs& v, hipStream_t s) {
-  const BwdLayout lay = bwd_layout(1, a.Hq, v.total, D, a.deterministic);
+  // (Hkv = Hq: the variable-length backward runs bwd_main_kernel, no head split.)
+  const BwdLayout lay = bwd_layout(1, a.Hq, a.Hq, v.total, D, a.deterministic);
   char* lists = (char*)a.workspace + lay.total;
   const size_t lbytes = varlen_workspace_bytes(v.B, v.total);
   int* main_n = (int*)lists;
@@ -1522,6 +1580,8 @@ hipError_t launch_bwd_varlen_t(const BwdArgs& a, const VarlenArgs& v, hipStream_
   BwdParams p = make_params(a);
   p.cu = v.cu;
   p.total = v.total;
+  p.hsplit = 1;
+  p.kv_part = nullptr;
   p.items = main_items;
   p.n_items = main_n;
   e = a.deterministic == kDqAtomic ? launch_bwd_t<D, CAUSAL, kDqAtomic, true>(a, p, s, items_max)
@@ -1544,7 +1604,7 @@ hipError_t launch_bwd_varlen_t(const BwdArgs& a, const VarlenArgs& v, hipStream_
 }  // namespace
 
 size_t bwd_varlen_workspace_bytes(int B, int Hq, int total, int D, int deterministic) {
-  return bwd_layout(1, Hq, total, D, deterministic).total + 2 * varlen_workspace_bytes(B, total);
+  return bwd_layout(1, Hq, Hq, total, D, deterministic).total + 2 * varlen_workspace_bytes(B, total);
 }
 
 hipError_t launch_bwd_varlen(const BwdArgs& a, const VarlenArgs& v, hipStream_t s) {
@@ -1558,7 +1618,16 @@ size_t ds_head_bytes(int N) {
   return nb * nb * 2048;
 }
 
-BwdLayout bwd_layout(int B, int Hq, int N, int D, int deterministic) {
+int bwd_head_split(int B, int Hq, int Hkv, int N, int D, int deterministic) {
+  if (!kBwdSplitRoles || D != 128 || deterministic == kDqAtomic) return 1;
+  const int G = Hq / Hkv;
+  const long tiles = (long)B * Hkv * ((N + kBwdBN - 1) / kBwdBN);
+  int s = 1;
+  while (2 * s <= G && G % (2 * s) == 0 && tiles * s < 1024) s *= 2;
+  return s;
+}
+
+BwdLayout bwd_layout(int B, int Hq, int Hkv, int N, int D, int deterministic) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const size_t rows = (size_t)B * Hq * N;
   BwdLayout l;
@@ -1568,7 +1637,10 @@ BwdLayout bwd_layout(int B, int Hq, int N, int D, int deterministic) {
   size_t extra = 0;
   if (deterministic == kDqAtomic) extra = up(rows * D * 4);
   if (deterministic == kDqStored) extra = up((size_t)B * Hq * ds_head_bytes(N));
-  l.total = l.dq_acc + extra;
+  l.kv_part = l.dq_acc + extra;
+  l.hsplit = bwd_head_split(B, Hq, Hkv, N, D, deterministic);
+  const size_t part = l.hsplit > 1 ? up((size_t)l.hsplit * 2 * B * Hkv * N * D * 4) : 0;
+  l.total = l.kv_part + part;
   return l;
 }
 

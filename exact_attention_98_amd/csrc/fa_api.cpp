@@ -275,7 +275,7 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
 size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int D, int deterministic) {
   if (check_shape(B, Hq, Hkv, N, D, 1.0f) != FA_OK) return 0;
   if (check_mode(N, deterministic) != FA_OK) return 0;
-  return fa::bwd_layout(B, Hq, N, D, deterministic).total;
+  return fa::bwd_layout(B, Hq, Hkv, N, D, deterministic).total;
 }
 
 }  // extern "C"
@@ -305,7 +305,7 @@ int check_bwd(int B, int Hq, int Hkv, int N, int D, float scale, const void* wor
     if (!aligned16(b.p)) return FA_ERR_ALIGN;
   for (const Buf& b : writes)
     if (!aligned16(b.p)) return FA_ERR_ALIGN;
-  const fa::BwdLayout lay = fa::bwd_layout(B, Hq, N, D, deterministic);
+  const fa::BwdLayout lay = fa::bwd_layout(B, Hq, Hkv, N, D, deterministic);
   if (!workspace || workspace_bytes < lay.total) return FA_ERR_WORKSPACE;
   if (((uintptr_t)workspace & 255u) != 0) return FA_ERR_ALIGN;
   const Buf ws{workspace, lay.total};

@@ -115,13 +115,21 @@ struct BwdLayout {
   size_t lse2;      // fp32 [B][Hq][N], LSE * log2(e)
   size_t dq_acc;    // fp32 [B][Hq][N][D] (atomic mode only)
   size_t ds;        // dS^T blocks, ds_head_bytes(N) per (b, hq) (stored-dS mode only)
+  size_t kv_part;   // fp32 [hsplit][2][B][Hkv][N][D] partial dK, dV (hsplit > 1 only)
+  int hsplit;       // query-head groups per K/V head in the main kernel's grid
   size_t total;
 };
+
+// Number of parts the G query heads of a K/V head are cut into in the main
+// backward kernel's grid (D = 128, fixed-order dQ modes): more than one when
+// B * Hkv * ceil(N / 128) key tiles alone would leave the grid short of
+// workgroups; the parts' dK, dV are then summed in a fixed order.
+int bwd_head_split(int B, int Hq, int Hkv, int N, int D, int deterministic);
 
 // Bytes of the stored-dS blocks of one (batch, query head).
 size_t ds_head_bytes(int N);
 
-BwdLayout bwd_layout(int B, int Hq, int N, int D, int deterministic);
+BwdLayout bwd_layout(int B, int Hq, int Hkv, int N, int D, int deterministic);
 // The three backward stages; each reads only the BwdArgs fields it needs.
 hipError_t launch_bwd_preprocess(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t stream);
