@@ -678,7 +678,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
 // LSE and Delta), i+1 (row reads), i+2 .. i+4 (copies in flight, three steps
 // of latency hidden).  Only the gradient waves copy step tiles in; only the
 // score waves store dS.
-template <bool CAUSAL, int DQM>
+template <bool CAUSAL, int DQM, bool VARLEN>
 __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
@@ -696,6 +696,7 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
   constexpr bool STORE_DS = DQM == kDqStored;
   static_assert(NLD >= 1, "step tile too small");
   static_assert(DQM != kDqAtomic, "atomic dQ uses bwd_main_kernel");
+  static_assert(!(VARLEN && DQM == kDqStored), "no stored-dS layout for packed sequences");
   constexpr int STAGE = 2 * TB + 512;  // Q, dO, 256 B LSE * log2 e, 256 B Delta
   constexpr int PSLOT = 4 * 4096;      // P, dS of the 4 score waves
   __shared__ __attribute__((aligned(1024))) char st0[STAGE];
@@ -711,13 +712,37 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
   const int wg = blockIdx.x;
   // Work item: (batch, K/V head, part hs of its G query heads, key tile);
   // key tiles vary slowest so the longest causal items start first.
+  // Variable length: (sequence, key tile) from the list sorted largest
+  // first, heads fastest, one part; a sequence's rows start at cu_seqlens[b]
+  // in every head's [total][D] matrix.
   const int BHkv = p.B * Hkv;
-  const int bhk = wg % BHkv;
-  const int hs = (wg / BHkv) % p.hsplit;
-  const int kb = wg / BHkv / p.hsplit;
-  const int b = bhk / Hkv, hk = bhk % Hkv;
-  const int gs = p.G / p.hsplit;       // query heads this workgroup walks
-  const int N = p.N;
+  int b, hk, kb, hs, bhk;
+  SeqGeom sg;
+  if constexpr (VARLEN) {
+    const int item = wg / Hkv;
+    hk = wg % Hkv;
+    if (item >= *p.n_items) return;  // whole workgroup: the grid is sized for the worst case
+    b = p.items[2 * item];
+    kb = p.items[2 * item + 1];
+    hs = 0;
+    bhk = hk;
+    const int s0 = min(max(p.cu[b], 0), p.total);
+    sg.N = min(max(p.cu[b + 1] - s0, 0), p.total - s0);
+    sg.row0 = (size_t)s0;
+    sg.hstride = (size_t)p.total;
+  } else {
+    bhk = wg % BHkv;
+    hs = (wg / BHkv) % p.hsplit;
+    kb = wg / BHkv / p.hsplit;
+    b = bhk / Hkv;
+    hk = bhk % Hkv;
+    sg.N = p.N;
+    sg.row0 = 0;
+    sg.hstride = (size_t)p.N;
+  }
+  const int bq = VARLEN ? 0 : b;       // batch index in the head arithmetic
+  const int gs = p.G / (VARLEN ? 1 : p.hsplit);  // query heads this workgroup walks
+  const int N = sg.N;
   const int nqs = (N + QS - 1) / QS;
   const int k0 = kb * BN;
 
@@ -729,7 +754,7 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
   const int kw = k0 + 32 * kwave;    // first key of this wave's 32 (uniform)
   const int key = kw + n;
   const uint32_t head_bytes = (uint32_t)((size_t)N * D * 2);
-  const size_t kv_head = ((size_t)b * Hkv + hk) * (size_t)N * D;
+  const size_t kv_head = (((size_t)bq * Hkv + hk) * sg.hstride + sg.row0) * D;
 
   // ---- step copies (gradient waves only) ----------------------------------
   // The score waves issue no loads in the loop, so their only memory traffic,
@@ -750,9 +775,9 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
   const int nsteps = gs * per_head;
   const int hq0 = hk * p.G + hs * gs;
   const uint32_t lse_head_bytes = (uint32_t)N * 4u;
-  const size_t q_hstride = (size_t)N * D * 2;
-  const size_t l_hstride = (size_t)N * 4;
-  const size_t qrow0 = ((size_t)b * p.Hq + hq0) * (size_t)N;
+  const size_t q_hstride = sg.hstride * D * 2;
+  const size_t l_hstride = sg.hstride * 4;
+  const size_t qrow0 = ((size_t)bq * p.Hq + hq0) * sg.hstride + sg.row0;
   int iss_qs = nqs - 1;
   const char* iss_q = (const char*)(Q + qrow0 * D);
   const char* iss_do = (const char*)(dO + qrow0 * D);
@@ -1023,7 +1048,7 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
     // key kw + 8(r/4) + 4h + r%4, d = 32 db + n.  With the query heads cut
     // into parts, each part writes fp32 partials that bwd_kv_reduce_kernel
     // sums in part order.
-    if (p.hsplit > 1) {
+    if (!VARLEN && p.hsplit > 1) {
       const size_t plane = (size_t)BHkv * N * D;
       float* pk = p.kv_part + (size_t)hs * 2 * plane + (size_t)bhk * N * D;
       float* pv = pk + plane;
@@ -1494,7 +1519,7 @@ constexpr bool kBwdSplitRoles = true;
 template <bool CAUSAL, int DQM>
 hipError_t launch_ws_t(const BwdArgs& a, const BwdParams& p, hipStream_t s) {
   const dim3 grid((unsigned)(a.B * a.Hkv * p.nkb * p.hsplit));
-  hipLaunchKernelGGL((bwd_ws_kernel<CAUSAL, DQM>), grid, dim3(512), 0, s, (const uint16_t*)a.q,
+  hipLaunchKernelGGL((bwd_ws_kernel<CAUSAL, DQM, false>), grid, dim3(512), 0, s, (const uint16_t*)a.q,
                      (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
                      (uint16_t*)a.dk, (uint16_t*)a.dv, p);
   if (p.hsplit > 1) {
@@ -1584,8 +1609,17 @@ hipError_t launch_bwd_varlen_t(const BwdArgs& a, const VarlenArgs& v, hipStream_
   p.kv_part = nullptr;
   p.items = main_items;
   p.n_items = main_n;
-  e = a.deterministic == kDqAtomic ? launch_bwd_t<D, CAUSAL, kDqAtomic, true>(a, p, s, items_max)
-                                   : launch_bwd_t<D, CAUSAL, kDqRecompute, true>(a, p, s, items_max);
+  if (kBwdSplitRoles && D == 128 && a.deterministic == kDqRecompute) {
+    // The warp-specialized kernel over the same (sequence, key tile) list.
+    hipLaunchKernelGGL((bwd_ws_kernel<CAUSAL, kDqRecompute, true>), dim3(items_max * (unsigned)a.Hkv),
+                       dim3(512), 0, s, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                       (const uint16_t*)a.v, (const uint16_t*)a.dout, (uint16_t*)a.dk,
+                       (uint16_t*)a.dv, p);
+    e = hipGetLastError();
+  } else {
+    e = a.deterministic == kDqAtomic ? launch_bwd_t<D, CAUSAL, kDqAtomic, true>(a, p, s, items_max)
+                                     : launch_bwd_t<D, CAUSAL, kDqRecompute, true>(a, p, s, items_max);
+  }
   if (e != hipSuccess) return e;
   if (a.deterministic == kDqAtomic) {
     const size_t n8 = (size_t)a.Hq * v.total * D / 8;
