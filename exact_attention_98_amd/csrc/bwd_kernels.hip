@@ -677,7 +677,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
 // Step tiles rotate through six stages: step i-1 (transposing reads), i (its
 // LSE and Delta), i+1 (row reads), i+2 .. i+4 (copies in flight, three steps
 // of latency hidden).  Only the gradient waves copy step tiles in; only the
-// score waves store dS.
+// score waves store dS, each half block as soon as it is packed.
 template <bool CAUSAL, int DQM, bool VARLEN>
 __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -855,18 +855,20 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
     for (int t = 0; t < T; ++t) a_off[t] = (uint32_t)(n * RB + (((2 * t + h) ^ tile_swz<D>(n)) * 16));
 
     int cur_qs = nqs - 1, cur_g = 0;
-    int prev_qs = 0, prev_g = 0;
-    u32x4 ds_keep[2];
+    // Stored-dS mode: half u of this wave's dS^T block of the current step
+    // goes out as soon as it is packed (spread over the step; these waves
+    // issue no loads, so no wait ever covers the stores).  Lane (key n, half
+    // h) holds positions 16u + 8h .. +8 of row n; a block that does not exist
+    // (padding rows, or above the diagonal under causal) gets an offset past
+    // the end of the head's range and the store is dropped.
     const int kb32 = kw / 32;
     const uint32_t ds_lane = (uint32_t)(n * 64 + h * 16);
-    auto store_ds = [&](int g, int qs) {
+    auto store_ds = [&](int u, u32x4 w) {
       if constexpr (STORE_DS) {
-        const rsrc_t r = make_rsrc_uniform(p.ds + ((size_t)b * p.Hq + hq0 + g) * p.ds_head, p.ds_head);
-        const bool ok = qs < p.nb32 && kb32 < p.nb32 && (!CAUSAL || kb32 <= qs);
-        const uint32_t off = ok ? (uint32_t)(qs * p.nb32 + kb32) * 2048u : 0xFFFFF000u;
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-          __builtin_amdgcn_raw_buffer_store_b128(ds_keep[u], r, off + ds_lane + 32u * u, 0, 0);
+        const rsrc_t r = make_rsrc_uniform(p.ds + ((size_t)b * p.Hq + hq0 + cur_g) * p.ds_head, p.ds_head);
+        const bool ok = cur_qs < p.nb32 && kb32 < p.nb32 && (!CAUSAL || kb32 <= cur_qs);
+        const uint32_t off = ok ? (uint32_t)(cur_qs * p.nb32 + kb32) * 2048u : 0xFFFFF000u;
+        __builtin_amdgcn_raw_buffer_store_b128(w, r, off + ds_lane + 32u * u, 0, 0);
       }
     };
 
@@ -889,7 +891,6 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
     auto body = [&](int i, const char* cur, const char* nxt, char* pbw, f32x16& sv, f32x16& dv,
                     f32x16& sn, f32x16& dn) __attribute__((always_inline)) {
       __syncthreads();
-      if (STORE_DS && i > 0 && i <= nsteps) store_ds(prev_g, prev_qs);
       if (i >= nsteps) return;
       const int q0 = cur_qs * QS;
       pin(sv);
@@ -946,13 +947,11 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
             }
             *(u32x4*)(pw + u * 1024) = w1;
             *(u32x4*)(pw + (2 + u) * 1024) = w2;
-            if constexpr (STORE_DS) ds_keep[u] = w2;
+            store_ds(u, w2);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      prev_qs = cur_qs;
-      prev_g = cur_g;
       if (--cur_qs < qs_first) {
         cur_qs = nqs - 1;
         ++cur_g;
