@@ -82,7 +82,11 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
  * Bytes of device workspace fa_bwd needs for this problem and dQ mode
  * (deterministic, see fa_bwd): per-row Delta = rowsum(dO * O) and
  * LSE * log2(e), plus the fp32 dQ accumulator (mode 0) or the bf16 dS blocks
- * (mode 1).  Returns 0 for invalid sizes or modes.
+ * (mode 1); with grouped heads (Hq > Hkv), D = 128 and modes 1 and 2, when
+ * B * Hkv * ceil(N / 128) is small the query heads of each group are split
+ * over several workgroups and the workspace also holds their fp32 partial dK
+ * and dV (at most 2 * Hq/Hkv * B * Hkv * N * D * 4 bytes more).  Returns 0 for
+ * invalid sizes or modes.
  */
 size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int D, int deterministic);
 
@@ -107,7 +111,8 @@ size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int D, int determini
  *     ascending order; workspace about B*Hq*N*N*2 bytes (one head's blocks
  *     must stay below 4 GiB - 8 KiB, else FA_ERR_TOO_LARGE).
  *   2: as 1, but the separate pass recomputes S, dP and dS instead of
- *     reading them; workspace B*Hq*N*8 bytes.
+ *     reading them; workspace B*Hq*N*8 bytes (plus the grouped-head partials
+ *     above).
  *   Modes 1 and 2 give dq, dk and dv bit-identical across calls with the
  *   same inputs on the same device.  Other values: FA_ERR_INVALID.
  * With Hq != Hkv, dk and dv sum over the query heads that share a K/V head.
