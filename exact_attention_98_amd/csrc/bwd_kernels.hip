@@ -378,12 +378,14 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
 
   // Stored-dS mode: this wave's dS^T blocks of one step, 32 keys x 32 queries
   // per block, 16 bytes per lane and block half u (lane of key n, half h:
-  // positions 16u + 8h .. +8 of row n).  Blocks that do not exist (padding
-  // rows, or above the diagonal under causal) get an offset past the end of
-  // the head's range and the store is dropped.
+  // positions 16u + 8h .. +8 of row n), each half a contiguous KiB in lane
+  // order (byte 1024u + 16 lane), so every store writes whole cache lines.
+  // Blocks that do not exist (padding rows, or above the diagonal under
+  // causal) get an offset past the end of the head's range and the store is
+  // dropped.
   u32x4 ds_keep[NQB][2];
   const int kb32 = kw / 32;
-  const uint32_t ds_lane = (uint32_t)(n * 64 + h * 16);
+  const uint32_t ds_lane = (uint32_t)lane * 16u;
   auto store_ds = [&](int g, int qs) {
     if constexpr (STORE_DS) {
       const rsrc_t r = make_rsrc_uniform(p.ds + ((size_t)b * p.Hq + hq0 + g) * p.ds_head, p.ds_head);
@@ -395,7 +397,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
 #pragma unroll
         for (int u = 0; u < 2; ++u)
           // Plain (cached) stores: measured faster here than non-temporal ones.
-          __builtin_amdgcn_raw_buffer_store_b128(ds_keep[qb][u], r, off + ds_lane + 32u * u, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(ds_keep[qb][u], r, off + ds_lane + 1024u * u, 0, 0);
       }
     }
   };
@@ -858,17 +860,18 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
     // Stored-dS mode: half u of this wave's dS^T block of the current step
     // goes out as soon as it is packed (spread over the step; these waves
     // issue no loads, so no wait ever covers the stores).  Lane (key n, half
-    // h) holds positions 16u + 8h .. +8 of row n; a block that does not exist
-    // (padding rows, or above the diagonal under causal) gets an offset past
-    // the end of the head's range and the store is dropped.
+    // h) holds positions 16u + 8h .. +8 of row n, stored at byte
+    // 1024u + 16 lane of the block (whole cache lines per store); a block that
+    // does not exist (padding rows, or above the diagonal under causal) gets
+    // an offset past the end of the head's range and the store is dropped.
     const int kb32 = kw / 32;
-    const uint32_t ds_lane = (uint32_t)(n * 64 + h * 16);
+    const uint32_t ds_lane = (uint32_t)lane * 16u;
     auto store_ds = [&](int u, u32x4 w) {
       if constexpr (STORE_DS) {
         const rsrc_t r = make_rsrc_uniform(p.ds + ((size_t)b * p.Hq + hq0 + cur_g) * p.ds_head, p.ds_head);
         const bool ok = cur_qs < p.nb32 && kb32 < p.nb32 && (!CAUSAL || kb32 <= cur_qs);
         const uint32_t off = ok ? (uint32_t)(cur_qs * p.nb32 + kb32) * 2048u : 0xFFFFF000u;
-        __builtin_amdgcn_raw_buffer_store_b128(w, r, off + ds_lane + 32u * u, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(w, r, off + ds_lane + 1024u * u, 0, 0);
       }
     };
 
@@ -1334,6 +1337,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_kernel(const uint16_t* __res
     const int row = g / KCH, pc = g % KCH;
     ld_off[s] = (uint32_t)(row * RB + ((pc ^ tile_swz<D>(row)) * 16));
   }
+  // A stored block holds key row r's positions 16u + 8h .. +8 as 16-byte
+  // chunk 64u + 32h + r.  In LDS that chunk goes to 64u + 32h + (r ^ 4h ^ 8u):
+  // the copy moves whole 64-byte groups of four chunks, so each 1 KiB half u
+  // (copy s = u) is still one contiguous read, and the transposing reads
+  // below, 16 key rows of both h at once, hit 64 distinct banks.
+  uint32_t ds_src[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) ds_src[s] = (uint32_t)((64 * s + (lane ^ (4 * (lane >> 5) + 8 * s))) * 16);
   auto issue_tile = [&](int kt, char* ks, char* dsb) {
     const uint32_t base = (uint32_t)kt * TB;
     const uint32_t left = head_bytes > base ? head_bytes - base : 0u;
@@ -1350,15 +1361,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_kernel(const uint16_t* __res
       const rsrc_t dr = make_rsrc_uniform(dsh + off, ok ? 2048u : 0u);
 #pragma unroll
       for (int s = 0; s < 2; ++s)
-        lds_dma16_nt(dr, (lds_void*)(dsb + wave * 4096 + j * 2048 + s * 1024),
-                     (uint32_t)(s * 1024 + lane * 16));
+        lds_dma16_nt(dr, (lds_void*)(dsb + wave * 4096 + j * 2048 + s * 1024), ds_src[s]);
     }
   };
 
   // Transposing reads.  K^T (A operand, row d = 32 db + n, 8 keys): lane j of
   // 16-lane group gq points at key row 8 rd + 4h + j/4 (+ 16 t), d = 32 db +
   // 16 (gq & 1) + 4 (j & 3).  dS^T (B operand, column = block position n, 8
-  // keys): key row 8 rd + 4h + j/4 (+ 16 t), position 16 (gq & 1) + 4 (j & 3).
+  // keys): key row r = 8 rd + 4h + j/4 (+ 16 t), position 16 (gq & 1) + 4 (j & 3),
+  // i.e. half u = gq & 1, h' = (j & 3) / 2, element 4 (j & 1) of LDS chunk
+  // 64u + 32h' + (r ^ 4h' ^ 8u) (the 16 t rows add 256 bytes).
   const int j16 = lane & 15, gq = lane >> 4;
   uint32_t t_off[ND][2], s_off[2];
 #pragma unroll
@@ -1369,7 +1381,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_kernel(const uint16_t* __res
       const int c = 4 * db + 2 * (gq & 1) + ((j16 & 3) >> 1);
       t_off[db][rd] = (uint32_t)(row * RB + ((c ^ tile_swz<D>(row)) * 16) + (j16 & 1) * 8);
     }
-    s_off[rd] = (uint32_t)(wave * 4096 + row * 64 + (16 * (gq & 1) + 4 * (j16 & 3)) * 2);
+    const int su = gq & 1, sh = (j16 & 3) >> 1;
+    s_off[rd] = (uint32_t)(wave * 4096 + (64 * su + 32 * sh + (row ^ (4 * sh) ^ (8 * su))) * 16 + (j16 & 1) * 8);
   }
 
   f32x16 acc[ND];
@@ -1387,7 +1400,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_kernel(const uint16_t* __res
     // accumulators.
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const char* sb = dsb + (t >> 1) * 2048 + (t & 1) * 16 * 64;
+      const char* sb = dsb + (t >> 1) * 2048 + (t & 1) * 256;
       const u32x2 slo = lds_read_tr16((const lds_void*)(sb + s_off[0]));
       const u32x2 shi = lds_read_tr16((const lds_void*)(sb + s_off[1]));
       const bf16x8 bs = as_bf16x8(u32x4{slo[0], slo[1], shi[0], shi[1]});
