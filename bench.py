@@ -318,6 +318,53 @@ def bench_decode(fa, torch, dev, stream, reps: int = 50) -> dict:
                          "bytes": nbytes}}
 
 
+def bench_fwd_choices(fa, torch, dev, stream, P, w, reps: int = 20, rounds: int = 3) -> dict:
+    """Forward design choices at the headline shape, each timed on the same
+    stream in interleaved rounds (median of the per-round means):
+    - the share of the exponentials computed by the FMA-only cubic instead of
+      v_exp_f32 (fa_fwd_ex, 0, 1 or 2 quarters; 0 is what fa_fwd runs);
+    - the conditional rescale under input variant (b), whose row maxima grow
+      by more than tau on many tiles, against variant (a)."""
+    import synth
+    B, Hq, Hkv, N, D = w.B, w.Hq, w.Hkv, w.N, w.D
+    sh = stream.cuda_stream
+    o = torch.empty((B, Hq, N, D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    wb = synth.WORKLOADS["causal_b"]
+    qb, kb, vb = (t.to(dev) for t in synth.generate_workload(wb))
+
+    def fwd(q, k, v, quarters):
+        rc = fa.fa_fwd_ex(q, k, v, o.data_ptr(), lse.data_ptr(), B, Hq, Hkv, N, D, 1, w.scale,
+                          quarters, sh)
+        if rc != 0:
+            raise RuntimeError(f"fa_fwd_ex: {fa.fa_strerror(rc)}")
+
+    cases = {"poly_0": (P["q"], P["k"], P["v"], 0), "poly_1": (P["q"], P["k"], P["v"], 1),
+             "poly_2": (P["q"], P["k"], P["v"], 2),
+             "variant_b": (qb.data_ptr(), kb.data_ptr(), vb.data_ptr(), 0)}
+    times = {c: [] for c in cases}
+    for _ in range(rounds):
+        for c, args in cases.items():
+            for _ in range(2):
+                fwd(*args)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(reps):
+                fwd(*args)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times[c].append(e0.elapsed_time(e1) / reps * 1e3)
+    med = {c: sorted(t)[len(t) // 2] for c, t in times.items()}
+    tf = lambda us: round(w.flops_fwd() / (us * 1e-6) / 1e12, 1)
+    return {"workload": f"forward B{B} H{Hq} N{N} D{D} causal",
+            "exp_poly_share": [{"quarters": qq, "us": round(med[f"poly_{qq}"], 1),
+                                "tflops": tf(med[f"poly_{qq}"])} for qq in (0, 1, 2)],
+            "lazy_rescale": {"variant_a_us": round(med["poly_0"], 1),
+                             "variant_b_us": round(med["variant_b"], 1),
+                             "variant_b_tflops": tf(med["variant_b"])}}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -329,7 +376,8 @@ def main() -> int:
                          "workspace), or atomic adds")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the variable-length, decode and FP8 measurements")
+                    help="skip the forward-choice, variable-length, grouped, decode and FP8 "
+                         "measurements")
     ap.add_argument("--cpu-heads", type=int, default=16)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device-to-device copy of MIB MiB (read MIB, write MIB) "
@@ -501,6 +549,8 @@ def main() -> int:
         del ows
     out["bwd"]["workspace_bytes"] = ws_bytes
     if not args.no_extras:
+        log("forward choices: exp2 polynomial share, rescale-heavy inputs")
+        out["fwd_choices"] = bench_fwd_choices(fa, torch, dev, stream, P, w)
         out["extras"] = {"varlen_fwd": bench_varlen(fa, torch, dev, stream),
                          "varlen_bwd": bench_varlen_bwd(fa, torch, dev, stream),
                          "grouped_fwd_bwd": bench_grouped(fa, torch, dev, stream),
