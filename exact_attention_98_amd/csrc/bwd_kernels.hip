@@ -661,8 +661,8 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Warp-specialized main backward kernel, D = 128 (dense; dQ modes stored and
-// recompute).  Same work item as bwd_main_kernel -- (batch, K/V head, 128-key
+// Warp-specialized main backward kernel, D = 64 or 128 (dQ modes stored and
+// recompute; dense, or packed sequences in the recompute mode).  Same work item as bwd_main_kernel -- (batch, K/V head, 128-key
 // tile), every query step of every query head of the group -- with 8 waves in
 // two roles over the same step tiles:
 //   score waves 0..3 (keys 32 w): the MFMA unit forms S, dP of step i+1 while
@@ -680,12 +680,12 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
 // LSE and Delta), i+1 (row reads), i+2 .. i+4 (copies in flight, three steps
 // of latency hidden).  Only the gradient waves copy step tiles in; only the
 // score waves store dS, each half block as soon as it is packed.
-template <bool CAUSAL, int DQM, bool VARLEN>
+template <int D, bool CAUSAL, int DQM, bool VARLEN>
 __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, BwdParams p) {
-  constexpr int D = 128;
+  static_assert(D == 64 || D == 128, "D = 64 or 128");
   constexpr int NW = 8;
   constexpr int BN = kBwdBN;
   constexpr int RB = D * 2;
@@ -693,6 +693,7 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
   constexpr int QS = 32;              // queries per step
   constexpr int ND = D / 32;          // 32-wide d blocks
   constexpr int T = D / 16;           // k-steps of S and dP
+  constexpr int EPJ = 16 / T;         // elements of P, dS formed per S/dP MFMA pair
   constexpr int TB = QS * RB;         // bytes of one Q (or dO) step tile
   constexpr int NLD = TB / 1024 / 4;  // 1 KiB direct loads per gradient wave and tensor
   constexpr bool STORE_DS = DQM == kDqStored;
@@ -936,7 +937,7 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
         sn = mfma32(opA[j], kB[j], sn);
         dn = mfma32(opB[j], vB[j], dn);
 #pragma unroll
-        for (int r = 2 * j; r < 2 * j + 2; ++r) {
+        for (int r = EPJ * j; r < EPJ * (j + 1); ++r) {
           const float pv = exp2_hw(__builtin_fmaf(sv[r], p.c, -lc[r >> 2][r & 3]));
           sv[r] = pv;
           dv[r] = pv * (dv[r] - dc[r >> 2][r & 3]);
@@ -1526,16 +1527,23 @@ __global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(const float* __restr
   ((u32x2*)(which ? dv : dk))[j] = w;
 }
 
-// D = 128 in the fixed-order dQ modes: the warp-specialized kernel.
+// The warp-specialized kernel runs the fixed-order dQ modes at D = 128 and the
+// recompute mode at D = 64.  At D = 64 a step has half the matrix work per dS
+// block, and in the stored mode the score waves' dS stores (2x the bytes per
+// flop of D = 128) stall them: 27% slower than bwd_main_kernel there, 8% faster
+// in the recompute mode (B2 H16 N16384 causal).
 constexpr bool kBwdSplitRoles = true;
-template <bool CAUSAL, int DQM>
+constexpr bool use_ws(int D, int deterministic) {
+  return kBwdSplitRoles && (deterministic == kDqRecompute || (D == 128 && deterministic == kDqStored));
+}
+template <int D, bool CAUSAL, int DQM>
 hipError_t launch_ws_t(const BwdArgs& a, const BwdParams& p, hipStream_t s) {
   const dim3 grid((unsigned)(a.B * a.Hkv * p.nkb * p.hsplit));
-  hipLaunchKernelGGL((bwd_ws_kernel<CAUSAL, DQM, false>), grid, dim3(512), 0, s, (const uint16_t*)a.q,
+  hipLaunchKernelGGL((bwd_ws_kernel<D, CAUSAL, DQM, false>), grid, dim3(512), 0, s, (const uint16_t*)a.q,
                      (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
                      (uint16_t*)a.dk, (uint16_t*)a.dv, p);
   if (p.hsplit > 1) {
-    const size_t n4 = (size_t)a.B * a.Hkv * a.N * 128 / 4;
+    const size_t n4 = (size_t)a.B * a.Hkv * a.N * D / 4;
     hipLaunchKernelGGL(bwd_kv_reduce_kernel, dim3((unsigned)((2 * n4 + 255) / 256)), dim3(256), 0,
                        s, (const float*)p.kv_part, (uint16_t*)a.dk, (uint16_t*)a.dv, n4, p.hsplit);
   }
@@ -1545,10 +1553,12 @@ hipError_t launch_ws_t(const BwdArgs& a, const BwdParams& p, hipStream_t s) {
 template <int D>
 hipError_t launch_main_d(const BwdArgs& a, hipStream_t s) {
   const BwdParams p = make_params(a);
-  if (kBwdSplitRoles && D == 128 && a.deterministic != kDqAtomic) {
-    if (a.deterministic == kDqStored)
-      return a.causal ? launch_ws_t<true, kDqStored>(a, p, s) : launch_ws_t<false, kDqStored>(a, p, s);
-    return a.causal ? launch_ws_t<true, kDqRecompute>(a, p, s) : launch_ws_t<false, kDqRecompute>(a, p, s);
+  if (use_ws(D, a.deterministic)) {
+    if constexpr (D == 128)
+      if (a.deterministic == kDqStored)
+        return a.causal ? launch_ws_t<D, true, kDqStored>(a, p, s) : launch_ws_t<D, false, kDqStored>(a, p, s);
+    return a.causal ? launch_ws_t<D, true, kDqRecompute>(a, p, s)
+                    : launch_ws_t<D, false, kDqRecompute>(a, p, s);
   }
   switch (a.deterministic) {
     case kDqAtomic:
@@ -1621,9 +1631,9 @@ hipError_t launch_bwd_varlen_t(const BwdArgs& a, const VarlenArgs& v, hipStream_
   p.kv_part = nullptr;
   p.items = main_items;
   p.n_items = main_n;
-  if (kBwdSplitRoles && D == 128 && a.deterministic == kDqRecompute) {
+  if (use_ws(D, a.deterministic)) {
     // The warp-specialized kernel over the same (sequence, key tile) list.
-    hipLaunchKernelGGL((bwd_ws_kernel<CAUSAL, kDqRecompute, true>), dim3(items_max * (unsigned)a.Hkv),
+    hipLaunchKernelGGL((bwd_ws_kernel<D, CAUSAL, kDqRecompute, true>), dim3(items_max * (unsigned)a.Hkv),
                        dim3(512), 0, s, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, (const uint16_t*)a.dout, (uint16_t*)a.dk,
                        (uint16_t*)a.dv, p);
@@ -1665,7 +1675,7 @@ size_t ds_head_bytes(int N) {
 }
 
 int bwd_head_split(int B, int Hq, int Hkv, int N, int D, int deterministic) {
-  if (!kBwdSplitRoles || D != 128 || deterministic == kDqAtomic) return 1;
+  if (!use_ws(D, deterministic)) return 1;
   const int G = Hq / Hkv;
   const long tiles = (long)B * Hkv * ((N + kBwdBN - 1) / kBwdBN);
   int s = 1;

@@ -80,8 +80,12 @@ def test_full_size_config(name):
             say(f"  mode {det}: {len(digests)} distinct result(s) over {reps} reruns")
             assert len(digests) == 1
         runs[det] = res[0]
-    # Both fixed-order modes own dK and dV the same way: identical bits.
-    assert torch.equal(runs[1][1], runs[2][1]) and torch.equal(runs[1][2], runs[2][2])
+    # At D = 128 both fixed-order modes form dK and dV in the same main kernel:
+    # identical bits.  At D = 64 the stored-dS mode runs the single-role kernel
+    # (64-query steps) and the recompute mode the warp-specialized one (32-query
+    # steps), so their dK, dV sums differ in order; each is checked below.
+    if w.D == 128:
+        assert torch.equal(runs[1][1], runs[2][1]) and torch.equal(runs[1][2], runs[2][2])
     b, h = w.B - 1, w.Hq - 1
     rq, rk, rv = oracle.attention_bwd(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
                                       do[b:b + 1, h:h + 1], w.causal, w.scale)
