@@ -428,7 +428,10 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
                   const char* dsprev, f32x16 (&sv)[NQB], f32x16 (&dv)[NQB], f32x16 (&sn)[NQB],
                   f32x16 (&dn)[NQB], const f32x4 (&lc)[NQB][4], const f32x4 (&dc)[NQB][4],
                   f32x4 (&ln)[NQB][4], f32x4 (&dln)[NQB][4]) {
-    // Step i+1 must be in LDS; step i+2 may still be in flight.
+    // Step i+1 must be in LDS.  __syncthreads' fence then drains the rest as
+    // well (direct-to-LDS copies count in vmcnt): this kernel's stores and
+    // atomics do not complete in order with its copies, so it does not keep
+    // copies in flight across the barrier.
     if (i + 2 < nsteps) wait_all_but_one_step();
     else wait_vmcnt<0>();
     __syncthreads();  // step i+1 visible to all; step i-1's stage and dS^T free
@@ -678,7 +681,8 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
 // kernel, which is what lets two waves live on a SIMD.  One barrier per step.
 // Step tiles rotate through six stages: step i-1 (transposing reads), i (its
 // LSE and Delta), i+1 (row reads), i+2 .. i+4 (copies in flight, three steps
-// of latency hidden).  Only the gradient waves copy step tiles in; only the
+// of latency hidden: the step barrier is lds_barrier, which leaves them in
+// flight; the gradient waves wait for exactly the copies the next step reads).  Only the gradient waves copy step tiles in; only the
 // score waves store dS, each half block as soon as it is packed.
 template <int D, bool CAUSAL, int DQM, bool VARLEN>
 __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
@@ -848,7 +852,7 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
       wait_vmcnt<0>();
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   if (!grad) {
     // ======================= score waves =======================
@@ -894,7 +898,7 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
     // with step i's LSE and Delta in stage `cur`; P, dS to `pbw`.
     auto body = [&](int i, const char* cur, const char* nxt, char* pbw, f32x16& sv, f32x16& dv,
                     f32x16& sn, f32x16& dn) __attribute__((always_inline)) {
-      __syncthreads();
+      lds_barrier();
       if (i >= nsteps) return;
       const int q0 = cur_qs * QS;
       pin(sv);
@@ -1000,7 +1004,7 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
     // Iteration i: dV, dK of step i-1 (tile `prv`, P and dS in `pbr`).
     auto body = [&](int i, const char* prv, const char* pbr, char* ld) __attribute__((always_inline)) {
       wait_step(i);
-      __syncthreads();
+      lds_barrier();
       if (i + 4 < nsteps) issue_next(ld);
       if (i == 0 || i > nsteps) return;
       const char* pr = pbr + kwave * 4096 + lane * 16;

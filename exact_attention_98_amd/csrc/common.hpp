@@ -118,6 +118,20 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
 }
 
+// Workgroup barrier for loops that keep direct-to-LDS copies in flight across
+// it.  __syncthreads' workgroup release fence makes every wave drain vmcnt,
+// and the copies count there, so no copy would outlive the barrier it was
+// issued before.  This barrier waits only for the wave's own LDS reads and
+// writes (lgkmcnt 0).  A wave must already have waited (wait_vmcnt) for the
+// copies whose data other waves read after the barrier.  The empty asm
+// statements stop the compiler from moving memory operations across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited for
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ---- LDS transposing read -------------------------------------------------------
 // ds_read_b64_tr_b16: in each group of 16 lanes, lane j supplies the address of
 // 4 consecutive bf16 (8 bytes); lane i receives element i % 4 of the chunks
