@@ -132,6 +132,20 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Wait for all of this wave's LDS reads and writes (vmcnt, expcnt not waited for).
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Workgroup barrier with no wait at all, for loops whose waves write LDS only
+// by direct copies (waited for with wait_vmcnt before it) and whose LDS reads
+// still in flight at the barrier are of buffers that no copy issued after it
+// overwrites.  The empty asm statements stop the compiler from moving memory
+// operations across it.
+__device__ __forceinline__ void plain_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ---- LDS transposing read -------------------------------------------------------
 // ds_read_b64_tr_b16: in each group of 16 lanes, lane j supplies the address of
 // 4 consecutive bf16 (8 bytes); lane i receives element i % 4 of the chunks
