@@ -77,11 +77,12 @@ constexpr int kDqAtomic = 0;     // main kernel adds dS K into an fp32 buffer
 constexpr int kDqStored = 1;     // main kernel stores dS; a fixed-order pass forms dS K
 constexpr int kDqRecompute = 2;  // a fixed-order pass recomputes S, dP, dS and forms dS K
 
-// Stored-dS layout: per (b, hq), block (query block qb32, key block kb32) of
-// 32 x 32 at byte (qb32 * nb32 + kb32) * 2048, as dS^T: 32 rows of keys, 64
-// bytes each.  Within a row, position p = 16u + 8h + i holds query
-// 16u + 4h + (i & 3) + 8 (i >> 2) of the block (the order of the main
-// kernel's MFMA A-operand registers, stored unchanged).
+// Stored-dS layout: per (b, hq), the 32 x 32 dS^T block (query block qb32,
+// key block kb32) at byte (qb32 * nb32 + kb32) * 2048.  Within a block, key
+// row r's query positions 16u + 8h .. +8 are the 16-byte chunk 64u + 32h + r,
+// and position p = 16u + 8h + i holds query 16u + 4h + (i & 3) + 8 (i >> 2)
+// of the block (the order of the main kernel's MFMA A-operand registers,
+// stored unchanged).
 
 // ---------------------------------------------------------------------------
 // Preprocess: Delta_i = sum_d dO[i,d] O[i,d] (fp32), LSE_i * log2(e), and

@@ -135,11 +135,11 @@ __device__ __forceinline__ void lds_barrier() {
 // Wait for all of this wave's LDS reads and writes (vmcnt, expcnt not waited for).
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-// Workgroup barrier with no wait at all, for loops whose waves write LDS only
-// by direct copies (waited for with wait_vmcnt before it) and whose LDS reads
-// still in flight at the barrier are of buffers that no copy issued after it
-// overwrites.  The empty asm statements stop the compiler from moving memory
-// operations across it.
+// Workgroup barrier with no wait at all.  Before it each wave must have waited
+// for its own LDS writes (wait_lgkmcnt0) and for the copies whose data other
+// waves read after it (wait_vmcnt); LDS reads it leaves in flight must be of
+// buffers that nothing writes after it.  The empty asm statements stop the
+// compiler from moving memory operations across it.
 __device__ __forceinline__ void plain_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
