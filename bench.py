@@ -365,6 +365,84 @@ def bench_fwd_choices(fa, torch, dev, stream, P, w, reps: int = 20, rounds: int 
                              "variant_b_tflops": tf(med["variant_b"])}}
 
 
+def bench_other_configs(fa, torch, dev, stream, reps: int = 5) -> dict:
+    """Throughput at the other configurations the parity tests cover (inputs
+    seeded N(0,1), drawn on the device): the non-causal forward B4 H16 N2048
+    D128, the multi-query and grouped causal forwards B1 Hq32 Hkv1 / Hkv8
+    N32768 D128, and the causal backward B2 H16 N16384 D64 in its two
+    fixed-order dQ modes (whole fa_bwd call)."""
+    sh = stream.cuda_stream
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+
+    def rnd(*shape):
+        return torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+
+    def timed(call):
+        for _ in range(2):
+            call()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    def line(name, us, flops):
+        tf = flops / (us * 1e-6) / 1e12
+        return {"workload": name, "us": round(us, 1), "tflops": round(tf, 1),
+                "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
+
+    out = {}
+    for key, (B, Hq, Hkv, N, D, causal) in {
+            "fwd_noncausal_B4H16N2048D128": (4, 16, 16, 2048, 128, False),
+            "fwd_mqa_B1Hq32Hkv1N32768D128": (1, 32, 1, 32768, 128, True),
+            "fwd_gqa_B1Hq32Hkv8N32768D128": (1, 32, 8, 32768, 128, True)}.items():
+        q, k, v = rnd(B, Hq, N, D), rnd(B, Hkv, N, D), rnd(B, Hkv, N, D)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+        scale = 1.0 / math.sqrt(D)
+
+        def call():
+            rc = fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, Hq,
+                           Hkv, N, D, int(causal), scale, sh)
+            if rc != 0:
+                raise RuntimeError(f"fa_fwd: {fa.fa_strerror(rc)}")
+
+        flops = 4.0 * B * Hq * N * N * D / (2 if causal else 1)
+        out[key] = line(f"forward B{B} Hq{Hq} Hkv{Hkv} N{N} D{D} {'causal' if causal else 'non-causal'}",
+                        timed(call), flops)
+        del q, k, v, o, lse
+    B, H, N, D = 2, 16, 16384, 64
+    q, k, v, do = rnd(B, H, N, D), rnd(B, H, N, D), rnd(B, H, N, D), rnd(B, H, N, D)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    scale = 1.0 / math.sqrt(D)
+    if fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, H, N, D,
+                 1, scale, sh) != 0:
+        raise RuntimeError("fa_fwd failed")
+    for det, tag in ((1, "stored"), (2, "recompute")):
+        wsb = fa.fa_bwd_workspace_size(B, H, H, N, D, det)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+        def call():
+            rc = fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                           do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, H, N, D, 1,
+                           scale, ws.data_ptr(), wsb, det, sh)
+            if rc != 0:
+                raise RuntimeError(f"fa_bwd: {fa.fa_strerror(rc)}")
+
+        out[f"bwd_{tag}_B2H16N16384D64"] = line(
+            f"backward B{B} H{H} N{N} D{D} causal, dQ mode {det} ({tag}), whole fa_bwd",
+            timed(call), 2.5 * 4.0 * B * H * N * N * D / 2)
+        del ws
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -376,8 +454,8 @@ def main() -> int:
                          "workspace), or atomic adds")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the forward-choice, variable-length, grouped, decode and FP8 "
-                         "measurements")
+                    help="skip the forward-choice, variable-length, grouped, decode, FP8 and "
+                         "other-configuration measurements")
     ap.add_argument("--cpu-heads", type=int, default=16)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device-to-device copy of MIB MiB (read MIB, write MIB) "
@@ -555,7 +633,8 @@ def main() -> int:
                          "varlen_bwd": bench_varlen_bwd(fa, torch, dev, stream),
                          "grouped_fwd_bwd": bench_grouped(fa, torch, dev, stream),
                          "decode_splitkv": bench_decode(fa, torch, dev, stream),
-                         "fp8_fwd": bench_fp8(fa, torch, dev, stream, P, w)}
+                         "fp8_fwd": bench_fp8(fa, torch, dev, stream, P, w),
+                         "other_configs": bench_other_configs(fa, torch, dev, stream)}
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_heads} heads")
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
