@@ -126,13 +126,14 @@ def test_padding_keys_with_very_negative_scores(D, deterministic):
     check_grad(dv, rv, "dV")
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("mode", [1, 2])
 @pytest.mark.parametrize("B,Hq,Hkv,N", [(1, 8, 1, 300), (2, 16, 2, 1000)])
-def test_grouped_heads_split_across_workgroups(B, Hq, Hkv, N, mode):
-    # Few K/V tiles per head group: the main kernel cuts each group's query
-    # heads into parts (fp32 partial dK, dV summed in part order by a second
-    # pass).  Parity with the oracle, and bitwise repeatable.
-    D = 128
+def test_grouped_heads_split_across_workgroups(B, Hq, Hkv, N, mode, D):
+    # Few K/V tiles per head group: the warp-specialized main kernel (D = 128
+    # both modes, D = 64 recompute mode) cuts each group's query heads into
+    # parts (fp32 partial dK, dV summed in part order by a second pass).
+    # Parity with the oracle, and bitwise repeatable.
     say(f"bwd grouped heads split B{B} Hq{Hq} Hkv{Hkv} N{N} D{D} causal mode {mode} x3")
     q, k, v, do = synth.generate(B, Hq, Hkv, N, D, seed=N + Hq, with_dout=True)
     scale = 1.0 / math.sqrt(D)
