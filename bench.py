@@ -483,7 +483,10 @@ def main() -> int:
     w = synth.WORKLOADS["bwd_d128"]  # B2 H16 N8192 D128 causal, with dO
     B, Hq, Hkv, N, D = w.B, w.Hq, w.Hkv, w.N, w.D
     log(f"generating inputs B{B} H{Hq} N{N} D{D} causal (seed 0)")
-    q, k, v, do = (t.to(dev) for t in synth.generate_workload(w))
+    host = synth.generate_workload(w)
+    input_sha = {n: synth.sha256(t) for n, t in zip(("q", "k", "v", "dout"), host)}
+    q, k, v, do = (t.to(dev) for t in host)
+    del host
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -588,7 +591,7 @@ def main() -> int:
         "config": {"workload": "attention forward+backward, B2 Hq16 Hkv16 N8192 D128 causal",
                    "B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "D": D, "causal": True,
                    "dq_accumulation": DQ_LABEL[det],
-                   "flops_per_step": f_fwd + f_bwd},
+                   "flops_per_step": f_fwd + f_bwd, "input_sha256": input_sha},
         "roofline": roofline,
         "fwd": {"tflops": round(fwd_tf, 1), "frac_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
                 "us": round(per_kernel["fwd_kernel"] * 1e3, 1)},
