@@ -300,12 +300,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(const uint16_t* __
     // MFMAs never accumulate into the same registers.  The K fragments are
     // read PDA k-steps ahead of their MFMAs.
     auto kread = [&](int j, int sb) { return as_bf16x8(*(const u32x4*)(kn + sb * 32 * RB + k_off[j])); };
-    // Ping-pong: phase A runs at raised wave priority, so when both waves of
-    // a SIMD are ready, the one forming S(kt+1) and the exponentials issues
-    // first and the other wave's P V products fill in behind it (1-3% faster
-    // at D = 128 and D = 64 than equal priorities; priority during phase B
-    // instead gave nothing).
-    if constexpr (PING) __builtin_amdgcn_s_setprio(1);
+    // Phase A runs at raised wave priority, so when both waves of a SIMD are
+    // ready, the one forming S(kt+1) and the exponentials issues first and
+    // the other wave's P V products fill in behind it (dense 8-wave form 1-3%
+    // faster at D = 128 and D = 64, variable-length form 2.5%, split-KV equal;
+    // priority during phase B instead gave nothing).
+    __builtin_amdgcn_s_setprio(1);
     bf16x8 kq[PDA][2];
 #pragma unroll
     for (int j = 0; j < PDA; ++j) {
@@ -339,7 +339,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(const uint16_t* __
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    if constexpr (PING) __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_s_setprio(0);
     mask(kt + 1, sn);
   };
 
