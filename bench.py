@@ -560,6 +560,17 @@ def main() -> int:
     for n, t in per_kernel.items():
         log(f"  {n}: {t * 1e3:.1f} us/launch")
 
+    def spread(us):
+        """Median, min and max over the timed steps (microseconds)."""
+        us = sorted(us)
+        mid = len(us) // 2
+        med = us[mid] if len(us) % 2 else 0.5 * (us[mid - 1] + us[mid])
+        return {"median": round(med, 1), "min": round(us[0], 1), "max": round(us[-1], 1)}
+
+    fwd_steps = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
+    bwd_steps = [e[1].elapsed_time(e[4]) * 1e3 for e in evs]
+    step_steps = [e[0].elapsed_time(e[4]) * 1e3 for e in evs]
+
     f_fwd, f_bwd = w.flops_fwd(), w.flops_bwd()
     value = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
     fwd_tf = f_fwd / (per_kernel["fwd_kernel"] * 1e-3) / 1e12
@@ -594,11 +605,12 @@ def main() -> int:
                    "flops_per_step": f_fwd + f_bwd, "input_sha256": input_sha},
         "roofline": roofline,
         "fwd": {"tflops": round(fwd_tf, 1), "frac_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
-                "us": round(per_kernel["fwd_kernel"] * 1e3, 1)},
+                "us": round(per_kernel["fwd_kernel"] * 1e3, 1), "us_spread": spread(fwd_steps)},
         "bwd": {"tflops": round(bwd_tf, 1), "frac_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
-                "us": round(bwd_ms * 1e3, 1),
+                "us": round(bwd_ms * 1e3, 1), "us_spread": spread(bwd_steps),
                 "kernels_us": {n: round(per_kernel[n] * 1e3, 1)
                                for n in names[1:]}},
+        "step_us_spread": spread(step_steps),
         "host_wall_ms_per_step": round(wall / args.steps * 1e3, 4),
     }
     # The other dQ modes, timed on the same inputs for comparison (whole
