@@ -91,7 +91,40 @@ def cpu_baseline(w, n_heads: int):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle",
             "sample": f"fp64 forward+backward of {n_heads} of the {w.B * w.Hq} (batch, head) "
-                      f"slices (N={w.N}, D={w.D}, causal), {dt:.1f} s wall"}
+                      f"slices (N={w.N}, D={w.D}, causal), {dt:.1f} s wall",
+            "cpu_model": cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "tiny_single_thread": tiny_single_thread()}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def tiny_single_thread() -> dict:
+    """The oracle's forward on the tiny workload (B1 H1 N256 D64, non-causal)
+    on one OpenMP thread (set through the oracle library, then restored)."""
+    import oracle
+    import synth
+    w = synth.WORKLOADS["tiny"]
+    q, k, v = synth.generate_workload(w)
+    before = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        oracle.attention_fwd(q, k, v, w.causal, w.scale)
+        t0 = time.perf_counter()
+        oracle.attention_fwd(q, k, v, w.causal, w.scale)
+        sec = time.perf_counter() - t0
+        threads = oracle.num_threads()
+    finally:
+        oracle.set_num_threads(before)
+    return {"seconds": round(sec, 4), "threads": threads, "gflops": round(w.flops_fwd() / sec / 1e9, 2)}
 
 
 def bench_varlen(fa, torch, dev, stream, reps: int = 20) -> dict:

@@ -57,6 +57,8 @@ def _load():
         lib.oracle_bwd.restype = ci
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ci
+        lib.oracle_set_num_threads.argtypes = [ci]
+        lib.oracle_set_num_threads.restype = None
         _lib = lib
     return _lib
 
@@ -64,6 +66,11 @@ def _load():
 def num_threads() -> int:
     """OpenMP threads the oracle runs with."""
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """OpenMP threads for the following oracle calls (timing only)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def _bits(t: torch.Tensor) -> np.ndarray:

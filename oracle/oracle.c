@@ -93,6 +93,15 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Threads for the following calls (timing only; the results do not depend on it). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 static int check_shape(int B, int Hq, int Hkv, int Nq, int Nk, int D) {
     if (B < 0 || Hq < 1 || Hkv < 1 || Nq < 0 || Nk < 0 || D < 1) return -1;
     if (Hq % Hkv != 0) return -1;
