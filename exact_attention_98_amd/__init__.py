@@ -18,7 +18,7 @@ __all__ = ["fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_workspace_size", "fa_bwd_pre
            "fa_bwd_main", "fa_bwd_dq", "fa_fwd_varlen", "fa_fwd_varlen_workspace_size",
            "fa_varlen_max_seqlen", "fa_fwd_splitkv", "fa_fwd_splitkv_num_splits",
            "fa_fwd_splitkv_workspace_size", "fa_bwd_varlen", "fa_bwd_varlen_workspace_size",
-           "fa_fwd_fp8", "fa_fwd_fp8_workspace_size", "fa_strerror", "forward", "backward",
+           "fa_fwd_fp8", "fa_fwd_fp8_workspace_size", "fa_exp2_poly_eval", "fa_strerror", "forward", "backward",
            "forward_varlen", "backward_varlen", "forward_splitkv", "forward_fp8", "FaError",
            "library_path", "load"]
 
@@ -38,7 +38,7 @@ EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_workspace_size", "fa_bwd_pr
             "fa_bwd_main", "fa_bwd_dq", "fa_fwd_varlen", "fa_fwd_varlen_workspace_size",
             "fa_varlen_max_seqlen", "fa_fwd_splitkv", "fa_fwd_splitkv_num_splits",
             "fa_fwd_splitkv_workspace_size", "fa_bwd_varlen", "fa_bwd_varlen_workspace_size",
-            "fa_fwd_fp8", "fa_fwd_fp8_workspace_size", "fa_strerror")
+            "fa_fwd_fp8", "fa_fwd_fp8_workspace_size", "fa_exp2_poly_eval", "fa_strerror")
 
 
 class FaError(RuntimeError):
@@ -98,6 +98,8 @@ def load():
     lib.fa_fwd_fp8_workspace_size.restype = sz
     lib.fa_fwd_fp8.argtypes = [vp] * 5 + [ci] * 6 + [cf, vp, vp, sz, vp]
     lib.fa_fwd_fp8.restype = ci
+    lib.fa_exp2_poly_eval.argtypes = [vp, vp, ci, vp]
+    lib.fa_exp2_poly_eval.restype = ci
     lib.fa_strerror.argtypes = [ci]
     lib.fa_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -112,6 +114,10 @@ def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, D, causal, scale, stream) -> int:
 def fa_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, N, D, causal, scale, exp_poly_quarters, stream) -> int:
     return load().fa_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, N, D, int(causal), float(scale),
                             int(exp_poly_quarters), stream)
+
+
+def fa_exp2_poly_eval(x, y, n, stream) -> int:
+    return load().fa_exp2_poly_eval(x, y, int(n), stream)
 
 
 def fa_bwd_workspace_size(B, Hq, Hkv, N, D, deterministic) -> int:

@@ -85,6 +85,11 @@ size_t fa_fwd_varlen_workspace_size(int B, int total) {
 
 int fa_varlen_max_seqlen(void) { return fa::varlen_max_seqlen_limit(); }
 
+int fa_exp2_poly_eval(const float* x, float* y, int n, void* stream) {
+  if (n < 0 || (n > 0 && (!x || !y))) return FA_ERR_INVALID;
+  return fa::launch_exp2_poly_eval(x, y, n, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                   const int* cu_seqlens, int B, int Hq, int Hkv, int total, int max_seqlen, int D,
                   int causal, float scale, void* workspace, size_t workspace_bytes,

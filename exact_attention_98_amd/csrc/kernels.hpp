@@ -42,6 +42,8 @@ struct FwdParams {
 };
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+// y[i] = exp2_poly(x[i]) on the device (the forward's FMA-only exp2).
+hipError_t launch_exp2_poly_eval(const float* x, float* y, int n, hipStream_t stream);
 
 // Variable-length forward.  Layout: q, o [Hq][total][D]; k, v [Hkv][total][D];
 // lse [Hq][total]; sequence b is rows cu[b] .. cu[b+1] of every head.

@@ -253,6 +253,17 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                int Hkv, int N, int D, int causal, float scale, const float* signs,
                void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Diagnostic: y[i] = the forward's FMA-only exp2 of x[i] (2^n times the cubic
+ * in the fraction, n = floor(x); the polynomial share of fa_fwd_ex; hotelren
+ * FlashAttention-4 summary, section 3.2), evaluated on the device exactly as
+ * the forward kernel evaluates it, so a test can compare it bit for bit with
+ * a host evaluation.  x, y: device float[n] (may alias), n >= 0; nothing is
+ * launched for n = 0.  Returns FA_ERR_INVALID for n < 0 or a null pointer
+ * with n > 0, FA_ERR_HIP if the launch fails.
+ */
+int fa_exp2_poly_eval(const float* x, float* y, int n, void* stream);
+
 /* Static text for a status code. */
 const char* fa_strerror(int status);
 

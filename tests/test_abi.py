@@ -236,3 +236,10 @@ def test_bwd_varlen_sizes_and_empty_batch():
     s0 = fa.fa_bwd_varlen_workspace_size(3, 2, 1, 500, 128, 0)
     s2 = fa.fa_bwd_varlen_workspace_size(3, 2, 1, 500, 128, 2)
     assert s0 >= 2 * 500 * 128 * 4 and s2 < s0
+
+
+def test_exp2_poly_eval_argument_checks():
+    # Rejected before any launch (no GPU needed); n = 0 launches nothing.
+    assert fa.fa_exp2_poly_eval(None, None, -1, None) == fa.FA_ERR_INVALID
+    assert fa.fa_exp2_poly_eval(None, None, 4, None) == fa.FA_ERR_INVALID
+    assert fa.fa_exp2_poly_eval(None, None, 0, None) == fa.FA_OK
