@@ -803,13 +803,13 @@ hipError_t launch_fwd_varlen(const FwdArgs& a, const VarlenArgs& v, hipStream_t 
 // The forward's FMA-only exp2 on an array, for host-side bit-for-bit checks.
 __global__ __launch_bounds__(256) void exp2_poly_eval_kernel(const float* __restrict__ x,
                                                              float* __restrict__ y, int n) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n) y[i] = exp2_poly(x[i]);
+  const unsigned i = blockIdx.x * 256u + threadIdx.x;  // n <= INT_MAX, so this does not wrap
+  if (i < (unsigned)n) y[i] = exp2_poly(x[i]);
 }
 
 hipError_t launch_exp2_poly_eval(const float* x, float* y, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(exp2_poly_eval_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, y, n);
+  hipLaunchKernelGGL(exp2_poly_eval_kernel, dim3((unsigned)(((long long)n + 255) / 256)), dim3(256), 0, s, x, y, n);
   return hipGetLastError();
 }
 
