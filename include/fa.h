@@ -48,8 +48,8 @@ extern "C" {
 
 typedef enum {
     FA_OK = 0,
-    FA_ERR_INVALID = -1,     /* null pointer, non-positive size, Hq % Hkv != 0, non-finite or non-positive scale, aliasing */
-    FA_ERR_UNSUPPORTED = -2, /* valid request this build does not handle (e.g. D not in {64,128}) */
+    FA_ERR_INVALID = -1,     /* null pointer, non-positive size, Hq % Hkv != 0, non-finite scale, aliasing */
+    FA_ERR_UNSUPPORTED = -2, /* valid request this build does not handle (D not in {64,128}, scale <= 0) */
     FA_ERR_ALIGN = -3,       /* a pointer is not 16-byte aligned */
     FA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than fa_bwd_workspace_size() */
     FA_ERR_HIP = -5,         /* the HIP runtime reported an error at launch */
@@ -60,7 +60,8 @@ typedef enum {
  * Forward pass.
  *   q [B][Hq][N][D], k/v [B][Hkv][N][D] (bf16, read)
  *   o [B][Hq][N][D] (bf16, written), lse [B][Hq][N] (fp32, written)
- *   scale: the softmax scale (typically 1/sqrt(D)), finite and > 0.
+ *   scale: the softmax scale (typically 1/sqrt(D)), finite and > 0
+ *   (non-finite: FA_ERR_INVALID; zero or negative: FA_ERR_UNSUPPORTED).
  * o must not overlap q, k or v.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
