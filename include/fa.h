@@ -49,7 +49,7 @@ extern "C" {
 typedef enum {
     FA_OK = 0,
     FA_ERR_INVALID = -1,     /* null pointer, non-positive size, Hq % Hkv != 0, non-finite scale, aliasing */
-    FA_ERR_UNSUPPORTED = -2, /* valid request this build does not handle (D not in {64,128}, scale <= 0) */
+    FA_ERR_UNSUPPORTED = -2, /* valid request the library does not handle (D not in {64,128}, scale <= 0) */
     FA_ERR_ALIGN = -3,       /* a pointer is not 16-byte aligned */
     FA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than fa_bwd_workspace_size() */
     FA_ERR_HIP = -5,         /* the HIP runtime reported an error at launch */
