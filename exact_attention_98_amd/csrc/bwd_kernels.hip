@@ -397,8 +397,10 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
         const uint32_t off = ok ? (uint32_t)(qb32 * p.nb32 + kb32) * 2048u : 0xFFFFF000u;
 #pragma unroll
         for (int u = 0; u < 2; ++u)
-          // Plain (cached) stores: measured faster here than non-temporal ones.
-          __builtin_amdgcn_raw_buffer_store_b128(ds_keep[qb][u], r, off + ds_lane + 1024u * u, 0, 0);
+          // Non-temporal stores (cache policy NT): dS is read once, by the
+          // dQ pass, so the caches keep K, V and the step tiles instead, and
+          // the dQ pass does not first write back lines left dirty here.
+          __builtin_amdgcn_raw_buffer_store_b128(ds_keep[qb][u], r, off + ds_lane + 1024u * u, 0, 2);
       }
     }
   };
@@ -886,7 +888,8 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
         const rsrc_t r = make_rsrc_uniform(p.ds + ((size_t)b * p.Hq + hq0 + cur_g) * p.ds_head, p.ds_head);
         const bool ok = cur_qs < p.nb32 && kb32 < p.nb32 && (!CAUSAL || kb32 <= cur_qs);
         const uint32_t off = ok ? (uint32_t)(cur_qs * p.nb32 + kb32) * 2048u : 0xFFFFF000u;
-        __builtin_amdgcn_raw_buffer_store_b128(w, r, off + ds_lane + 1024u * u, 0, 0);
+        // Non-temporal (NT), as in bwd_main_kernel: dS is read once, later.
+        __builtin_amdgcn_raw_buffer_store_b128(w, r, off + ds_lane + 1024u * u, 0, 2);
       }
     };
 
