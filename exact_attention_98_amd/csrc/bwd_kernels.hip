@@ -400,7 +400,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
           // Non-temporal stores (cache policy NT): dS is read once, by the
           // dQ pass, so the caches keep K, V and the step tiles instead, and
           // the dQ pass does not first write back lines left dirty here.
-          __builtin_amdgcn_raw_buffer_store_b128(ds_keep[qb][u], r, off + ds_lane + 1024u * u, 0, 2);
+          __builtin_amdgcn_raw_buffer_store_b128(ds_keep[qb][u], r, off + ds_lane + 1024u * u, 0, kCachePolicyNT);
       }
     }
   };
@@ -889,7 +889,7 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
         const bool ok = cur_qs < p.nb32 && kb32 < p.nb32 && (!CAUSAL || kb32 <= cur_qs);
         const uint32_t off = ok ? (uint32_t)(cur_qs * p.nb32 + kb32) * 2048u : 0xFFFFF000u;
         // Non-temporal (NT), as in bwd_main_kernel: dS is read once, later.
-        __builtin_amdgcn_raw_buffer_store_b128(w, r, off + ds_lane + 1024u * u, 0, 2);
+        __builtin_amdgcn_raw_buffer_store_b128(w, r, off + ds_lane + 1024u * u, 0, kCachePolicyNT);
       }
     };
 
