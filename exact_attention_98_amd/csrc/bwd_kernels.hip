@@ -1570,14 +1570,14 @@ __global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(const float* __restr
   ((u32x2*)(which ? dv : dk))[j] = w;
 }
 
-// The warp-specialized kernel runs the fixed-order dQ modes at D = 128 and the
-// recompute mode at D = 64.  At D = 64 a step has half the matrix work per dS
-// block, and in the stored mode the score waves' dS stores (2x the bytes per
-// flop of D = 128) stall them: 27% slower than bwd_main_kernel there, 8% faster
-// in the recompute mode (B2 H16 N16384 causal).
+// The warp-specialized kernel runs both fixed-order dQ modes, at D = 64 and
+// 128.  At D = 64 (B2 H16 N16384 causal) it is 4% faster than bwd_main_kernel
+// in the stored mode, now that the dS stores are non-temporal (27% slower with
+// cached ones), and 8% faster in the recompute mode.
 constexpr bool kBwdSplitRoles = true;
 constexpr bool use_ws(int D, int deterministic) {
-  return kBwdSplitRoles && (deterministic == kDqRecompute || (D == 128 && deterministic == kDqStored));
+  (void)D;
+  return kBwdSplitRoles && (deterministic == kDqRecompute || deterministic == kDqStored);
 }
 template <int D, bool CAUSAL, int DQM>
 hipError_t launch_ws_t(const BwdArgs& a, const BwdParams& p, hipStream_t s) {
@@ -1597,9 +1597,8 @@ template <int D>
 hipError_t launch_main_d(const BwdArgs& a, hipStream_t s) {
   const BwdParams p = make_params(a);
   if (use_ws(D, a.deterministic)) {
-    if constexpr (D == 128)
-      if (a.deterministic == kDqStored)
-        return a.causal ? launch_ws_t<D, true, kDqStored>(a, p, s) : launch_ws_t<D, false, kDqStored>(a, p, s);
+    if (a.deterministic == kDqStored)
+      return a.causal ? launch_ws_t<D, true, kDqStored>(a, p, s) : launch_ws_t<D, false, kDqStored>(a, p, s);
     return a.causal ? launch_ws_t<D, true, kDqRecompute>(a, p, s)
                     : launch_ws_t<D, false, kDqRecompute>(a, p, s);
   }

@@ -83,9 +83,8 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
  * Bytes of device workspace fa_bwd needs for this problem and dQ mode
  * (deterministic, see fa_bwd): per-row Delta = rowsum(dO * O) and
  * LSE * log2(e), plus the fp32 dQ accumulator (mode 0) or the bf16 dS blocks
- * (mode 1); with grouped heads (Hq > Hkv), in modes 1 and 2 at D = 128 and
- * mode 2 at D = 64, when B * Hkv * ceil(N / 128) is small the query heads of
- * each group are split
+ * (mode 1); with grouped heads (Hq > Hkv), in modes 1 and 2, when
+ * B * Hkv * ceil(N / 128) is small the query heads of each group are split
  * over several workgroups and the workspace also holds their fp32 partial dK
  * and dV (at most 2 * Hq/Hkv * B * Hkv * N * D * 4 bytes more).  Returns 0 for
  * invalid sizes or modes.

@@ -80,12 +80,9 @@ def test_full_size_config(name):
             say(f"  mode {det}: {len(digests)} distinct result(s) over {reps} reruns")
             assert len(digests) == 1
         runs[det] = res[0]
-    # At D = 128 both fixed-order modes form dK and dV in the same main kernel:
-    # identical bits.  At D = 64 the stored-dS mode runs the single-role kernel
-    # (64-query steps) and the recompute mode the warp-specialized one (32-query
-    # steps), so their dK, dV sums differ in order; each is checked below.
-    if w.D == 128:
-        assert torch.equal(runs[1][1], runs[2][1]) and torch.equal(runs[1][2], runs[2][2])
+    # Both fixed-order modes form dK and dV in the same main kernel, in the
+    # same order: identical bits.
+    assert torch.equal(runs[1][1], runs[2][1]) and torch.equal(runs[1][2], runs[2][2])
     b, h = w.B - 1, w.Hq - 1
     rq, rk, rv = oracle.attention_bwd(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
                                       do[b:b + 1, h:h + 1], w.causal, w.scale)
@@ -130,8 +127,8 @@ def test_padding_keys_with_very_negative_scores(D, deterministic):
 @pytest.mark.parametrize("mode", [1, 2])
 @pytest.mark.parametrize("B,Hq,Hkv,N", [(1, 8, 1, 300), (2, 16, 2, 1000)])
 def test_grouped_heads_split_across_workgroups(B, Hq, Hkv, N, mode, D):
-    # Few K/V tiles per head group: the warp-specialized main kernel (D = 128
-    # both modes, D = 64 recompute mode) cuts each group's query heads into
+    # Few K/V tiles per head group: the warp-specialized main kernel (both
+    # fixed-order modes) cuts each group's query heads into
     # parts (fp32 partial dK, dV summed in part order by a second pass).
     # Parity with the oracle, and bitwise repeatable.
     say(f"bwd grouped heads split B{B} Hq{Hq} Hkv{Hkv} N{N} D{D} causal mode {mode} x3")
