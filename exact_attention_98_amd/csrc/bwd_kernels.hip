@@ -685,12 +685,14 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
 // Step tiles rotate through six stages: step i-1 (transposing reads), i (its
 // LSE and Delta), i+1 (row reads), i+2 .. i+4 (copies in flight; the step
 // barrier does not drain them, and the gradient waves wait for exactly the
-// copies that must be complete).  In the stored-dS mode (PREF) step i+2 is
-// complete one step earlier, and the score waves read its first operands and
-// step i+1's row constants before the next barrier, so their products start
-// right after it (2.5% faster there; the recompute mode measured 1.8% slower
-// with it and keeps the later reads).  Only the gradient waves copy step tiles in; only the
-// score waves store dS, each half block as soon as it is packed.
+// copies that must be complete).  In the stored-dS mode at D = 128 (PREF)
+// step i+2 is complete one step earlier, and the score waves read its first
+// operands and step i+1's row constants before the next barrier, so their
+// products start right after it (2.5% faster there with cached dS stores,
+// equal with non-temporal ones; the recompute mode measured 1.8% slower with
+// it, and the stored mode at D = 64 1.3% slower, so they keep the later
+// reads).  Only the gradient waves copy step tiles in; only the score waves
+// store dS, each half block as soon as it is packed.
 template <int D, bool CAUSAL, int DQM, bool VARLEN>
 __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -708,7 +710,7 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
   constexpr int TB = QS * RB;         // bytes of one Q (or dO) step tile
   constexpr int NLD = TB / 1024 / 4;  // 1 KiB direct loads per gradient wave and tensor
   constexpr bool STORE_DS = DQM == kDqStored;
-  constexpr bool PREF = STORE_DS;     // score-wave reads ahead of the barrier
+  constexpr bool PREF = STORE_DS && D == 128;  // score-wave reads ahead of the barrier
   static_assert(NLD >= 1, "step tile too small");
   static_assert(DQM != kDqAtomic, "atomic dQ uses bwd_main_kernel");
   static_assert(!(VARLEN && DQM == kDqStored), "no stored-dS layout for packed sequences");
