@@ -223,7 +223,7 @@ def bench_varlen_bwd(fa, torch, dev, stream, det: int = 2, reps: int = 10) -> di
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
 
 
-def bench_grouped(fa, torch, dev, stream, Hkv: int = 2, reps: int = 5) -> dict:
+def bench_grouped(fa, torch, dev, stream, Hkv: int = 2, reps: int = 10, warmup: int = 3) -> dict:
     """Grouped heads (Hq 16 over Hkv K/V heads) at the headline size: forward
     plus backward (stored-dS dQ mode; dK and dV summed over each group inside
     the main kernel)."""
@@ -253,7 +253,8 @@ def bench_grouped(fa, torch, dev, stream, Hkv: int = 2, reps: int = 5) -> dict:
         if rc != 0:
             raise RuntimeError(f"grouped fwd+bwd: {fa.fa_strerror(rc)}")
 
-    call()
+    for _ in range(warmup):
+        call()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
