@@ -168,3 +168,26 @@ def attention_fwd_rows(q, k, v, causal: bool, scale: float, rows):
         outs.append(o[0, 0, 0])
         lses.append(lse[0, 0, 0])
     return torch.stack(outs), torch.stack(lses)
+
+
+def attention_bwd_dq_rows(q, k, v, dout, causal: bool, scale: float, rows):
+    """dQ of selected query rows only, each computed on its own.
+
+    dQ_i = scale * sum_j dS_ij K_j with dS_ij = P_ij (dP_ij - Delta_i) and
+    Delta_i = sum_j P_ij dP_ij uses row i's scores, dO_i and the keys it sees,
+    nothing of the other rows.  So row i is evaluated as a one-row problem
+    over its key prefix (causal) or all keys, by the full backward above; the
+    dK and dV of that problem are discarded.  ``rows`` is an iterable of
+    (b, hq, i); returns fp64 [len(rows), D].
+    """
+    B, Hq, Hkv, Nq, Nk, D = _dims(q, k)
+    G = Hq // Hkv
+    outs = []
+    for (b, hq, i) in rows:
+        nk = min(i + 1, Nk) if causal else Nk
+        hk = hq // G
+        dq, _, _ = attention_bwd(q[b:b + 1, hq:hq + 1, i:i + 1, :], k[b:b + 1, hk:hk + 1, :nk, :],
+                                 v[b:b + 1, hk:hk + 1, :nk, :], dout[b:b + 1, hq:hq + 1, i:i + 1, :],
+                                 False, scale)
+        outs.append(dq[0, 0, 0])
+    return torch.stack(outs)

@@ -65,19 +65,45 @@ def test_fp8_matches_quantized_oracle(B, Hq, Hkv, N, D, causal, rot):
     check_fp8(o, lse, ro, rl, vmax, "vs quantized oracle")
 
 
-def test_rotation_reduces_error_on_outlier_channels():
-    # Q and K with a few channels 30x larger than the rest: quantizing per
-    # tile then wastes almost all of e4m3's range on them.  The rotation
-    # spreads them, so the FP8 result moves closer to exact attention.
+def _outlier_inputs():
+    # Q and K with three channels 30x larger than the rest: quantizing per
+    # tile then wastes almost all of e4m3's range on them unless the rotation
+    # spreads them over the head dimension first.
     B, H, N, D = 1, 2, 512, 128
-    say("fp8 outliers: error vs exact attention with and without rotation")
     q, k, v = synth.generate(B, H, H, N, D, seed=21)
     q, k = q.float(), k.float()
     for c in (3, 40, 77):
         q[..., c] *= 30.0
         k[..., c] *= 30.0
-    q, k = q.to(torch.bfloat16), k.to(torch.bfloat16)
-    scale = 1.0 / math.sqrt(D) / 10.0
+    return q.to(torch.bfloat16), k.to(torch.bfloat16), v, 1.0 / math.sqrt(D) / 10.0
+
+
+def test_fp8_outlier_channels_match_rotated_oracle():
+    # Element by element against the rotated, quantized oracle, on inputs
+    # where the rotation matters: the unrotated oracle is more than twice the
+    # relative-L2 gate away from the rotated one, so a kernel that skipped or
+    # misplaced the rotation would fail the gate (its own P rounding moves it
+    # by about 2.6e-2 at most).
+    say("fp8 outlier channels B1 H2 N512 D128 causal, rotation on, vs rotated oracle")
+    q, k, v, scale = _outlier_inputs()
+    signs = synth.hadamard_signs(128, seed=5)
+    ro, rl = fp8.attention_fwd_fp8(q, k, v, True, scale, signs=signs)
+    uo, _ = fp8.attention_fwd_fp8(q, k, v, True, scale, signs=None)
+    gap = ((uo - ro).norm() / ro.norm()).item()
+    say(f"  rotated vs unrotated oracle: rel L2 {gap:.3e}")
+    assert gap > 2 * 2 ** -4
+    o, lse = run(q, k, v, True, scale, signs)
+    vmax = float(v.double().abs().max()) * 1.07
+    check_fp8(o, lse, ro, rl, vmax, "outliers vs rotated oracle")
+
+
+def test_rotation_reduces_error_on_outlier_channels():
+    # Q and K with a few channels 30x larger than the rest: quantizing per
+    # tile then wastes almost all of e4m3's range on them.  The rotation
+    # spreads them, so the FP8 result moves closer to exact attention.
+    say("fp8 outliers: error vs exact attention with and without rotation")
+    q, k, v, scale = _outlier_inputs()
+    D = q.shape[-1]
     ro, _ = oracle.attention_fwd(q, k, v, True, scale)
     errs = {}
     for rot in (False, True):

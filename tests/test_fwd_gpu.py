@@ -108,5 +108,9 @@ def test_full_size_config(name):
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
     rows = _sample_rows(w.B, w.Hq, w.N, 48, seed=1)
     _check_rows(o, lse, q, k, v, w, rows, name)
+    # Whole heads: the last (batch, head) of every config (at N = 32768 that
+    # is a grouped head of the multi-query / grouped-query problems), and the
+    # first one as well up to N = 8192.
+    _check_head(o, lse, q, k, v, w, w.B - 1, w.Hq - 1, name)
     if w.N <= 8192:
-        _check_head(o, lse, q, k, v, w, w.B - 1, w.Hq - 1, name)
+        _check_head(o, lse, q, k, v, w, 0, 0, name)

@@ -86,3 +86,63 @@ def test_fp8_attention_close_to_exact_on_plain_inputs():
     o1, l1 = fp8.attention_fwd_fp8(q, k, v, True, 0.125)
     rel = ((o1 - o0).norm() / o0.norm()).item()
     assert 1e-4 < rel < 5e-2
+
+
+def _spike_rows(rng, n, positions, scale_rows=448.0):
+    """Rows of 64 with two spikes: +-448 at one position and +-a at another,
+    a in {40, 96, 160, 224}.  Every value is an e4m3 code and every row's
+    largest magnitude is 448, so a tile of such rows quantizes exactly at
+    factor 1."""
+    y = np.zeros((n, 64))
+    for i in range(n):
+        p1, p2 = rng.choice(positions, size=2, replace=False)
+        y[i, p1] = scale_rows * rng.choice([-1.0, 1.0])
+        y[i, p2] = rng.choice([40.0, 96.0, 160.0, 224.0]) * rng.choice([-1.0, 1.0])
+    return y
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_rotation_applied_before_quantization(causal):
+    # Q and K are built as the inverse rotation of rows whose rotated form is
+    # exactly representable: rotate(Q) = Y with Y made of e4m3 codes at a tile
+    # factor of 1 (Q = fwht(Y) * signs, since the orthonormal transform is its
+    # own inverse, and (448 +- a) / 8 is exact in bf16).  V holds values whose
+    # power-of-two quantization is exact too.  Rotating first and then
+    # quantizing therefore loses nothing, and the FP8 oracle must equal exact
+    # attention on the bf16 inputs.  Quantizing Q and K as given (before the
+    # rotation, or with no rotation) rounds (448 +- a) / 8 at a tile factor of
+    # 448 / 84 and moves the result; both mistakes are built here from the
+    # oracle's own parts and must be told apart.
+    rng = np.random.default_rng(7)
+    D, N = 64, 64
+    signs = np.where(rng.random(D) < 0.5, -1.0, 1.0)
+    positions = np.array([0, 5, 17, 40])
+    yq = _spike_rows(rng, N, positions)
+    yk = _spike_rows(rng, N, positions)
+    qd = fp8.fwht(yq) * signs
+    kd = fp8.fwht(yk) * signs
+    q = torch.from_numpy(qd).reshape(1, 1, N, D).to(torch.bfloat16)
+    k = torch.from_numpy(kd).reshape(1, 1, N, D).to(torch.bfloat16)
+    assert torch.equal(q.double()[0, 0], torch.from_numpy(qd)), "Q must be exact in bf16"
+    assert torch.equal(k.double()[0, 0], torch.from_numpy(kd)), "K must be exact in bf16"
+    vvals = np.array([-1.5, -1.0, -0.5, -0.25, 0.25, 0.5, 1.0, 1.5])
+    v = torch.from_numpy(rng.choice(vvals, size=(1, 1, N, D))).to(torch.bfloat16)
+    scale = 2e-5  # scores Y_q . Y_k of up to ~2.2e5 -> a few units
+
+    exact_o, exact_l = oracle.attention_fwd(q, k, v, causal, scale)
+    o, lse = fp8.attention_fwd_fp8(q, k, v, causal, scale, signs=torch.from_numpy(signs))
+    assert torch.allclose(o, exact_o, rtol=0, atol=1e-9)
+    assert torch.allclose(lse, exact_l, rtol=0, atol=1e-9)
+
+    # The two plausible mistakes, from the same building blocks.
+    qn, kn, vn = (t.double().numpy() for t in (q, k, v))
+    vq = fp8.quantize_pow2(vn)[0]
+    assert np.array_equal(vq, vn)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a))
+    quant_then_rot = oracle.attention_fwd_f64(
+        t(fp8.rotate(fp8.quantize_scaled(qn)[0], signs)),
+        t(fp8.rotate(fp8.quantize_scaled(kn)[0], signs)), t(vq), causal, scale)[0]
+    no_rotation = oracle.attention_fwd_f64(t(fp8.quantize_scaled(qn)[0]),
+                                           t(fp8.quantize_scaled(kn)[0]), t(vq), causal, scale)[0]
+    for wrong in (quant_then_rot, no_rotation):
+        assert (wrong - exact_o).abs().max().item() > 1e-3

@@ -254,6 +254,18 @@ def test_sampled_rows_equal_full():
             assert abs(float(lrow[n] - lse[b, h, i])) < 1e-13
 
 
+def test_sampled_dq_rows_equal_full():
+    # dQ of a row from the one-row problem equals that row of the full
+    # backward (itself pinned to brute force, finite differences and SDPA).
+    q, k, v, do = synth.generate(2, 4, 2, 50, 16, seed=8, with_dout=True)
+    for causal in (False, True):
+        dq, _, _ = oracle.attention_bwd(q, k, v, do, causal, 0.25)
+        rows = [(0, 0, 0), (1, 3, 49), (0, 1, 17), (1, 2, 33), (0, 3, 1)]
+        got = oracle.attention_bwd_dq_rows(q, k, v, do, causal, 0.25, rows)
+        for n, (b, h, i) in enumerate(rows):
+            assert torch.allclose(got[n], dq[b, h, i], rtol=0, atol=1e-13)
+
+
 # --------------------------------------------------------------- worked example
 def test_golden_two_by_two():
     with open(os.path.join(GOLDEN, "two_by_two.json")) as f:
