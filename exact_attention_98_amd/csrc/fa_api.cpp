@@ -34,12 +34,18 @@ int check_shape(int B, int Hq, int Hkv, int N, int D, float scale) {
   return FA_OK;
 }
 
+// Largest byte range of one head's fp32 rows that the kernels address with
+// 32-bit signed offsets (the atomic dQ accumulator, the split-KV partials).
+constexpr uint64_t kMaxFp32HeadBytes = 0x7FFFFFFFull;
+
 // The dQ mode (the deterministic argument): 0 atomic, 1 stored dS, 2
 // recompute.  Stored-dS blocks of one head are addressed with 32-bit offsets,
-// with offsets from 2^32 - 4096 up reserved as "no block".
-int check_mode(int N, int deterministic) {
+// with offsets from 2^32 - 4096 up reserved as "no block"; the atomic mode's
+// fp32 accumulator rows of one head with 32-bit signed offsets.
+int check_mode(int N, int D, int deterministic) {
   if (deterministic < 0 || deterministic > 2) return FA_ERR_INVALID;
   if (deterministic == 1 && fa::ds_head_bytes(N) > 0xFFFFF000ull - 4096) return FA_ERR_TOO_LARGE;
+  if (deterministic == 0 && (uint64_t)N * (uint64_t)D * 4u > kMaxFp32HeadBytes) return FA_ERR_TOO_LARGE;
   return FA_OK;
 }
 
@@ -144,6 +150,14 @@ int resolve_splits(int B, int Hq, int Hkv, int Nq, int Nk, int num_splits) {
   return num_splits;
 }
 
+// With more than one key range, the fp32 partial rows of one K/V head group
+// (G * Nq rows of D) are addressed with 32-bit signed offsets.
+int check_split_partials(int Hq, int Hkv, int Nq, int D, int splits) {
+  if (splits > 1 && (uint64_t)(Hq / Hkv) * (uint64_t)Nq * (uint64_t)D * 4u > kMaxFp32HeadBytes)
+    return FA_ERR_TOO_LARGE;
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -241,6 +255,7 @@ size_t fa_fwd_splitkv_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int
   if (check_split(B, Hq, Hkv, Nq, Nk, D, 0, 1.0f) != FA_OK) return 0;
   const int sp = resolve_splits(B, Hq, Hkv, Nq, Nk, num_splits);
   if (sp < 1) return 0;
+  if (check_split_partials(Hq, Hkv, Nq, D, sp) != FA_OK) return 0;
   return fa::split_workspace_bytes(B, Hq, Nq, D, sp);
 }
 
@@ -252,6 +267,8 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
   if (rc != FA_OK) return rc;
   const int sp = resolve_splits(B, Hq, Hkv, Nq, Nk, num_splits);
   if (sp < 1) return FA_ERR_INVALID;
+  rc = check_split_partials(Hq, Hkv, Nq, D, sp);
+  if (rc != FA_OK) return rc;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA_ERR_ALIGN;
   const size_t wbytes = fa::split_workspace_bytes(B, Hq, Nq, D, sp);
@@ -279,7 +296,7 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
 
 size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int D, int deterministic) {
   if (check_shape(B, Hq, Hkv, N, D, 1.0f) != FA_OK) return 0;
-  if (check_mode(N, deterministic) != FA_OK) return 0;
+  if (check_mode(N, D, deterministic) != FA_OK) return 0;
   return fa::bwd_layout(B, Hq, Hkv, N, D, deterministic).total;
 }
 
@@ -304,7 +321,7 @@ int check_bwd(int B, int Hq, int Hkv, int N, int D, float scale, const void* wor
     if (!b.p) return FA_ERR_INVALID;
   int rc = check_shape(B, Hq, Hkv, N, D, scale);
   if (rc != FA_OK) return rc;
-  rc = check_mode(N, deterministic);
+  rc = check_mode(N, D, deterministic);
   if (rc != FA_OK) return rc;
   for (const Buf& b : reads)
     if (!aligned16(b.p)) return FA_ERR_ALIGN;

@@ -530,11 +530,15 @@ constexpr int kSchedMaxCost = 16384 - kSchedThreads - 1;  // histogram + chunk s
 // Items are (sequence, tile of `rows` rows).  KIND 0 costs a query tile by
 // the 64-key tiles it walks (forward, fixed-order dQ pass); KIND 1 costs a key
 // block by the query steps of qstep queries it walks (main backward kernel).
+// The list holds at most `cap` items: well-formed offsets give at most
+// total / rows + B of them, but overlapping ones (clamping keeps each
+// sequence inside [0, total], not apart from the others) can give more, and
+// those past the capacity are dropped rather than written past the list.
 template <bool CAUSAL, int KIND>
 __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(const int* __restrict__ cu,
                                                                       int B, int total,
                                                                       int max_cost, int qstep,
-                                                                      int rows,
+                                                                      int rows, int cap,
                                                                       int* __restrict__ n_items,
                                                                       int* __restrict__ items) {
   extern __shared__ int sm[];
@@ -583,28 +587,28 @@ __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(const in
     hist[c] = run;
     run += cnt;
   }
-  if (tid == kSchedThreads - 1) *n_items = csum[tid];
+  if (tid == kSchedThreads - 1) *n_items = min(csum[tid], cap);
   __syncthreads();
   for (int b = tid; b < B; b += kSchedThreads) {
     const int len = seq_len(b);
     for (int qb = 0; qb * rows < len; ++qb) {
       const int pos = atomicAdd(&hist[cost(len, qb)], 1);
-      items[2 * pos] = b;
-      items[2 * pos + 1] = qb;
+      if (pos < cap) {
+        items[2 * pos] = b;
+        items[2 * pos + 1] = qb;
+      }
     }
   }
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch_fwd_varlen_t(const FwdArgs& a, const VarlenArgs& v, hipStream_t s) {
-  const size_t items_max = (size_t)v.total / kVarlenBM + v.B;
+  const size_t items_max = (size_t)varlen_item_capacity(v.B, v.total);
   char* ws = (char*)v.workspace;
   int* n_items = (int*)ws;
   int* items = (int*)(ws + 256);
-  const int max_cost = (v.max_seqlen + kFwdBN - 1) / kFwdBN;
-  const size_t shm = (size_t)(max_cost + 1 + kSchedThreads) * sizeof(int);
-  hipLaunchKernelGGL((varlen_schedule_kernel<CAUSAL, 0>), dim3(1), dim3(kSchedThreads), shm, s,
-                     v.cu, v.B, v.total, max_cost, 0, kVarlenBM, n_items, items);
+  const hipError_t e = launch_varlen_schedule(v, CAUSAL, 0, 0, kVarlenBM, n_items, items, s);
+  if (e != hipSuccess) return e;
   FwdParams p;
   p.BH = 0;
   p.Hq = a.Hq;
@@ -768,28 +772,32 @@ hipError_t launch_varlen_schedule(const VarlenArgs& v, int causal, int kind, int
   const int max_cost = kind == 0 ? (v.max_seqlen + kFwdBN - 1) / kFwdBN
                                  : (v.max_seqlen + qstep - 1) / qstep;
   const size_t shm = (size_t)(max_cost + 1 + kSchedThreads) * sizeof(int);
+  const int cap = varlen_item_capacity(v.B, v.total);
   if (kind == 0) {
     if (causal)
       hipLaunchKernelGGL((varlen_schedule_kernel<true, 0>), dim3(1), dim3(kSchedThreads), shm, s,
-                         v.cu, v.B, v.total, max_cost, qstep, rows, n_items, items);
+                         v.cu, v.B, v.total, max_cost, qstep, rows, cap, n_items, items);
     else
       hipLaunchKernelGGL((varlen_schedule_kernel<false, 0>), dim3(1), dim3(kSchedThreads), shm, s,
-                         v.cu, v.B, v.total, max_cost, qstep, rows, n_items, items);
+                         v.cu, v.B, v.total, max_cost, qstep, rows, cap, n_items, items);
   } else {
     if (causal)
       hipLaunchKernelGGL((varlen_schedule_kernel<true, 1>), dim3(1), dim3(kSchedThreads), shm, s,
-                         v.cu, v.B, v.total, max_cost, qstep, rows, n_items, items);
+                         v.cu, v.B, v.total, max_cost, qstep, rows, cap, n_items, items);
     else
       hipLaunchKernelGGL((varlen_schedule_kernel<false, 1>), dim3(1), dim3(kSchedThreads), shm, s,
-                         v.cu, v.B, v.total, max_cost, qstep, rows, n_items, items);
+                         v.cu, v.B, v.total, max_cost, qstep, rows, cap, n_items, items);
   }
   return hipGetLastError();
 }
 
 // Room for one work list of tiles of at least 128 rows: at most
-// sum_b ceil(len_b / 128) <= total / 128 + B items.
+// sum_b ceil(len_b / 128) <= total / 128 + B items when the sequences do not
+// overlap (the schedule kernel drops any beyond that).
+int varlen_item_capacity(int B, int total) { return total / 128 + B; }
+
 size_t varlen_workspace_bytes(int B, int total) {
-  return 256 + ((size_t)total / 128 + B) * 2 * sizeof(int);
+  return 256 + (size_t)varlen_item_capacity(B, total) * 2 * sizeof(int);
 }
 
 int varlen_max_seqlen_limit() { return kSchedMaxCost * kFwdBN; }

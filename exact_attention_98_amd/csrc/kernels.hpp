@@ -55,12 +55,14 @@ struct VarlenArgs {
   void* workspace;     // varlen_workspace_bytes(B, total)
 };
 size_t varlen_workspace_bytes(int B, int total);
+// Items one work list holds (tiles of 128 rows or more): total / 128 + B.
+int varlen_item_capacity(int B, int total);
 // Largest max_seqlen the work-list builder supports (its histogram lives in LDS).
 int varlen_max_seqlen_limit();
 hipError_t launch_fwd_varlen(const FwdArgs& a, const VarlenArgs& v, hipStream_t stream);
 // Work list of a variable-length batch into n_items / items (2 ints per item,
-// room for varlen_workspace_bytes(B, total) - 256 bytes, enough for tiles of
-// rows >= 128): kind 0 = (sequence, query tile of `rows`) by 64-key tiles
+// at most varlen_item_capacity(B, total) items, enough for tiles of rows >= 128
+// of sequences that do not overlap): kind 0 = (sequence, query tile of `rows`) by 64-key tiles
 // walked; kind 1 = (sequence, key block of `rows`) by query steps of qstep
 // walked; largest first.
 hipError_t launch_varlen_schedule(const VarlenArgs& v, int causal, int kind, int qstep, int rows,

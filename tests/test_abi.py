@@ -87,6 +87,10 @@ def test_workspace_size():
     assert fa.fa_bwd_workspace_size(1, 1, 1, 46336, 64, 1) > 0
     assert fa.fa_bwd_workspace_size(1, 1, 1, 46400, 64, 1) == 0
     assert fa.fa_bwd_workspace_size(1, 1, 1, 46400, 64, 2) > 0
+    # The atomic mode's fp32 accumulator of one head within 32-bit signed offsets.
+    assert fa.fa_bwd_workspace_size(1, 1, 1, (1 << 22) - 1, 128, 0) > 0
+    assert fa.fa_bwd_workspace_size(1, 1, 1, 1 << 22, 128, 0) == 0
+    assert fa.fa_bwd_workspace_size(1, 1, 1, 1 << 22, 128, 2) > 0
 
 
 def bwd(**kw):
@@ -107,6 +111,9 @@ def bwd(**kw):
     (dict(ws=DQ), fa.FA_ERR_INVALID), (dict(scale=float("nan")), fa.FA_ERR_INVALID),
     (dict(det=3), fa.FA_ERR_INVALID), (dict(det=-1), fa.FA_ERR_INVALID),
     (dict(N=46400, det=1), fa.FA_ERR_TOO_LARGE),
+    # Atomic mode: one head's fp32 dQ accumulator rows (N D 4 bytes) must stay
+    # within 32-bit signed offsets.
+    (dict(Hq=1, Hkv=1, N=1 << 22, D=128, det=0), fa.FA_ERR_TOO_LARGE),
 ])
 def test_bwd_rejects(kw, code):
     assert bwd(**kw) == code
@@ -189,6 +196,9 @@ def fwds(**kw):
     (dict(ws=WS + 64), fa.FA_ERR_ALIGN), (dict(o=K), fa.FA_ERR_INVALID),
     (dict(ws=O), fa.FA_ERR_INVALID),
     (dict(Hkv=1 << 8, Hq=1 << 8, Nk=1 << 17), fa.FA_ERR_TOO_LARGE),
+    # Several key ranges: the fp32 partial rows of one K/V group (G Nq D 4
+    # bytes) within 32-bit signed offsets.
+    (dict(Hq=1024, Hkv=1, Nq=4096, Nk=8192), fa.FA_ERR_TOO_LARGE),
 ])
 def test_fwd_splitkv_rejects(kw, code):
     assert fwds(**kw) == code
@@ -204,6 +214,9 @@ def test_splitkv_sizes():
     assert fa.fa_fwd_splitkv_workspace_size(1, 32, 1, 1, 32768, 128, 0) == \
         fa.fa_fwd_splitkv_workspace_size(1, 32, 1, 1, 32768, 128, s)
     assert fa.fa_fwd_splitkv_workspace_size(1, 32, 1, 1, 100, 128, 3) == 0   # ceil(100/64) = 2 ranges max
+    assert fa.fa_fwd_splitkv_workspace_size(1, 1024, 1, 4095, 8192, 128, 4) > 0
+    assert fa.fa_fwd_splitkv_workspace_size(1, 1024, 1, 4096, 8192, 128, 4) == 0
+    assert fa.fa_fwd_splitkv_workspace_size(1, 1024, 1, 4096, 8192, 128, 1) == 0   # one range: none needed
 
 
 def bwdv(**kw):

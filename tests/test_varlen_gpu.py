@@ -88,3 +88,42 @@ def test_varlen_workload_sampled_rows():
         got_l.append(torch.stack([lse[h, s0 + i] for (_, h, i) in rows]))
     check_o(torch.cat(got_o), torch.cat(ref_o), f"sampled O ({sum(len(x) for x in got_o)} rows)")
     check_lse(torch.cat(got_l), torch.cat(ref_l), "sampled LSE")
+
+
+@pytest.mark.parametrize("direction", ["fwd", "bwd0", "bwd2"])
+def test_overlapping_sequences_stay_inside_the_workspace(direction):
+    # cu_seqlens = [0, T, 0, T]: sequences 0 and 2 both cover rows 0..T-1
+    # (clamping keeps each inside the tensors but not apart), which lists 20
+    # (sequence, 128-row tile) items against room for T/128 + B = 13.  The
+    # work list must stop at its capacity: the library gets exactly the
+    # workspace it asks for, inside a larger buffer whose tail is a guard
+    # pattern that must come back unchanged.  (Results for overlapping
+    # sequences are unspecified; the call must complete and stay in bounds.)
+    dev = require_gpu()
+    T, Hq, Hkv, D = 1280, 2, 1, 128
+    say(f"varlen overlapping cu_seqlens [0,T,0,T] T={T} {direction}")
+    g = torch.Generator().manual_seed(4)
+    mk = lambda h: torch.randn(h, T, D, generator=g).to(torch.bfloat16).to(dev)
+    q, k, v = mk(Hq), mk(Hkv), mk(Hkv)
+    cu = torch.tensor([0, T, 0, T], dtype=torch.int32, device=dev)
+    scale = 1.0 / math.sqrt(D)
+    guard = 4096
+    if direction == "fwd":
+        ws_bytes = fa.fa_fwd_varlen_workspace_size(3, T)
+    else:
+        ws_bytes = fa.fa_bwd_varlen_workspace_size(3, Hq, Hkv, T, D, int(direction[-1]))
+    assert ws_bytes > 0
+    buf = torch.full((ws_bytes + guard,), 0xA5, dtype=torch.uint8, device=dev)
+    ws = buf[:ws_bytes]
+    if direction == "fwd":
+        o, lse = fa.forward_varlen(q, k, v, cu, T, True, scale, workspace=ws)
+        outs = (o, lse)
+    else:
+        o, lse = fa.forward_varlen(q, k, v, cu, T, True, scale)
+        do = mk(Hq)
+        outs = fa.backward_varlen(q, k, v, o, lse, do, cu, T, True, scale,
+                                  deterministic=int(direction[-1]), workspace=ws)
+    torch.cuda.synchronize()
+    assert bool((buf[ws_bytes:] == 0xA5).all()), "work list written past the workspace"
+    for t in outs:
+        assert torch.isfinite(t.float()).all()
