@@ -35,8 +35,8 @@ KERNEL_SOURCES = {
                    "exact_attention_98_amd/csrc/common.hpp"],
     "bwd_ws_kernel": ["exact_attention_98_amd/csrc/bwd_kernels.hip",
                       "exact_attention_98_amd/csrc/common.hpp"],
-    "bwd_main_kernel": ["exact_attention_98_amd/csrc/bwd_kernels.hip",
-                        "exact_attention_98_amd/csrc/common.hpp"],
+    "bwd_atomic_kernel": ["exact_attention_98_amd/csrc/bwd_kernels.hip",
+                          "exact_attention_98_amd/csrc/common.hpp"],
     "bwd_dq_kernel": ["exact_attention_98_amd/csrc/bwd_kernels.hip",
                       "exact_attention_98_amd/csrc/common.hpp"],
     "bwd_dq_ds_kernel": ["exact_attention_98_amd/csrc/bwd_kernels.hip",
@@ -538,8 +538,8 @@ def main() -> int:
             raise RuntimeError(f"{what}: {fa.fa_strerror(rc)}")
 
     dq_name = DQ_KERNEL[det]
-    # D = 128 runs the warp-specialized main kernel in the fixed-order modes.
-    main_name = "bwd_main_kernel" if det == 0 else "bwd_ws_kernel"
+    # The fixed-order modes run the warp-specialized main kernel, the atomic mode its own.
+    main_name = "bwd_atomic_kernel" if det == 0 else "bwd_ws_kernel"
     names = ["fwd_kernel", "bwd_pre_kernel", main_name, dq_name]
 
     def step(ev):

@@ -122,14 +122,14 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// Main backward kernel: dK, dV and, by dQ mode, atomic dQ or stored dS
-// blocks.  Workgroup =
+// Atomic-mode backward kernel: dK, dV and each key tile's dQ contribution,
+// added into an fp32 accumulator with atomics.  Workgroup =
 // (batch, K/V head, key tile of 128); wave w owns keys 32w..32w+31 of the
 // tile.  Query steps of QS = 4096 / D queries (32 for D = 128, 64 for D = 64)
 // are walked from the last one down to the first that meets the tile's
 // diagonal, for each of the G query heads.
-template <int D, bool CAUSAL, int DQM, bool VARLEN>
-__global__ __launch_bounds__(256, 1) void bwd_main_kernel(
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(256, 1) void bwd_atomic_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, BwdParams p) {
@@ -144,25 +144,22 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
   constexpr int DSB = BN * QS * 2;    // bytes of one dS^T buffer [key][query]
   constexpr int DSRB = QS * 2;        // bytes per dS^T row
   static_assert(NQB * ND == kBwdWaves, "one dQ output block per wave");
-  constexpr bool FUSED_DQ = DQM == kDqAtomic;
-  constexpr bool STORE_DS = DQM == kDqStored;
   static_assert(NLD >= 1, "step tile too small");
 
-  // Per stage: Q tile, dO tile, 256 B of LSE*log2e, 256 B of Delta; then (atomic
-  // mode) two dS^T buffers.
+  // Per stage: Q tile, dO tile, 256 B of LSE*log2e, 256 B of Delta; then two
+  // dS^T buffers.
   // Four stages: the step being finished (its LSE, Delta and the transposing
   // reads of its Q and dO), the next step (row reads of Q and dO for its S and
   // dP), and two more in flight, so a copy has two steps to land.  Each buffer
   // is its own array so the compiler can tell an in-flight copy from reads of
   // the others.
   constexpr int STAGE = 2 * TB + 512;
-  constexpr int DSA = FUSED_DQ ? DSB : 16;
   __shared__ __attribute__((aligned(1024))) char stage0[STAGE];
   __shared__ __attribute__((aligned(1024))) char stage1[STAGE];
   __shared__ __attribute__((aligned(1024))) char stage2[STAGE];
   __shared__ __attribute__((aligned(1024))) char stage3[STAGE];
-  __shared__ __attribute__((aligned(1024))) char dsbuf0[DSA];
-  __shared__ __attribute__((aligned(1024))) char dsbuf1[DSA];
+  __shared__ __attribute__((aligned(1024))) char dsbuf0[DSB];
+  __shared__ __attribute__((aligned(1024))) char dsbuf1[DSB];
 
   const int Hkv = p.Hq / p.G;
   const int wg = blockIdx.x;
@@ -218,8 +215,8 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
   // lane (d, h) holds K[k0 + 16t + 8(i/4) + 4h + i%4][d] in slot i, matching
   // the transposing read of dS^T.
   const int dq_qb = wave / ND, dq_db = wave % ND;
-  bf16x8 kT[FUSED_DQ ? BN / 16 : 1];
-  if constexpr (FUSED_DQ) {
+  bf16x8 kT[BN / 16];
+  {
     const int d = 32 * dq_db + n;
     const uint16_t* Kh = K + kv_head;
 #pragma unroll
@@ -351,7 +348,6 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
 
   // dQ block of the step at (head offset g, query step qs), whose dS^T is in dsb.
   auto dq_step = [&](int g, int qs, const char* dsb) {
-    if constexpr (FUSED_DQ) {
     const int hq = hq0 + g;
     const int q0 = qs * QS;
     f32x16 acc;
@@ -374,35 +370,6 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r)
       buf_atomic_add(dqr, (uint32_t)(((qrow0 + 8 * (r >> 2) + (r & 3)) * D + d) * 4), acc[r]);
-    }
-  };
-
-  // Stored-dS mode: this wave's dS^T blocks of one step, 32 keys x 32 queries
-  // per block, 16 bytes per lane and block half u (lane of key n, half h:
-  // positions 16u + 8h .. +8 of row n), each half a contiguous KiB in lane
-  // order (byte 1024u + 16 lane), so every store writes whole cache lines.
-  // Blocks that do not exist (padding rows, or above the diagonal under
-  // causal) get an offset past the end of the head's range and the store is
-  // dropped.
-  u32x4 ds_keep[NQB][2];
-  const int kb32 = kw / 32;
-  const uint32_t ds_lane = (uint32_t)lane * 16u;
-  auto store_ds = [&](int g, int qs) {
-    if constexpr (STORE_DS) {
-      const rsrc_t r = make_rsrc_uniform(p.ds + ((size_t)b * p.Hq + hq0 + g) * p.ds_head, p.ds_head);
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        const int qb32 = qs * NQB + qb;
-        const bool ok = qb32 < p.nb32 && kb32 < p.nb32 && (!CAUSAL || kb32 <= qb32);
-        const uint32_t off = ok ? (uint32_t)(qb32 * p.nb32 + kb32) * 2048u : 0xFFFFF000u;
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-          // Non-temporal stores (cache policy NT): dS is read once, by the
-          // dQ pass, so the caches keep K, V and the step tiles instead, and
-          // the dQ pass does not first write back lines left dirty here.
-          __builtin_amdgcn_raw_buffer_store_b128(ds_keep[qb][u], r, off + ds_lane + 1024u * u, 0, kCachePolicyNT);
-      }
-    }
   };
 
   // S and dP of one step (A operands Q, dO by row reads of its stage).
@@ -432,18 +399,14 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
                   f32x16 (&dn)[NQB], const f32x4 (&lc)[NQB][4], const f32x4 (&dc)[NQB][4],
                   f32x4 (&ln)[NQB][4], f32x4 (&dln)[NQB][4]) {
     // Step i+1 must be in LDS.  __syncthreads' fence then drains the rest as
-    // well (direct-to-LDS copies count in vmcnt): this kernel's stores and
-    // atomics do not complete in order with its copies, so it does not keep
-    // copies in flight across the barrier.
+    // well (direct-to-LDS copies count in vmcnt): this kernel's atomics do
+    // not complete in order with its copies, so it does not keep copies in
+    // flight across the barrier.
     if (i + 2 < nsteps) wait_all_but_one_step();
     else wait_vmcnt<0>();
     __syncthreads();  // step i+1 visible to all; step i-1's stage and dS^T free
-    // Stored-dS mode: step i-1's dS blocks go out before step i+3's copies,
-    // so the copies are the newest memory operations when the next step
-    // waits for its own (loads complete in order; stores need not).
-    if (STORE_DS && i > 0) store_ds(prev_g, prev_qs);
     if (i + 3 < nsteps) issue_next(ld);
-    if (FUSED_DQ && i > 0) dq_step(prev_g, prev_qs, dsprev);
+    if (i > 0) dq_step(prev_g, prev_qs, dsprev);
 
     const int q0 = cur_qs * QS;
     // S(i) and dP(i) are read by the VALU below: move them to VGPRs here, so
@@ -561,13 +524,6 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    if constexpr (STORE_DS)
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        ds_keep[qb][0] = as_u32x4(dsa[qb][0]);
-        ds_keep[qb][1] = as_u32x4(dsa[qb][1]);
-      }
-
     // Phase B.
     const float* lse_n = (const float*)(nxt + 2 * TB);
     const float* dlt_n = (const float*)(nxt + 2 * TB + 256);
@@ -584,17 +540,15 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
         dln[lq][r4] = *(const f32x4*)(dlt_n + 32 * lq + 8 * r4 + 4 * h);
       }
       // dS^T -> LDS: lane (key 32 wave + n) writes queries 32qb + 8g + 4h .. +4.
-      if constexpr (FUSED_DQ) {
-        if (db == 0 && u == 0) {
+      if (db == 0 && u == 0) {
 #pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const int col = 32 * qb + 8 * g4 + 4 * h;
-            const u32x4 dsw4 = as_u32x4(dsa[qb][g4 >> 1]);
-            u32x2 w;
-            w[0] = dsw4[(g4 & 1) * 2];
-            w[1] = dsw4[(g4 & 1) * 2 + 1];
-            *(u32x2*)(dsw + ds_wrow * DSRB + (((col >> 3) ^ fd(ds_wrow)) * 16) + ((col >> 2) & 1) * 8) = w;
-          }
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int col = 32 * qb + 8 * g4 + 4 * h;
+          const u32x4 dsw4 = as_u32x4(dsa[qb][g4 >> 1]);
+          u32x2 w;
+          w[0] = dsw4[(g4 & 1) * 2];
+          w[1] = dsw4[(g4 & 1) * 2 + 1];
+          *(u32x2*)(dsw + ds_wrow * DSRB + (((col >> 3) ^ fd(ds_wrow)) * 16) + ((col >> 2) & 1) * 8) = w;
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -643,8 +597,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
     body(i + 1, stage1, stage2, stage0, dsbuf1, dsbuf0, sB, dB, sA, dA, lB, dlB, lA, dlA);
   if (i + 2 < nsteps)
     body(i + 2, stage2, stage3, stage1, dsbuf0, dsbuf1, sA, dA, sB, dB, lA, dlA, lB, dlB);
-  if (STORE_DS && nsteps > 0) store_ds(prev_g, prev_qs);
-  if (FUSED_DQ && nsteps > 0) {
+  if (nsteps > 0) {
     __syncthreads();
     dq_step(prev_g, prev_qs, ((nsteps - 1) & 1) ? dsbuf1 : dsbuf0);
   }
@@ -668,7 +621,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
 
 // ---------------------------------------------------------------------------
 // Warp-specialized main backward kernel, D = 64 or 128 (dQ modes stored and
-// recompute; dense, or packed sequences in the recompute mode).  Same work item as bwd_main_kernel -- (batch, K/V head, 128-key
+// recompute; dense, or packed sequences in the recompute mode).  Same work item as bwd_atomic_kernel -- (batch, K/V head, 128-key
 // tile), every query step of every query head of the group -- with 8 waves in
 // two roles over the same step tiles:
 //   score waves 0..3 (keys 32 w): the MFMA unit forms S, dP of step i+1 while
@@ -712,7 +665,7 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
   constexpr bool STORE_DS = DQM == kDqStored;
   constexpr bool PREF = STORE_DS && D == 128;  // score-wave reads ahead of the barrier
   static_assert(NLD >= 1, "step tile too small");
-  static_assert(DQM != kDqAtomic, "atomic dQ uses bwd_main_kernel");
+  static_assert(DQM != kDqAtomic, "atomic dQ uses bwd_atomic_kernel");
   static_assert(!(VARLEN && DQM == kDqStored), "no stored-dS layout for packed sequences");
   constexpr int STAGE = 2 * TB + 512;  // Q, dO, 256 B LSE * log2 e, 256 B Delta
   constexpr int PSLOT = 4 * 4096;      // P, dS of the 4 score waves
@@ -890,7 +843,9 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
         const rsrc_t r = make_rsrc_uniform(p.ds + ((size_t)b * p.Hq + hq0 + cur_g) * p.ds_head, p.ds_head);
         const bool ok = cur_qs < p.nb32 && kb32 < p.nb32 && (!CAUSAL || kb32 <= cur_qs);
         const uint32_t off = ok ? (uint32_t)(cur_qs * p.nb32 + kb32) * 2048u : 0xFFFFF000u;
-        // Non-temporal (NT), as in bwd_main_kernel: dS is read once, later.
+        // Non-temporal (NT): dS is read once, by the dQ pass, so the caches
+        // keep K, V and the step tiles instead, and the dQ pass does not first
+        // write back lines left dirty here.
         __builtin_amdgcn_raw_buffer_store_b128(w, r, off + ds_lane + 1024u * u, 0, kCachePolicyNT);
       }
     };
@@ -1151,7 +1106,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t* __restri
   constexpr int TB = BN * RB;
   constexpr int NLD = TB / 1024 / NW;
   static_assert(NLD >= 1, "tile too small");
-  // Two stages of [K, V] tiles as two arrays (see the main kernel).
+  // Two stages of [K, V] tiles as two arrays (so the compiler can tell an
+  // in-flight copy into one from reads of the other).
   __shared__ __attribute__((aligned(1024))) char kv0[2 * TB];
   __shared__ __attribute__((aligned(1024))) char kv1[2 * TB];
 
@@ -1500,10 +1456,10 @@ __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(const float* __rest
   ((u32x4*)dq)[i] = w;
 }
 
-template <int D, bool CAUSAL, int DQM, bool VARLEN = false>
-hipError_t launch_bwd_t(const BwdArgs& a, const BwdParams& p, hipStream_t s, unsigned items = 0) {
+template <int D, bool CAUSAL, bool VARLEN = false>
+hipError_t launch_atomic_t(const BwdArgs& a, const BwdParams& p, hipStream_t s, unsigned items = 0) {
   const dim3 grid(VARLEN ? items * (unsigned)a.Hkv : (unsigned)(a.B * a.Hkv * p.nkb));
-  hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL, DQM, VARLEN>), grid, dim3(64 * kBwdWaves), 0, s,
+  hipLaunchKernelGGL((bwd_atomic_kernel<D, CAUSAL, VARLEN>), grid, dim3(64 * kBwdWaves), 0, s,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, (uint16_t*)a.dk, (uint16_t*)a.dv, p);
   return hipGetLastError();
@@ -1573,14 +1529,7 @@ __global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(const float* __restr
 }
 
 // The warp-specialized kernel runs both fixed-order dQ modes, at D = 64 and
-// 128.  At D = 64 (B2 H16 N16384 causal) it is 4% faster than bwd_main_kernel
-// in the stored mode, now that the dS stores are non-temporal (27% slower with
-// cached ones), and 8% faster in the recompute mode.
-constexpr bool kBwdSplitRoles = true;
-constexpr bool use_ws(int D, int deterministic) {
-  (void)D;
-  return kBwdSplitRoles && (deterministic == kDqRecompute || deterministic == kDqStored);
-}
+// 128; the atomic mode runs bwd_atomic_kernel.
 template <int D, bool CAUSAL, int DQM>
 hipError_t launch_ws_t(const BwdArgs& a, const BwdParams& p, hipStream_t s) {
   const dim3 grid((unsigned)(a.B * a.Hkv * p.nkb * p.hsplit));
@@ -1598,20 +1547,14 @@ hipError_t launch_ws_t(const BwdArgs& a, const BwdParams& p, hipStream_t s) {
 template <int D>
 hipError_t launch_main_d(const BwdArgs& a, hipStream_t s) {
   const BwdParams p = make_params(a);
-  if (use_ws(D, a.deterministic)) {
-    if (a.deterministic == kDqStored)
-      return a.causal ? launch_ws_t<D, true, kDqStored>(a, p, s) : launch_ws_t<D, false, kDqStored>(a, p, s);
-    return a.causal ? launch_ws_t<D, true, kDqRecompute>(a, p, s)
-                    : launch_ws_t<D, false, kDqRecompute>(a, p, s);
-  }
   switch (a.deterministic) {
     case kDqAtomic:
-      return a.causal ? launch_bwd_t<D, true, kDqAtomic>(a, p, s) : launch_bwd_t<D, false, kDqAtomic>(a, p, s);
+      return a.causal ? launch_atomic_t<D, true>(a, p, s) : launch_atomic_t<D, false>(a, p, s);
     case kDqStored:
-      return a.causal ? launch_bwd_t<D, true, kDqStored>(a, p, s) : launch_bwd_t<D, false, kDqStored>(a, p, s);
+      return a.causal ? launch_ws_t<D, true, kDqStored>(a, p, s) : launch_ws_t<D, false, kDqStored>(a, p, s);
     default:
-      return a.causal ? launch_bwd_t<D, true, kDqRecompute>(a, p, s)
-                      : launch_bwd_t<D, false, kDqRecompute>(a, p, s);
+      return a.causal ? launch_ws_t<D, true, kDqRecompute>(a, p, s)
+                      : launch_ws_t<D, false, kDqRecompute>(a, p, s);
   }
 }
 
@@ -1650,7 +1593,7 @@ hipError_t launch_dq_d(const BwdArgs& a, hipStream_t s) {
 // preprocess and the atomic-mode convert run over every row unchanged.
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_varlen_t(const BwdArgs& a, const VarlenArgs& v, hipStream_t s) {
-  // (Hkv = Hq: the variable-length backward runs bwd_main_kernel, no head split.)
+  // (Hkv = Hq in the layout: the variable-length backward has no head split.)
   const BwdLayout lay = bwd_layout(1, a.Hq, a.Hq, v.total, D, a.deterministic);
   char* lists = (char*)a.workspace + lay.total;
   const size_t lbytes = varlen_workspace_bytes(v.B, v.total);
@@ -1658,7 +1601,7 @@ hipError_t launch_bwd_varlen_t(const BwdArgs& a, const VarlenArgs& v, hipStream_
   int* main_items = (int*)(lists + 256);
   int* dq_n = (int*)(lists + lbytes);
   int* dq_items = (int*)(lists + lbytes + 256);
-  const unsigned items_max = (unsigned)(v.total / 128 + v.B);
+  const unsigned items_max = (unsigned)varlen_item_capacity(v.B, v.total);
   constexpr int QS = 4096 / D;
   hipError_t e = launch_varlen_schedule(v, CAUSAL, 1, QS, kBwdBN, main_n, main_items, s);
   if (e != hipSuccess) return e;
@@ -1675,16 +1618,15 @@ hipError_t launch_bwd_varlen_t(const BwdArgs& a, const VarlenArgs& v, hipStream_
   p.kv_part = nullptr;
   p.items = main_items;
   p.n_items = main_n;
-  if (use_ws(D, a.deterministic)) {
-    // The warp-specialized kernel over the same (sequence, key tile) list.
+  if (a.deterministic == kDqAtomic) {
+    e = launch_atomic_t<D, CAUSAL, true>(a, p, s, items_max);
+  } else {
+    // The warp-specialized kernel over the (sequence, key tile) list.
     hipLaunchKernelGGL((bwd_ws_kernel<D, CAUSAL, kDqRecompute, true>), dim3(items_max * (unsigned)a.Hkv),
                        dim3(512), 0, s, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, (const uint16_t*)a.dout, (uint16_t*)a.dk,
                        (uint16_t*)a.dv, p);
     e = hipGetLastError();
-  } else {
-    e = a.deterministic == kDqAtomic ? launch_bwd_t<D, CAUSAL, kDqAtomic, true>(a, p, s, items_max)
-                                     : launch_bwd_t<D, CAUSAL, kDqRecompute, true>(a, p, s, items_max);
   }
   if (e != hipSuccess) return e;
   if (a.deterministic == kDqAtomic) {
@@ -1719,7 +1661,8 @@ size_t ds_head_bytes(int N) {
 }
 
 int bwd_head_split(int B, int Hq, int Hkv, int N, int D, int deterministic) {
-  if (!use_ws(D, deterministic)) return 1;
+  (void)D;
+  if (deterministic == kDqAtomic) return 1;
   const int G = Hq / Hkv;
   const long tiles = (long)B * Hkv * ((N + kBwdBN - 1) / kBwdBN);
   int s = 1;
