@@ -98,7 +98,9 @@ def test_overlapping_sequences_stay_inside_the_workspace(direction):
     # work list must stop at its capacity: the library gets exactly the
     # workspace it asks for, inside a larger buffer whose tail is a guard
     # pattern that must come back unchanged.  (Results for overlapping
-    # sequences are unspecified; the call must complete and stay in bounds.)
+    # sequences are unspecified -- items past the capacity are not run, so
+    # some output rows are never written; the call must complete and stay in
+    # bounds.)
     dev = require_gpu()
     T, Hq, Hkv, D = 1280, 2, 1, 128
     say(f"varlen overlapping cu_seqlens [0,T,0,T] T={T} {direction}")
@@ -116,14 +118,10 @@ def test_overlapping_sequences_stay_inside_the_workspace(direction):
     buf = torch.full((ws_bytes + guard,), 0xA5, dtype=torch.uint8, device=dev)
     ws = buf[:ws_bytes]
     if direction == "fwd":
-        o, lse = fa.forward_varlen(q, k, v, cu, T, True, scale, workspace=ws)
-        outs = (o, lse)
+        fa.forward_varlen(q, k, v, cu, T, True, scale, workspace=ws)
     else:
         o, lse = fa.forward_varlen(q, k, v, cu, T, True, scale)
-        do = mk(Hq)
-        outs = fa.backward_varlen(q, k, v, o, lse, do, cu, T, True, scale,
-                                  deterministic=int(direction[-1]), workspace=ws)
+        fa.backward_varlen(q, k, v, o, lse, mk(Hq), cu, T, True, scale,
+                           deterministic=int(direction[-1]), workspace=ws)
     torch.cuda.synchronize()
     assert bool((buf[ws_bytes:] == 0xA5).all()), "work list written past the workspace"
-    for t in outs:
-        assert torch.isfinite(t.float()).all()
