@@ -18,7 +18,8 @@ __all__ = ["fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_workspace_size", "fa_bwd_pre
            "fa_bwd_main", "fa_bwd_dq", "fa_fwd_varlen", "fa_fwd_varlen_workspace_size",
            "fa_varlen_max_seqlen", "fa_fwd_splitkv", "fa_fwd_splitkv_num_splits",
            "fa_fwd_splitkv_workspace_size", "fa_bwd_varlen", "fa_bwd_varlen_workspace_size",
-           "fa_fwd_fp8", "fa_fwd_fp8_workspace_size", "fa_exp2_poly_eval", "fa_strerror", "forward", "backward",
+           "fa_fwd_fp8", "fa_fwd_fp8_workspace_size", "fa_exp2_poly_eval", "fa_bwd_noalloc", "fa_strerror",
+           "forward", "backward", "backward_noalloc",
            "forward_varlen", "backward_varlen", "forward_splitkv", "forward_fp8", "FaError",
            "library_path", "load"]
 
@@ -33,12 +34,16 @@ FA_ERR_ALIGN = -3
 FA_ERR_WORKSPACE = -4
 FA_ERR_HIP = -5
 FA_ERR_TOO_LARGE = -6
+FA_ERR_SCRATCH = -7
+# Fixed scratch behind fa_bwd_noalloc (FA_BWD_NOALLOC_SCRATCH_BYTES in fa.h).
+BWD_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_workspace_size", "fa_bwd_preprocess",
             "fa_bwd_main", "fa_bwd_dq", "fa_fwd_varlen", "fa_fwd_varlen_workspace_size",
             "fa_varlen_max_seqlen", "fa_fwd_splitkv", "fa_fwd_splitkv_num_splits",
             "fa_fwd_splitkv_workspace_size", "fa_bwd_varlen", "fa_bwd_varlen_workspace_size",
-            "fa_fwd_fp8", "fa_fwd_fp8_workspace_size", "fa_exp2_poly_eval", "fa_strerror")
+            "fa_fwd_fp8", "fa_fwd_fp8_workspace_size", "fa_exp2_poly_eval", "fa_bwd_noalloc",
+            "fa_strerror")
 
 
 class FaError(RuntimeError):
@@ -70,6 +75,8 @@ def load():
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp, sz,
                            ci, vp]
     lib.fa_bwd.restype = ci
+    lib.fa_bwd_noalloc.argtypes = [vp] * 9 + [ci] * 6 + [cf, vp]
+    lib.fa_bwd_noalloc.restype = ci
     lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, vp, sz, ci, vp]
     lib.fa_bwd_preprocess.restype = ci
     lib.fa_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp, sz, ci, vp]
@@ -128,6 +135,12 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, D, causal, scale, w
            workspace_bytes, deterministic, stream) -> int:
     return load().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, D, int(causal),
                          float(scale), workspace, workspace_bytes, int(deterministic), stream)
+
+
+def fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, D, causal, scale,
+                   stream) -> int:
+    return load().fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, D, int(causal),
+                                 float(scale), stream)
 
 
 def fa_bwd_preprocess(o, dout, lse, B, Hq, Hkv, N, D, workspace, workspace_bytes, deterministic,
@@ -283,6 +296,33 @@ def backward(q, k, v, o, lse, dout, causal: bool, scale: float, *, deterministic
                 _stream_handle(q.device))
     if rc != FA_OK:
         raise FaError(rc, "fa_bwd")
+    return dq, dk, dv
+
+
+def backward_noalloc(q, k, v, o, lse, dout, causal: bool, scale: float, *, dq=None, dk=None,
+                     dv=None):
+    """dQ, dK, dV (bf16) through fa_bwd_noalloc: fixed-order dQ recomputing dS,
+    with the library's fixed scratch instead of a workspace (no device memory
+    is allocated when dq, dk and dv are given)."""
+    import torch
+    B, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    for name, t, shp in (("q", q, (B, Hq, N, D)), ("k", k, (B, Hkv, N, D)),
+                         ("v", v, (B, Hkv, N, D)), ("o", o, (B, Hq, N, D)),
+                         ("dout", dout, (B, Hq, N, D))):
+        _check(name, t, torch.bfloat16, shp)
+    _check("lse", lse, torch.float32, (B, Hq, N))
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check("dq", dq, torch.bfloat16, (B, Hq, N, D))
+    _check("dk", dk, torch.bfloat16, (B, Hkv, N, D))
+    _check("dv", dv, torch.bfloat16, (B, Hkv, N, D))
+    rc = fa_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                        dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv,
+                        N, D, causal, scale, _stream_handle(q.device))
+    if rc != FA_OK:
+        raise FaError(rc, "fa_bwd_noalloc")
     return dq, dk, dv
 
 

@@ -32,6 +32,10 @@
 // copied from HBM straight into LDS (buffer_load ... lds) while step i
 // computes; in atomic mode the dQ product of step i runs during step i+1,
 // after the one barrier per step that publishes step i's dS^T.
+#include <atomic>
+#include <mutex>
+
+#include "../../include/fa.h"
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -1467,7 +1471,7 @@ hipError_t launch_atomic_t(const BwdArgs& a, const BwdParams& p, hipStream_t s, 
 
 BwdParams make_params(const BwdArgs& a) {
   const int QS = 4096 / a.D;
-  const BwdLayout lay = bwd_layout(a.B, a.Hq, a.Hkv, a.N, a.D, a.deterministic);
+  const BwdLayout lay = bwd_layout(a.B, a.Hq, a.Hkv, a.N, a.D, a.deterministic, a.allow_head_split != 0);
   char* ws = (char*)a.workspace;
   BwdParams p;
   p.B = a.B;
@@ -1670,7 +1674,7 @@ int bwd_head_split(int B, int Hq, int Hkv, int N, int D, int deterministic) {
   return s;
 }
 
-BwdLayout bwd_layout(int B, int Hq, int Hkv, int N, int D, int deterministic) {
+BwdLayout bwd_layout(int B, int Hq, int Hkv, int N, int D, int deterministic, bool allow_head_split) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const size_t rows = (size_t)B * Hq * N;
   BwdLayout l;
@@ -1681,7 +1685,7 @@ BwdLayout bwd_layout(int B, int Hq, int Hkv, int N, int D, int deterministic) {
   if (deterministic == kDqAtomic) extra = up(rows * D * 4);
   if (deterministic == kDqStored) extra = up((size_t)B * Hq * ds_head_bytes(N));
   l.kv_part = l.dq_acc + extra;
-  l.hsplit = bwd_head_split(B, Hq, Hkv, N, D, deterministic);
+  l.hsplit = allow_head_split ? bwd_head_split(B, Hq, Hkv, N, D, deterministic) : 1;
   const size_t part = l.hsplit > 1 ? up((size_t)l.hsplit * 2 * B * Hkv * N * D * 4) : 0;
   l.total = l.kv_part + part;
   return l;
@@ -1693,6 +1697,46 @@ hipError_t launch_bwd_preprocess(const BwdArgs& a, hipStream_t s) {
 
 hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t s) {
   return a.D == 64 ? launch_main_d<64>(a, s) : launch_main_d<128>(a, s);
+}
+
+// ---------------------------------------------------------------------------
+// Fixed scratch of the allocation-free backward (fa_bwd_noalloc), for callers
+// that cannot allocate device memory.  It holds the per-row Delta and
+// LSE * log2(e) of the recompute mode; the preprocess kernel writes every row
+// it later reads, so nothing needs clearing between calls.  Each GPU that runs
+// the library holds its own copy for the life of the process, and every call
+// on that GPU shares it: calls that overlap in time on one GPU race.
+static __device__ __align__(256) char scratch[FA_BWD_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+// Device address of `scratch` per device, looked up once per device (with
+// that device current).  In host code the array's name is only a host-side
+// stand-in, so kernels and copies use these addresses, never the name.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+size_t noalloc_scratch_bytes() { return sizeof(scratch); }
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!p) return hipErrorInvalidSymbol;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t s) {

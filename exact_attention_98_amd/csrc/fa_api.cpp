@@ -1,7 +1,8 @@
 // C ABI of the attention library: argument checks, workspace sizing and
 // dispatch to the gfx950 kernels.  Every check runs before any launch, the
 // library allocates and synchronizes nothing, and no exception crosses the
-// boundary.
+// boundary.  Its only state is the per-device address of the fixed scratch
+// behind fa_bwd_noalloc.
 #include <math.h>
 #include <stdint.h>
 
@@ -314,7 +315,8 @@ struct Buf {
 // other buffer of the call.
 int check_bwd(int B, int Hq, int Hkv, int N, int D, float scale, const void* workspace,
               size_t workspace_bytes, int deterministic, std::initializer_list<Buf> reads,
-              std::initializer_list<Buf> writes) {
+              std::initializer_list<Buf> writes, bool allow_head_split = true,
+              bool own_workspace = false) {
   for (const Buf& b : reads)
     if (!b.p) return FA_ERR_INVALID;
   for (const Buf& b : writes)
@@ -327,10 +329,15 @@ int check_bwd(int B, int Hq, int Hkv, int N, int D, float scale, const void* wor
     if (!aligned16(b.p)) return FA_ERR_ALIGN;
   for (const Buf& b : writes)
     if (!aligned16(b.p)) return FA_ERR_ALIGN;
-  const fa::BwdLayout lay = fa::bwd_layout(B, Hq, Hkv, N, D, deterministic);
-  if (!workspace || workspace_bytes < lay.total) return FA_ERR_WORKSPACE;
-  if (((uintptr_t)workspace & 255u) != 0) return FA_ERR_ALIGN;
-  const Buf ws{workspace, lay.total};
+  const fa::BwdLayout lay = fa::bwd_layout(B, Hq, Hkv, N, D, deterministic, allow_head_split);
+  if (own_workspace) {
+    // The library's fixed scratch stands in for the workspace.
+    if (lay.total > fa::noalloc_scratch_bytes()) return FA_ERR_SCRATCH;
+  } else {
+    if (!workspace || workspace_bytes < lay.total) return FA_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255u) != 0) return FA_ERR_ALIGN;
+  }
+  const Buf ws{workspace, own_workspace ? 0 : lay.total};
   const Buf* wb = writes.begin();
   const size_t nw = writes.size();
   for (size_t i = 0; i < nw; ++i) {
@@ -413,6 +420,27 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   return FA_OK;
 }
 
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N,
+                   int D, int causal, float scale, void* stream) {
+  constexpr int kMode = 2;  // fixed-order dQ recomputing dS: row constants only
+  const size_t qb = qbytes(B, Hq, N, D), kb = qbytes(B, Hkv, N, D), lb = lbytes(B, Hq, N);
+  int rc = check_bwd(B, Hq, Hkv, N, D, scale, nullptr, 0, kMode,
+                     {{q, qb}, {k, kb}, {v, kb}, {o, qb}, {lse, lb}, {dout, qb}},
+                     {{dq, qb}, {dk, kb}, {dv, kb}}, false, true);
+  if (rc != FA_OK) return rc;
+  void* ws = nullptr;
+  if (fa::noalloc_scratch(&ws) != hipSuccess) return FA_ERR_HIP;
+  fa::BwdArgs a = bwd_args(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, D, causal, scale, ws,
+                           kMode);
+  a.allow_head_split = 0;
+  hipStream_t s = (hipStream_t)stream;
+  if (fa::launch_bwd_preprocess(a, s) != hipSuccess) return FA_ERR_HIP;
+  if (fa::launch_bwd_main(a, s) != hipSuccess) return FA_ERR_HIP;
+  if (fa::launch_bwd_dq(a, s) != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
+}
+
 const char* fa_strerror(int status) {
   switch (status) {
     case FA_OK: return "success";
@@ -422,6 +450,7 @@ const char* fa_strerror(int status) {
     case FA_ERR_WORKSPACE: return "workspace missing or too small";
     case FA_ERR_HIP: return "HIP runtime error at launch";
     case FA_ERR_TOO_LARGE: return "tensor too large (2^31 elements or more)";
+    case FA_ERR_SCRATCH: return "problem needs more than the fixed scratch of fa_bwd_noalloc";
     default: return "unknown status";
   }
 }

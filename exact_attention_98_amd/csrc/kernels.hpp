@@ -111,6 +111,9 @@ struct BwdArgs {
   float scale;
   int deterministic;
   void* workspace;
+  // 0: the main kernel never splits a K/V head's query heads over several
+  // workgroups (no fp32 partial dK, dV in the workspace).
+  int allow_head_split = 1;
 };
 
 // Workspace layout of the backward (offsets in bytes, 256-byte aligned).
@@ -133,7 +136,13 @@ int bwd_head_split(int B, int Hq, int Hkv, int N, int D, int deterministic);
 // Bytes of the stored-dS blocks of one (batch, query head).
 size_t ds_head_bytes(int N);
 
-BwdLayout bwd_layout(int B, int Hq, int Hkv, int N, int D, int deterministic);
+BwdLayout bwd_layout(int B, int Hq, int Hkv, int N, int D, int deterministic,
+                     bool allow_head_split = true);
+
+// The library's own fixed scratch for fa_bwd_noalloc: its size, and its
+// device address on the current device (looked up once per device).
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void** ptr);
 // The three backward stages; each reads only the BwdArgs fields it needs.
 hipError_t launch_bwd_preprocess(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t stream);

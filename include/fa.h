@@ -32,6 +32,8 @@
  *     included.  The library never allocates device memory, never frees and
  *     never synchronizes: each call only enqueues kernels on `stream` and
  *     returns.  Outputs are valid once that stream's work has completed.
+ *     (fa_bwd_noalloc uses a fixed buffer that is part of the library's code
+ *     object instead of a workspace; see there.)
  *   - Errors: every argument check runs before any launch, so a call that
  *     returns an error has launched nothing.  No exception crosses the ABI.
  *   - Supported now: D in {64, 128}; N >= 1; B, Hq, Hkv >= 1; B*Hq*N*D below
@@ -53,8 +55,13 @@ typedef enum {
     FA_ERR_ALIGN = -3,       /* a pointer is not 16-byte aligned */
     FA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than fa_bwd_workspace_size() */
     FA_ERR_HIP = -5,         /* the HIP runtime reported an error at launch */
-    FA_ERR_TOO_LARGE = -6    /* a tensor exceeds 2^31 elements */
+    FA_ERR_TOO_LARGE = -6,   /* a tensor exceeds 2^31 elements */
+    FA_ERR_SCRATCH = -7      /* fa_bwd_noalloc: the problem needs more than the library's fixed scratch */
 } fa_status;
+
+/* Size of the fixed device scratch behind fa_bwd_noalloc (per GPU, held until
+ * the process ends). */
+#define FA_BWD_NOALLOC_SCRATCH_BYTES (32u << 20)
 
 /*
  * Forward pass.
@@ -148,6 +155,32 @@ int fa_bwd_main(const void* q, const void* k, const void* v, const void* dout, v
 int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq, int B,
               int Hq, int Hkv, int N, int D, int causal, float scale, void* workspace,
               size_t workspace_bytes, int deterministic, void* stream);
+
+/*
+ * Backward pass that allocates nothing and takes no workspace, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * training or serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, layout and results as fa_bwd in dQ mode 2 (fixed-order dQ,
+ * recomputing dS; dq, dk, dv bit-identical run to run), except that:
+ *   - its scratch (per-row Delta and LSE * log2(e), 256-byte aligned) lives
+ *     in a fixed buffer of FA_BWD_NOALLOC_SCRATCH_BYTES inside the library,
+ *     one per GPU, kept for the life of the process.  A problem that needs
+ *     more (B*Hq*N*8 bytes plus alignment, i.e. B*Hq*N above about 4.19
+ *     million rows) returns FA_ERR_SCRATCH before anything is launched;
+ *   - the query heads of a K/V head are never split over several workgroups
+ *     (no fp32 partial dK, dV), so with Hq > Hkv the sum over a group's
+ *     heads runs in one workgroup: dk and dv can differ from fa_bwd's in the
+ *     last bits, within the same tolerances;
+ *   - every call on one GPU shares that buffer: calls that may overlap in
+ *     time on one GPU (other streams, other threads) race and must be
+ *     serialized by the caller.  Nothing in it needs clearing between calls.
+ * The first call on a device looks the buffer's device address up once
+ * (hipGetSymbolAddress, with that device current); no call allocates or frees.
+ * Errors as fa_bwd, plus FA_ERR_SCRATCH; FA_ERR_HIP also if the lookup fails.
+ */
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv,
+                   int B, int Hq, int Hkv, int N, int D, int causal, float scale, void* stream);
 
 /*
  * Variable-length batches (forward).  B sequences of lengths len_b are packed

@@ -30,7 +30,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 def test_strerror():
     assert fa.fa_strerror(0) == "success"
-    for code in range(-6, 0):
+    for code in range(-7, 0):
         assert fa.fa_strerror(code) != "unknown status"
     assert fa.fa_strerror(-99) == "unknown status"
 
@@ -117,6 +117,33 @@ def bwd(**kw):
 ])
 def test_bwd_rejects(kw, code):
     assert bwd(**kw) == code
+
+
+def bwd_noalloc(**kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, dout=DO, dq=DQ, dk=DK, dv=DV, B=1, Hq=2, Hkv=2, N=100,
+             D=64, causal=1, scale=0.125, stream=None)
+    a.update(kw)
+    return fa.fa_bwd_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dout"], a["dq"],
+                             a["dk"], a["dv"], a["B"], a["Hq"], a["Hkv"], a["N"], a["D"],
+                             a["causal"], a["scale"], a["stream"])
+
+
+# Largest problem the fixed scratch holds: Delta and LSE * log2(e), 4 bytes
+# per row each, each region rounded up to 256 bytes.
+_NOALLOC_ROWS = fa.BWD_NOALLOC_SCRATCH_BYTES // 8
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), fa.FA_ERR_INVALID), (dict(dv=None), fa.FA_ERR_INVALID),
+    (dict(lse=None), fa.FA_ERR_INVALID), (dict(dk=DK + 4), fa.FA_ERR_ALIGN),
+    (dict(D=32), fa.FA_ERR_UNSUPPORTED), (dict(Hq=4, Hkv=3), fa.FA_ERR_INVALID),
+    (dict(dq=Q), fa.FA_ERR_INVALID), (dict(scale=float("nan")), fa.FA_ERR_INVALID),
+    (dict(B=1, Hq=1, Hkv=1, N=_NOALLOC_ROWS + 1), fa.FA_ERR_SCRATCH),
+    (dict(B=4, Hq=32, Hkv=8, N=32768 + 1), fa.FA_ERR_SCRATCH),
+])
+def test_bwd_noalloc_rejects(kw, code):
+    # Every case fails a host-side check, before the scratch lookup (no GPU needed).
+    assert bwd_noalloc(**kw) == code
 
 
 def test_bwd_stages_reject():
