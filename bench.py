@@ -93,7 +93,38 @@ def cpu_baseline(w, n_heads: int):
             "sample": f"fp64 forward+backward of {n_heads} of the {w.B * w.Hq} (batch, head) "
                       f"slices (N={w.N}, D={w.D}, causal), {dt:.1f} s wall",
             "cpu_model": cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0)),
-            "tiny_single_thread": tiny_single_thread()}
+            "tiny_single_thread": tiny_single_thread(), "per_config": cpu_per_config()}
+
+
+def cpu_per_config() -> dict:
+    """The fp64 oracle on a bounded sample of every workload the parity tests
+    cover (all host threads): whole (batch, head) slices of each workload's
+    shape, drawn like it (seed 0), forward only except for the backward
+    workloads.  One query head of the multi-query / grouped N=32768 forward is
+    the same computation for Hkv = 1 and 8, so it is timed once for both."""
+    import oracle
+    import synth
+    samples = [("tiny", 1), ("noncausal", 4), ("causal_a", 2), ("causal_b", 2), ("mqa", 1),
+               ("bwd_d64", 1)]
+    out = {}
+    for name, heads in samples:
+        w = synth.WORKLOADS[name]
+        q, k, v, do = synth.generate(1, heads, heads, w.N, w.D, seed=0, variant=w.variant,
+                                     with_dout=True)
+        t0 = time.perf_counter()
+        oracle.attention_fwd(q, k, v, w.causal, w.scale)
+        if w.backward:
+            oracle.attention_bwd(q, k, v, do, w.causal, w.scale)
+        dt = time.perf_counter() - t0
+        per_head = (w.flops_fwd() + (w.flops_bwd() if w.backward else 0.0)) / (w.B * w.Hq)
+        key = "mqa_gqa" if name == "mqa" else name
+        out[key] = {"workload": f"B{w.B} Hq{w.Hq} Hkv{w.Hkv} N{w.N} D{w.D} "
+                                f"{'causal' if w.causal else 'non-causal'}"
+                                f"{' variant ' + w.variant if name.startswith('causal') else ''}",
+                    "pass": "forward+backward" if w.backward else "forward",
+                    "sample_heads": heads, "seconds": round(dt, 3),
+                    "tflops": round(per_head * heads / dt / 1e12, 4)}
+    return out
 
 
 def cpu_model() -> str:
@@ -125,6 +156,81 @@ def tiny_single_thread() -> dict:
     finally:
         oracle.set_num_threads(before)
     return {"seconds": round(sec, 4), "threads": threads, "gflops": round(w.flops_fwd() / sec / 1e9, 2)}
+
+
+def rescale_counts(q, k, causal: bool, scale: float, tau: float, bn: int = 64,
+                   rows_per_wave: int = 32, heads_per_chunk: int = 4):
+    """How often the forward's conditional rescale is taken on these inputs.
+
+    Follows the kernel's decision: per wave of `rows_per_wave` query rows and
+    per `bn`-key tile that the wave can see, the candidate max of each row is
+    max(m_ref, c * tile max of its scores), c = scale * log2(e); the wave
+    rescales (every row moves to its candidate) when any row's candidate
+    exceeds its m_ref by more than tau (log2 units).  Scores are formed the way
+    the kernel forms them (bf16 inputs, fp32 products and sums), on the device
+    the tensors live on.  Returns (steps taken, wave-tile steps).
+    q: [B, Hq, N, D], k: [B, Hkv, N, D] bf16."""
+    import torch
+    B, Hq, N, D = q.shape
+    G = Hq // k.shape[1]
+    c = scale / math.log(2.0)
+    nt = (N + bn - 1) // bn
+    nw = (N + rows_per_wave - 1) // rows_per_wave
+    taken = total = 0
+    heads = [(b, h) for b in range(B) for h in range(Hq)]
+    for i in range(0, len(heads), heads_per_chunk):
+        chunk = heads[i:i + heads_per_chunk]
+        qs = torch.stack([q[b, h] for b, h in chunk]).float()
+        ks = torch.stack([k[b, h // G] for b, h in chunk]).float()
+        s = torch.matmul(qs, ks.transpose(1, 2).contiguous())   # [h, N, N] fp32
+        if causal:
+            s.masked_fill_(torch.ones(N, N, dtype=torch.bool, device=s.device).triu_(1), -math.inf)
+        pad = nt * bn - N
+        if pad:
+            s = torch.nn.functional.pad(s, (0, pad), value=-math.inf)
+        tmax = s.view(len(chunk), N, nt, bn).amax(-1) * c        # [h, N, nt]
+        del s
+        rpad = nw * rows_per_wave - N
+        if rpad:
+            tmax = torch.nn.functional.pad(tmax, (0, 0, 0, rpad), value=-math.inf)
+        tmax = tmax.reshape(len(chunk), nw, rows_per_wave, nt)
+        m_ref = torch.full(tmax.shape[:3], -math.inf, device=tmax.device)
+        last_row = torch.clamp(torch.arange(nw, device=tmax.device) * rows_per_wave
+                               + rows_per_wave - 1, max=N - 1)
+        for kt in range(nt):
+            if causal:
+                visible = kt * bn <= last_row
+            else:
+                visible = torch.ones_like(last_row, dtype=torch.bool)
+            m_new = torch.maximum(m_ref, tmax[..., kt])
+            trig = (m_new > m_ref + tau).any(-1) & visible[None, :]
+            m_ref = torch.where(trig[..., None], m_new, m_ref)
+            taken += int(trig.sum())
+            total += int(visible.sum()) * len(chunk)
+    return taken, total
+
+
+def rescale_report(torch, dev) -> dict:
+    """Rescale rate of the forward on the long causal inputs (variants a and b)
+    with the kernel's tiles (32-row waves, 64-key tiles), at tau = 8 and at
+    tau = 0 (a rescale whenever a row max grows).  The hotelren summary
+    (section 3.3) reports about 85% fewer rescales with tau = 8."""
+    import synth
+    out = {}
+    for var in ("a", "b"):
+        w = synth.WORKLOADS[f"causal_{var}"]
+        q, k, _ = (t.to(dev) for t in synth.generate_workload(w))
+        t8, n = rescale_counts(q, k, True, w.scale, 8.0)
+        t0, _ = rescale_counts(q, k, True, w.scale, 0.0)
+        out[f"variant_{var}"] = {"wave_tile_steps": n, "rescaled_tau8": t8, "rescaled_tau0": t0,
+                                 "rate_tau8": round(t8 / n, 4), "rate_tau0": round(t0 / n, 4),
+                                 "fewer_rescales_than_tau0": round(1 - t8 / max(t0, 1), 4)}
+        del q, k
+    out["pages_fewer_rescales"] = 0.85
+    out["what"] = ("forward conditional rescale on the B2 H16 N8192 D128 causal inputs: (wave, "
+                   "64-key tile) steps that rescaled with tau = 8 (the method) and with tau = 0; "
+                   "the first tile of each wave always rescales")
+    return out
 
 
 def bench_varlen(fa, torch, dev, stream, reps: int = 20) -> dict:
@@ -403,8 +509,8 @@ def bench_other_configs(fa, torch, dev, stream, reps: int = 5) -> dict:
     """Throughput at the other configurations the parity tests cover (inputs
     seeded N(0,1), drawn on the device): the non-causal forward B4 H16 N2048
     D128, the multi-query and grouped causal forwards B1 Hq32 Hkv1 / Hkv8
-    N32768 D128, and the causal backward B2 H16 N16384 D64 in its two
-    fixed-order dQ modes (whole fa_bwd call)."""
+    N32768 D128, and the causal backward B2 H16 N16384 D64 in its three dQ
+    modes (whole fa_bwd call)."""
     sh = stream.cuda_stream
     g = torch.Generator(device=dev)
     g.manual_seed(0)
@@ -459,7 +565,7 @@ def bench_other_configs(fa, torch, dev, stream, reps: int = 5) -> dict:
     if fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, H, N, D,
                  1, scale, sh) != 0:
         raise RuntimeError("fa_fwd failed")
-    for det, tag in ((1, "stored"), (2, "recompute")):
+    for det, tag in ((1, "stored"), (2, "recompute"), (0, "atomic")):
         wsb = fa.fa_bwd_workspace_size(B, H, H, N, D, det)
         ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
 
@@ -678,6 +784,8 @@ def main() -> int:
     if not args.no_extras:
         log("forward choices: exp2 polynomial share, rescale-heavy inputs")
         out["fwd_choices"] = bench_fwd_choices(fa, torch, dev, stream, P, w)
+        log("forward rescale rate on the headline inputs")
+        out["fwd_choices"]["rescale_rate"] = rescale_report(torch, dev)
         out["extras"] = {"varlen_fwd": bench_varlen(fa, torch, dev, stream),
                          "varlen_bwd": bench_varlen_bwd(fa, torch, dev, stream),
                          "grouped_fwd_bwd": bench_grouped(fa, torch, dev, stream),

@@ -83,3 +83,26 @@ def test_trigger_rate_reported():
               f"(every step that grows the max with tau=0: {rate0:.1%})")
     assert rates["a"][0] < rates["b"][0]
     assert rates["a"][0] < rates["a"][1]
+
+
+@pytest.mark.parametrize("variant", ["a", "b"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("tau", [0.0, 8.0])
+def test_bench_rescale_count_matches_the_model(tau, causal, variant):
+    # bench.py counts the rescales on the headline inputs with a vectorised
+    # form of the same decision (fp32 scores, as the kernel forms them); on
+    # small inputs it must agree with this fp64 model step for step.
+    import bench
+    N, D = 300, 32
+    q, k, v = synth.generate(1, 2, 1, N, D, seed=5, variant=variant)
+    scale = 1.0 / math.sqrt(D)
+    taken, total = bench.rescale_counts(q, k, causal, scale, tau, heads_per_chunk=1)
+    want_taken = want_total = 0
+    for h in range(2):
+        _, _, rate = tiled_model(q[:, h:h + 1], k, v, causal, scale, tau)
+        steps = sum(len(range(0, min(N, min(N, w0 + 32)) if causal else N, 64))
+                    for w0 in range(0, N, 32))
+        want_total += steps
+        want_taken += round(rate * steps)
+    assert total == want_total
+    assert taken == want_taken
