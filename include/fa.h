@@ -1,9 +1,13 @@
 /*
  * fa.h -- C ABI of the fused exact-attention library for AMD Instinct MI355X (gfx950).
  *
- * The library computes O = softmax(scale * Q K^T) V and its gradients without
- * ever forming the N x N score matrix: Q tiles stay resident while K/V tiles
- * stream past them, with a running row max and row sum (online softmax).
+ * The library computes O = softmax(scale * Q K^T) V and its gradients.  The
+ * forward never forms the N x N score matrix: Q tiles stay resident while K/V
+ * tiles stream past them, with a running row max and row sum (online
+ * softmax).  The backward recomputes the probabilities tile by tile; its
+ * fastest dQ mode (deterministic = 1) does keep one N x N quantity, the bf16
+ * dS blocks on and below the diagonal, in the caller's workspace, while modes
+ * 0 and 2 need only O(N) workspace per head (see fa_bwd).
  * Passages followed:
  *   - tiling and online softmax: "FlashAttention-4 算法解析" (zeeklog), section 4,
  *     the tiled forward pseudocode;
