@@ -175,15 +175,19 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(const uint16_t* __
   float m_ref = -__builtin_inff();
   float l_part = 0.f;  // this lane half's share of the row sum
 
-  // Every wave walks all tiles of the workgroup; a tile wholly above a wave's
-  // diagonal is masked to -inf and adds exactly nothing.  With 256-query
-  // workgroups and 64-key tiles, waves 0..5 walk 3, 3, 2, 2, 1, 1 such tiles
-  // on the diagonal workgroup of each head (about 2.3% of the forward's
-  // matrix work); they are kept so the pipeline has no per-wave branch.
-  // Split-KV causal rows see keys up to Nk - Nq + (row mod Nq): no tile-level
-  // cut, the mask handles it.
+  // The workgroup walks the tiles up to its last query; each wave computes
+  // only those up to its own diagonal (klast) and after that just meets the
+  // barriers and takes its share of the copies.  With 256-query workgroups
+  // and 64-key tiles, waves 0..5 would otherwise walk 3, 3, 2, 2, 1, 1 tiles
+  // that their causal mask clears entirely (about 2.3% of the forward's
+  // matrix work, most of it in the short workgroups that run last).  On its
+  // last tile a wave still forms S^T(klast+1), unused: leaving those products
+  // out through a second instantiation of phase A made the register
+  // allocator spill.  Split-KV causal rows see keys up to
+  // Nk - Nq + (row mod Nq): no tile-level cut, the mask handles it.
   const int kend = (CAUSAL && MODE != kModeSplit) ? min(N, q0 + BM) : Nkv;
   const int ntiles = (kend + BN - 1) / BN;
+  const int klast = (CAUSAL && MODE != kModeSplit) ? min(qw + 31, N - 1) / BN : ntiles - 1;
 
   // ---- direct HBM -> LDS staging -------------------------------------------
   // Load s of this wave fills LDS chunks g = (s*NW + wave)*64 + lane of the
@@ -421,11 +425,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(const uint16_t* __
       if constexpr (MODE == kModeSplit)
         if (qw >= N) return;
       if constexpr (LAG) {
-        if (kt > 0) phase_b(vp, sv, m_new);
-        phase_a(kt, kn, sv, sn, m_new);
+        if (kt > 0 && kt <= klast + 1) phase_b(vp, sv, m_new);
+        if (kt <= klast) phase_a(kt, kn, sv, sn, m_new);
       } else {
-        phase_a(kt, kn, sv, sn, m_new);
-        phase_b(vc, sn, m_new);
+        if (kt <= klast) {
+          phase_a(kt, kn, sv, sn, m_new);
+          phase_b(vc, sn, m_new);
+        }
       }
     };
     // K(j) lives in kbuf[j % 2] and V(j) in vbuf[j % 4] (vbuf2, vbuf3 alias
@@ -443,7 +449,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(const uint16_t* __
     // The lagging waves still owe B(last); its max (of a tile past the end)
     // is not used.
     if constexpr (LAG) {
-      if (ntiles > 0) {
+      if (ntiles > 0 && ntiles - 1 <= klast) {
         const int r = (ntiles - 1) & 3;
         phase_b(r == 0 ? vbuf0 : r == 1 ? vbuf1 : r == 2 ? vbuf2 : vbuf3, sA, m_new);
       }
