@@ -114,3 +114,38 @@ def test_noalloc_too_large_launches_nothing():
     rc = fa.fa_bwd_noalloc(1 << 36, 2 << 36, 3 << 36, 4 << 36, 5 << 36, 6 << 36, 7 << 36, 8 << 36,
                            9 << 36, 1, 1, 1, rows, 64, 1, 0.125, None)
     assert rc == fa.FA_ERR_SCRATCH
+
+
+def test_noalloc_inside_a_captured_graph():
+    # The use the entry point exists for: captured into a HIP graph (where no
+    # allocation may happen) and replayed.  The first call on the device, made
+    # before capture, looks up the scratch address; each replay, with eager
+    # work and a synchronization between replays, must equal the eager result
+    # bit for bit (dQ mode 2 is deterministic).
+    B, Hq, Hkv, N, D, causal = 1, 4, 2, 320, 128, True
+    say(f"noalloc graph capture B{B} Hq{Hq} Hkv{Hkv} N{N} D{D} causal={causal}")
+    _, t, scale = _inputs(B, Hq, Hkv, N, D, causal, seed=11)
+    eager = _noalloc(t, B, Hq, Hkv, N, D, causal, scale)
+    qd, kd, vd, o, lse, dod = t
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            rc = fa.fa_bwd_noalloc(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(),
+                                   lse.data_ptr(), dod.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                   dv.data_ptr(), B, Hq, Hkv, N, D, int(causal), scale,
+                                   side.cuda_stream)
+            assert rc == fa.FA_OK, fa.fa_strerror(rc)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for x in (dq, dk, dv):
+            x.fill_(7.0)
+        graph.replay()
+        torch.cuda.synchronize()
+        for g, r, name in zip((dq, dk, dv), eager, ("dQ", "dK", "dV")):
+            _bitwise(g, r, f"replay {rep + 1} {name}")
+        # eager work between replays, on the same scratch
+        _noalloc(t, B, Hq, Hkv, N, D, causal, scale)
