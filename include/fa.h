@@ -180,6 +180,8 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, voi
  *     serialized by the caller.  Nothing in it needs clearing between calls.
  * The first call on a device looks the buffer's device address up once
  * (hipGetSymbolAddress, with that device current); no call allocates or frees.
+ * The buffer used is the current device's, so stream must be a stream of the
+ * current device (or NULL).
  * Errors as fa_bwd, plus FA_ERR_SCRATCH; FA_ERR_HIP also if the lookup fails.
  */
 int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
