@@ -187,7 +187,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(const uint16_t* __
   // Nk - Nq + (row mod Nq): no tile-level cut, the mask handles it.
   const int kend = (CAUSAL && MODE != kModeSplit) ? min(N, q0 + BM) : Nkv;
   const int ntiles = (kend + BN - 1) / BN;
-  const int klast = (CAUSAL && MODE != kModeSplit) ? min(qw + 31, N - 1) / BN : ntiles - 1;
+  // A wave whose rows all lie past the end (short sequences, ragged tails)
+  // computes nothing (klast = -1); its stores fall outside the buffer ranges.
+  int klast = (CAUSAL && MODE != kModeSplit) ? min(qw + 31, N - 1) / BN : ntiles - 1;
+  if (MODE != kModeSplit && qw >= N) klast = -1;
 
   // ---- direct HBM -> LDS staging -------------------------------------------
   // Load s of this wave fills LDS chunks g = (s*NW + wave)*64 + lane of the
