@@ -278,8 +278,7 @@ def bench_varlen(fa, torch, dev, stream, reps: int = 20) -> dict:
 def bench_varlen_bwd(fa, torch, dev, stream, det: int = 2, reps: int = 10) -> dict:
     """Variable-length backward (fa_bwd_varlen: preprocess, both work lists,
     dK/dV and dQ passes) on the packed workload of synth.VARLEN, dQ mode det
-    (2: fixed order, deterministic; the stored-dS mode has no variable-length
-    form)."""
+    (1: fixed order from stored dS blocks; 2: fixed order, recomputing dS)."""
     import synth
     w = synth.VARLEN
     lens = synth.varlen_lengths(w["n_seqs"], w["total"], w["lo"], w["hi"])
@@ -293,7 +292,7 @@ def bench_varlen_bwd(fa, torch, dev, stream, det: int = 2, reps: int = 10) -> di
     lse = torch.empty((Hq, total), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     fws = torch.empty(fa.fa_fwd_varlen_workspace_size(B, total), dtype=torch.uint8, device=dev)
-    wsb = fa.fa_bwd_varlen_workspace_size(B, Hq, Hkv, total, D, det)
+    wsb = fa.fa_bwd_varlen_workspace_size(B, Hq, Hkv, total, max(lens), D, det)
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
     sh = stream.cuda_stream
     rc = fa.fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
@@ -788,6 +787,7 @@ def main() -> int:
         out["fwd_choices"]["rescale_rate"] = rescale_report(torch, dev)
         out["extras"] = {"varlen_fwd": bench_varlen(fa, torch, dev, stream),
                          "varlen_bwd": bench_varlen_bwd(fa, torch, dev, stream),
+                         "varlen_bwd_stored_ds": bench_varlen_bwd(fa, torch, dev, stream, det=1),
                          "grouped_fwd_bwd": bench_grouped(fa, torch, dev, stream),
                          "decode_splitkv": bench_decode(fa, torch, dev, stream),
                          "fp8_fwd": bench_fp8(fa, torch, dev, stream, P, w),

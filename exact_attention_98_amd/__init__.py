@@ -97,7 +97,7 @@ def load():
     lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, ci, vp, sz,
                                    vp]
     lib.fa_fwd_splitkv.restype = ci
-    lib.fa_bwd_varlen_workspace_size.argtypes = [ci] * 6
+    lib.fa_bwd_varlen_workspace_size.argtypes = [ci] * 7
     lib.fa_bwd_varlen_workspace_size.restype = sz
     lib.fa_bwd_varlen.argtypes = [vp] * 10 + [ci] * 7 + [cf, vp, sz, ci, vp]
     lib.fa_bwd_varlen.restype = ci
@@ -190,8 +190,9 @@ def fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, D, causal, scale, num_sp
                                  stream)
 
 
-def fa_bwd_varlen_workspace_size(B, Hq, Hkv, total, D, deterministic) -> int:
-    return int(load().fa_bwd_varlen_workspace_size(B, Hq, Hkv, total, D, int(deterministic)))
+def fa_bwd_varlen_workspace_size(B, Hq, Hkv, total, max_seqlen, D, deterministic) -> int:
+    return int(load().fa_bwd_varlen_workspace_size(B, Hq, Hkv, total, int(max_seqlen), D,
+                                                   int(deterministic)))
 
 
 def fa_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens, B, Hq, Hkv, total, max_seqlen, D,
@@ -399,8 +400,9 @@ def forward_splitkv(q, k, v, causal: bool, scale: float, *, num_splits: int = 0,
 
 def backward_varlen(q, k, v, o, lse, dout, cu_seqlens, max_seqlen: int, causal: bool,
                     scale: float, *, deterministic: int = 0, workspace=None):
-    """dQ, dK, dV (bf16) of forward_varlen; deterministic is 0 (atomic) or 2
-    (fixed order, recomputing dS)."""
+    """dQ, dK, dV (bf16) of forward_varlen; deterministic is 0 (atomic), 1
+    (fixed order from stored dS blocks; every sequence at most max_seqlen
+    long) or 2 (fixed order, recomputing dS)."""
     import torch
     Hq, total, D = q.shape
     Hkv = k.shape[0]
@@ -414,11 +416,11 @@ def backward_varlen(q, k, v, o, lse, dout, cu_seqlens, max_seqlen: int, causal: 
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     if total == 0:
         return dq, dk, dv
-    ws_bytes = fa_bwd_varlen_workspace_size(B, Hq, Hkv, total, D, deterministic)
-    if ws_bytes == 0:
-        raise FaError(FA_ERR_INVALID, "fa_bwd_varlen_workspace_size")
+    ws_bytes = fa_bwd_varlen_workspace_size(B, Hq, Hkv, total, max_seqlen, D, deterministic)
     if workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+        # A size of 0 marks an invalid argument: the call below then reports
+        # which one (it checks the arguments before the workspace).
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=q.device)
     rc = fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                        dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                        cu_seqlens.data_ptr(), B, Hq, Hkv, total, int(max_seqlen), D, causal, scale,

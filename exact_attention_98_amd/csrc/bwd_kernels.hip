@@ -57,6 +57,9 @@ struct BwdParams {
   float* lse2;     // fp32 [B][Hq][N]
   char* ds;        // dS^T blocks (stored-dS mode), ds_head bytes per (b, hq)
   uint32_t ds_head;
+  // Stored-dS mode with packed sequences: sequence b's blocks start at block
+  // blk_off[b] of each head's region (B + 1 entries, clamped to its size).
+  const int* blk_off;
   int hsplit;      // query-head parts per K/V head (warp-specialized kernel)
   float* kv_part;  // fp32 partial dK, dV when hsplit > 1
   int nb32;        // 32-row blocks per head, ceil(N / 32)
@@ -670,7 +673,6 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
   constexpr bool PREF = STORE_DS && D == 128;  // score-wave reads ahead of the barrier
   static_assert(NLD >= 1, "step tile too small");
   static_assert(DQM != kDqAtomic, "atomic dQ uses bwd_atomic_kernel");
-  static_assert(!(VARLEN && DQM == kDqStored), "no stored-dS layout for packed sequences");
   constexpr int STAGE = 2 * TB + 512;  // Q, dO, 256 B LSE * log2 e, 256 B Delta
   constexpr int PSLOT = 4 * 4096;      // P, dS of the 4 score waves
   __shared__ __attribute__((aligned(1024))) char st0[STAGE];
@@ -840,13 +842,25 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
     // 1024u + 16 lane of the block (whole cache lines per store); a block that
     // does not exist (padding rows, or above the diagonal under causal) gets
     // an offset past the end of the head's range and the store is dropped.
+    // Packed sequences: the sequence's own grid of ceil(N / 32)^2 blocks,
+    // from block blk_off[b] of the head's region, its range limited to the
+    // blocks the offsets give it.
     const int kb32 = kw / 32;
     const uint32_t ds_lane = (uint32_t)lane * 16u;
+    const int nb32s = VARLEN ? (N + 31) / 32 : p.nb32;
+    size_t ds_seq = 0;
+    uint32_t ds_range = p.ds_head;
+    if constexpr (VARLEN && STORE_DS) {
+      const int o0 = p.blk_off[b], o1 = p.blk_off[b + 1];
+      ds_seq = (size_t)o0 * 2048;
+      ds_range = (uint32_t)max(o1 - o0, 0) * 2048u;
+    }
     auto store_ds = [&](int u, u32x4 w) {
       if constexpr (STORE_DS) {
-        const rsrc_t r = make_rsrc_uniform(p.ds + ((size_t)b * p.Hq + hq0 + cur_g) * p.ds_head, p.ds_head);
-        const bool ok = cur_qs < p.nb32 && kb32 < p.nb32 && (!CAUSAL || kb32 <= cur_qs);
-        const uint32_t off = ok ? (uint32_t)(cur_qs * p.nb32 + kb32) * 2048u : 0xFFFFF000u;
+        const size_t hidx = (VARLEN ? 0 : (size_t)b * p.Hq) + hq0 + cur_g;
+        const rsrc_t r = make_rsrc_uniform(p.ds + hidx * p.ds_head + ds_seq, ds_range);
+        const bool ok = cur_qs < nb32s && kb32 < nb32s && (!CAUSAL || kb32 <= cur_qs);
+        const uint32_t off = ok ? (uint32_t)(cur_qs * nb32s + kb32) * 2048u : 0xFFFFF000u;
         // Non-temporal (NT): dS is read once, by the dQ pass, so the caches
         // keep K, V and the step tiles instead, and the dQ pass does not first
         // write back lines left dirty here.
@@ -1300,7 +1314,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t* __restri
 // row); key tiles of 64 (two blocks) in ascending order, so the sum order is
 // fixed.  Per tile: K (shared) and this wave's two dS^T blocks are copied
 // into LDS; dQ^T += K^T dS^T with both operands by transposing reads.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(256, 2) void bwd_dq_ds_kernel(const uint16_t* __restrict__ K,
                                                            uint16_t* __restrict__ dQ, BwdParams p,
                                                            int nqb) {
@@ -1316,16 +1330,41 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_kernel(const uint16_t* __res
   __shared__ __attribute__((aligned(1024))) char dbuf0[NW * 4096];
   __shared__ __attribute__((aligned(1024))) char dbuf1[NW * 4096];
 
-  const int BH = p.B * p.Hq;
+  // Work item: (batch, query head, 128-query tile), or for packed sequences
+  // (sequence, tile) pairs from a list sorted largest first, heads fastest.
   const int wg = blockIdx.x;
-  const int bh = wg % BH;
-  const int qb = nqb - 1 - wg / BH;
-  const int b = bh / p.Hq, hq = bh % p.Hq;
-  const int hk = hq / p.G;
-  const size_t head_elems = (size_t)p.N * D;
-  const uint32_t head_bytes = (uint32_t)(head_elems * 2);
-  const uint16_t* Kh = K + ((size_t)b * (p.Hq / p.G) + hk) * head_elems;
-  const char* dsh = p.ds + (size_t)bh * p.ds_head;
+  int qb, N, nb32;
+  size_t qrow, kvrow;   // first row of this (sequence, head) in dQ and in K
+  const char* dsh;      // this (sequence, head)'s block grid
+  uint32_t ds_range;
+  if constexpr (VARLEN) {
+    const int item = wg / p.Hq;
+    const int hq = wg % p.Hq;
+    if (item >= *p.n_items) return;
+    const int b = p.items[2 * item];
+    qb = p.items[2 * item + 1];
+    const int s0 = min(max(p.cu[b], 0), p.total);
+    N = min(max(p.cu[b + 1] - s0, 0), p.total - s0);
+    nb32 = (N + 31) / 32;
+    qrow = (size_t)hq * p.total + s0;
+    kvrow = (size_t)(hq / p.G) * p.total + s0;
+    const int o0 = p.blk_off[b], o1 = p.blk_off[b + 1];
+    dsh = p.ds + (size_t)hq * p.ds_head + (size_t)o0 * 2048;
+    ds_range = (uint32_t)max(o1 - o0, 0) * 2048u;
+  } else {
+    const int BH = p.B * p.Hq;
+    const int bh = wg % BH;
+    qb = nqb - 1 - wg / BH;
+    const int b = bh / p.Hq, hq = bh % p.Hq;
+    N = p.N;
+    nb32 = p.nb32;
+    qrow = (size_t)bh * N;
+    kvrow = ((size_t)b * (p.Hq / p.G) + hq / p.G) * N;
+    dsh = p.ds + (size_t)bh * p.ds_head;
+    ds_range = p.ds_head;
+  }
+  const uint32_t head_bytes = (uint32_t)((size_t)N * D * 2);
+  const uint16_t* Kh = K + kvrow * D;
 
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
@@ -1333,7 +1372,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_kernel(const uint16_t* __res
   const int q0 = qb * BM;
   const int qb32 = qb * 4 + wave;   // this wave's query block
 
-  const int kend = CAUSAL ? min(p.N, q0 + BM) : p.N;
+  const int kend = CAUSAL ? min(N, q0 + BM) : N;
   const int ntiles = (kend + BN - 1) / BN;
 
   uint32_t ld_off[NLD];
@@ -1362,8 +1401,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_kernel(const uint16_t* __res
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int kb32 = 2 * kt + j;
-      const bool ok = qb32 < p.nb32 && kb32 < p.nb32 && (!CAUSAL || kb32 <= qb32);
-      const uint32_t off = ok ? (uint32_t)(qb32 * p.nb32 + kb32) * 2048u : 0u;
+      const uint32_t blk = (uint32_t)(qb32 * nb32 + kb32);
+      const bool ok = qb32 < nb32 && kb32 < nb32 && (!CAUSAL || kb32 <= qb32) &&
+                      (blk + 1) * 2048u <= ds_range;
+      const uint32_t off = ok ? blk * 2048u : 0u;
       const rsrc_t dr = make_rsrc_uniform(dsh + off, ok ? 2048u : 0u);
 #pragma unroll
       for (int s = 0; s < 2; ++s)
@@ -1431,7 +1472,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_kernel(const uint16_t* __res
   // (register r of block db) is d = 32 db + 8 (r/4) + 4 h + r % 4.
   const int pu = n >> 4, ph = (n >> 3) & 1, pi = n & 7;
   const int qi = qb32 * 32 + 16 * pu + 4 * ph + (pi & 3) + 8 * (pi >> 2);
-  const rsrc_t out = make_rsrc_uniform(dQ + (size_t)bh * head_elems, head_bytes);
+  const rsrc_t out = make_rsrc_uniform(dQ + qrow * D, head_bytes);
 #pragma unroll
   for (int db = 0; db < ND; ++db)
 #pragma unroll
@@ -1491,6 +1532,7 @@ BwdParams make_params(const BwdArgs& a) {
   p.hsplit = lay.hsplit;
   p.kv_part = lay.hsplit > 1 ? (float*)(ws + lay.kv_part) : nullptr;
   p.cu = nullptr;
+  p.blk_off = nullptr;
   p.total = 0;
   p.items = nullptr;
   p.n_items = nullptr;
@@ -1568,10 +1610,10 @@ hipError_t launch_dq_ds_d(const BwdArgs& a, hipStream_t s) {
   const int nqb = (a.N + 127) / 128;
   const dim3 grid((unsigned)(a.B * a.Hq * nqb));
   if (a.causal)
-    hipLaunchKernelGGL((bwd_dq_ds_kernel<D, true>), grid, dim3(256), 0, s, (const uint16_t*)a.k,
+    hipLaunchKernelGGL((bwd_dq_ds_kernel<D, true, false>), grid, dim3(256), 0, s, (const uint16_t*)a.k,
                        (uint16_t*)a.dq, p, nqb);
   else
-    hipLaunchKernelGGL((bwd_dq_ds_kernel<D, false>), grid, dim3(256), 0, s, (const uint16_t*)a.k,
+    hipLaunchKernelGGL((bwd_dq_ds_kernel<D, false, false>), grid, dim3(256), 0, s, (const uint16_t*)a.k,
                        (uint16_t*)a.dq, p, nqb);
   return hipGetLastError();
 }
@@ -1592,25 +1634,76 @@ hipError_t launch_dq_d(const BwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Variable-length backward (dQ modes 0 and 2).  The BwdArgs describe the
+// Stored-dS mode with packed sequences: where each sequence's dS blocks start
+// in a head's region.  blk_off[b] = sum over b' < b of ceil(len_b' / 32)^2
+// (each sequence's full square grid of 32 x 32 blocks, of which the causal
+// part is written), clamped to the region's cap_blocks.  One workgroup: each
+// thread sums a run of sequences, a scan over the 1024 partial sums, then each
+// thread writes its run.  cu_seqlens entries are clamped into [0, total] as
+// in the other kernels.
+constexpr int kOffThreads = 1024;
+__global__ __launch_bounds__(kOffThreads) void varlen_block_offsets_kernel(const int* __restrict__ cu,
+                                                                          int B, int total,
+                                                                          int cap_blocks,
+                                                                          int* __restrict__ blk_off) {
+  __shared__ long long part[kOffThreads];
+  const int tid = threadIdx.x;
+  const int per = (B + kOffThreads - 1) / kOffThreads;
+  const int b0 = min(tid * per, B), b1 = min(b0 + per, B);
+  auto blocks = [&](int b) -> long long {
+    const int s0 = min(max(cu[b], 0), total);
+    const int len = min(max(cu[b + 1] - s0, 0), total - s0);
+    const long long nb = (len + 31) / 32;
+    return nb * nb;
+  };
+  long long sum = 0;
+  for (int b = b0; b < b1; ++b) sum += blocks(b);
+  part[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < kOffThreads; off <<= 1) {
+    const long long add = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += add;
+    __syncthreads();
+  }
+  long long run = tid > 0 ? part[tid - 1] : 0;
+  for (int b = b0; b < b1; ++b) {
+    blk_off[b] = (int)min(run, (long long)cap_blocks);
+    run += blocks(b);
+  }
+  if (tid == kOffThreads - 1) blk_off[B] = (int)min(part[kOffThreads - 1], (long long)cap_blocks);
+}
+
+// Variable-length backward (dQ modes 0, 1 and 2).  The BwdArgs describe the
 // packed tensors as one batch of total rows (a.B = 1, a.N = total), so the
 // preprocess and the atomic-mode convert run over every row unchanged.
 template <int D, bool CAUSAL>
-hipError_t launch_bwd_varlen_t(const BwdArgs& a, const VarlenArgs& v, hipStream_t s) {
-  // (Hkv = Hq in the layout: the variable-length backward has no head split.)
-  const BwdLayout lay = bwd_layout(1, a.Hq, a.Hq, v.total, D, a.deterministic);
-  char* lists = (char*)a.workspace + lay.total;
-  const size_t lbytes = varlen_workspace_bytes(v.B, v.total);
-  int* main_n = (int*)lists;
-  int* main_items = (int*)(lists + 256);
-  int* dq_n = (int*)(lists + lbytes);
-  int* dq_items = (int*)(lists + lbytes + 256);
+hipError_t launch_bwd_varlen_t(const BwdArgs& a_in, const VarlenArgs& v, hipStream_t s) {
+  const VarlenBwdLayout vl = bwd_varlen_layout(v.B, a_in.Hq, v.total, D, a_in.deterministic, v.max_seqlen);
+  char* ws = (char*)a_in.workspace;
+  int* main_n = (int*)(ws + vl.main_list);
+  int* main_items = (int*)(ws + vl.main_list + 256);
+  int* dq_n = (int*)(ws + vl.dq_list);
+  int* dq_items = (int*)(ws + vl.dq_list + 256);
   const unsigned items_max = (unsigned)varlen_item_capacity(v.B, v.total);
   constexpr int QS = 4096 / D;
+  const bool stored = a_in.deterministic == kDqStored;
+  // The row constants (and, mode 0, the fp32 dQ accumulator) sit where the
+  // dense layout of B = 1, N = total puts them; the stored-dS mode takes the
+  // recompute mode's rows-only layout and adds its block grids after it.
+  BwdArgs a = a_in;
+  if (stored) a.deterministic = kDqRecompute;
   hipError_t e = launch_varlen_schedule(v, CAUSAL, 1, QS, kBwdBN, main_n, main_items, s);
   if (e != hipSuccess) return e;
-  if (a.deterministic == kDqRecompute) {
+  if (a_in.deterministic != kDqAtomic) {
     e = launch_varlen_schedule(v, CAUSAL, 0, QS, 128, dq_n, dq_items, s);
+    if (e != hipSuccess) return e;
+  }
+  int* blk_off = (int*)(ws + vl.blk_off);
+  if (stored) {
+    hipLaunchKernelGGL(varlen_block_offsets_kernel, dim3(1), dim3(kOffThreads), 0, s, v.cu, v.B, v.total,
+                       vl.cap_blocks, blk_off);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   e = launch_pre_d<D>(a, s);
@@ -1622,8 +1715,20 @@ hipError_t launch_bwd_varlen_t(const BwdArgs& a, const VarlenArgs& v, hipStream_
   p.kv_part = nullptr;
   p.items = main_items;
   p.n_items = main_n;
+  if (stored) {
+    p.ds = ws + vl.ds;
+    p.ds_head = (uint32_t)vl.ds_head;
+    p.blk_off = blk_off;
+  }
   if (a.deterministic == kDqAtomic) {
     e = launch_atomic_t<D, CAUSAL, true>(a, p, s, items_max);
+  } else if (stored) {
+    // The warp-specialized kernel over the (sequence, key tile) list, storing dS.
+    hipLaunchKernelGGL((bwd_ws_kernel<D, CAUSAL, kDqStored, true>), dim3(items_max * (unsigned)a.Hkv),
+                       dim3(512), 0, s, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                       (const uint16_t*)a.v, (const uint16_t*)a.dout, (uint16_t*)a.dk,
+                       (uint16_t*)a.dv, p);
+    e = hipGetLastError();
   } else {
     // The warp-specialized kernel over the (sequence, key tile) list.
     hipLaunchKernelGGL((bwd_ws_kernel<D, CAUSAL, kDqRecompute, true>), dim3(items_max * (unsigned)a.Hkv),
@@ -1641,16 +1746,48 @@ hipError_t launch_bwd_varlen_t(const BwdArgs& a, const VarlenArgs& v, hipStream_
   }
   p.items = dq_items;
   p.n_items = dq_n;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, true>), dim3(items_max * (unsigned)a.Hq), dim3(256), 0,
-                     s, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (const uint16_t*)a.dout, (uint16_t*)a.dq, p, 0);
+  if (stored)
+    hipLaunchKernelGGL((bwd_dq_ds_kernel<D, CAUSAL, true>), dim3(items_max * (unsigned)a.Hq), dim3(256), 0,
+                       s, (const uint16_t*)a.k, (uint16_t*)a.dq, p, 0);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, true>), dim3(items_max * (unsigned)a.Hq), dim3(256), 0,
+                       s, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.dout, (uint16_t*)a.dq, p, 0);
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t bwd_varlen_workspace_bytes(int B, int Hq, int total, int D, int deterministic) {
-  return bwd_layout(1, Hq, Hq, total, D, deterministic).total + 2 * varlen_workspace_bytes(B, total);
+size_t varlen_ds_head_bytes(int B, int total, int max_seqlen) {
+  // Sum over sequences of ceil(len / 32)^2 <= (sum of ceil(len / 32)) *
+  // (largest ceil(len / 32)) <= (ceil(total / 32) + B) * ceil(max_seqlen / 32)
+  // when no sequence is longer than max_seqlen.
+  const size_t nsum = ((size_t)total + 31) / 32 + (size_t)B;
+  const size_t nmax = ((size_t)max_seqlen + 31) / 32;
+  return nsum * nmax * 2048;
+}
+
+VarlenBwdLayout bwd_varlen_layout(int B, int Hq, int total, int D, int deterministic, int max_seqlen) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  VarlenBwdLayout l;
+  const bool stored = deterministic == kDqStored;
+  size_t off = bwd_layout(1, Hq, Hq, total, D, stored ? kDqRecompute : deterministic).total;
+  l.ds = off;
+  l.ds_head = stored ? varlen_ds_head_bytes(B, total, max_seqlen) : 0;
+  l.cap_blocks = stored ? (int)(l.ds_head / 2048) : 0;
+  off += stored ? up((size_t)Hq * l.ds_head) : 0;
+  l.main_list = off;
+  off += varlen_workspace_bytes(B, total);
+  l.dq_list = off;
+  off += varlen_workspace_bytes(B, total);
+  l.blk_off = off;
+  off += stored ? up((size_t)(B + 1) * 4) : 0;
+  l.total = off;
+  return l;
+}
+
+size_t bwd_varlen_workspace_bytes(int B, int Hq, int total, int D, int deterministic, int max_seqlen) {
+  return bwd_varlen_layout(B, Hq, total, D, deterministic, max_seqlen).total;
 }
 
 hipError_t launch_bwd_varlen(const BwdArgs& a, const VarlenArgs& v, hipStream_t s) {

@@ -135,6 +135,16 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
 
 namespace {
 
+// dQ mode of the variable-length backward: 0, 1 or 2; in mode 1 one head's
+// region of dS blocks (bounded by total, B and max_seqlen) is addressed with
+// 32-bit offsets, as in the dense stored-dS mode.
+int check_varlen_mode(int B, int total, int max_seqlen, int deterministic) {
+  if (deterministic < 0 || deterministic > 2) return FA_ERR_INVALID;
+  if (deterministic == 1 && fa::varlen_ds_head_bytes(B, total, max_seqlen) > 0xFFFFF000ull - 4096)
+    return FA_ERR_TOO_LARGE;
+  return FA_OK;
+}
+
 // Shape checks of the split-KV forward (q and k checked as their own
 // tensors, which may differ in length).
 int check_split(int B, int Hq, int Hkv, int Nq, int Nk, int D, int causal, float scale) {
@@ -163,12 +173,13 @@ int check_split_partials(int Hq, int Hkv, int Nq, int D, int splits) {
 
 extern "C" {
 
-size_t fa_bwd_varlen_workspace_size(int B, int Hq, int Hkv, int total, int D,
+size_t fa_bwd_varlen_workspace_size(int B, int Hq, int Hkv, int total, int max_seqlen, int D,
                                     int deterministic) {
   if (B < 1 || total < 0) return 0;
+  if (max_seqlen < 1 || max_seqlen > fa::varlen_max_seqlen_limit() / 2) return 0;
   if (check_shape(1, Hq, Hkv, total > 0 ? total : 1, D, 1.0f) != FA_OK) return 0;
-  if (deterministic != 0 && deterministic != 2) return 0;
-  return fa::bwd_varlen_workspace_bytes(B, Hq, total, D, deterministic);
+  if (check_varlen_mode(B, total, max_seqlen, deterministic) != FA_OK) return 0;
+  return fa::bwd_varlen_workspace_bytes(B, Hq, total, D, deterministic, max_seqlen);
 }
 
 int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -182,13 +193,13 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, co
     return FA_ERR_INVALID;
   int rc = check_shape(1, Hq, Hkv, total > 0 ? total : 1, D, scale);
   if (rc != FA_OK) return rc;
-  if (deterministic == 1) return FA_ERR_UNSUPPORTED;
-  if (deterministic != 0 && deterministic != 2) return FA_ERR_INVALID;
+  rc = check_varlen_mode(B, total, max_seqlen, deterministic);
+  if (rc != FA_OK) return rc;
   const void* all[11] = {q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens, workspace};
   for (int i = 0; i < 10; ++i)
     if (!aligned16(all[i])) return FA_ERR_ALIGN;
   if (((uintptr_t)workspace & 255u) != 0) return FA_ERR_ALIGN;
-  const size_t wbytes = fa::bwd_varlen_workspace_bytes(B, Hq, total, D, deterministic);
+  const size_t wbytes = fa::bwd_varlen_workspace_bytes(B, Hq, total, D, deterministic, max_seqlen);
   if (workspace_bytes < wbytes) return FA_ERR_WORKSPACE;
   const size_t qb = (size_t)Hq * total * D * 2, kb = (size_t)Hkv * total * D * 2;
   const size_t lb = (size_t)Hq * total * 4, cb = (size_t)(B + 1) * 4;

@@ -151,10 +151,21 @@ hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t stream);
 // fixed-order pass that recomputes S, dP and dS.
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 
-// Variable-length backward, dQ modes 0 (atomic) and 2 (recompute): a holds
-// the packed tensors as B = 1, N = total; v the sequences.  Workspace layout:
-// the dense layout for (1, Hq, total), then two work lists.
-size_t bwd_varlen_workspace_bytes(int B, int Hq, int total, int D, int deterministic);
+// Variable-length backward, dQ modes 0 (atomic), 1 (stored dS) and 2
+// (recompute): a holds the packed tensors as B = 1, N = total; v the
+// sequences.  Workspace layout: the dense layout for (1, Hq, total) (mode 1:
+// that of mode 2), then (mode 1) Hq regions of ds_head bytes of dS blocks,
+// the two work lists and (mode 1) the B + 1 block offsets.
+struct VarlenBwdLayout {
+  size_t ds, ds_head;   // stored-dS regions (mode 1): offset, bytes per head
+  int cap_blocks;       // 32 x 32 blocks per head region
+  size_t main_list, dq_list, blk_off, total;
+};
+// Bytes of one head's stored-dS region for packed sequences no longer than
+// max_seqlen.
+size_t varlen_ds_head_bytes(int B, int total, int max_seqlen);
+VarlenBwdLayout bwd_varlen_layout(int B, int Hq, int total, int D, int deterministic, int max_seqlen);
+size_t bwd_varlen_workspace_bytes(int B, int Hq, int total, int D, int deterministic, int max_seqlen);
 hipError_t launch_bwd_varlen(const BwdArgs& a, const VarlenArgs& v, hipStream_t stream);
 
 }  // namespace fa

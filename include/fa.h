@@ -225,16 +225,22 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
  *   q, o, dout, dq [Hq][total][D], k, v, dk, dv [Hkv][total][D], lse
  *   [Hq][total]; cu_seqlens, B, total, max_seqlen as for fa_fwd_varlen, with
  *   max_seqlen <= fa_varlen_max_seqlen() / 2.
- *   deterministic: 0 (atomic dQ) or 2 (fixed-order dQ recomputing dS); the
- *     stored-dS mode 1 is not available for variable length
- *     (FA_ERR_UNSUPPORTED).
- *   workspace: fa_bwd_varlen_workspace_size() bytes, 256-byte aligned.
+ *   deterministic: 0, 1 or 2 as for fa_bwd.  Mode 1 keeps, per query head,
+ *     each sequence's grid of 32 x 32 dS blocks in the workspace, packed one
+ *     sequence after another; its size is bounded with max_seqlen, so in
+ *     mode 1 every sequence must be at most max_seqlen long for a correct dQ
+ *     (a longer one stays memory-safe: blocks beyond the region are neither
+ *     written nor read, and that dQ is unspecified).  Mode 1 returns
+ *     FA_ERR_TOO_LARGE when one head's region would exceed 4 GiB
+ *     ((ceil(total/32) + B) * ceil(max_seqlen/32) blocks of 2 KiB).
+ *   workspace: fa_bwd_varlen_workspace_size(B, Hq, Hkv, total, max_seqlen, D,
+ *     deterministic) bytes, 256-byte aligned (0 for an invalid argument).
  * Work lists are built on the device as for the forward: the dK/dV pass takes
  * (sequence, 128-key block) items by decreasing number of query steps, the
  * dQ pass (sequence, 128-query tile) items by decreasing number of key tiles.
  * total = 0 is valid and writes nothing.
  */
-size_t fa_bwd_varlen_workspace_size(int B, int Hq, int Hkv, int total, int D,
+size_t fa_bwd_varlen_workspace_size(int B, int Hq, int Hkv, int total, int max_seqlen, int D,
                                     int deterministic);
 int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
                   const void* dout, void* dq, void* dk, void* dv, const int* cu_seqlens,

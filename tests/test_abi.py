@@ -259,7 +259,8 @@ def bwdv(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dout=None), fa.FA_ERR_INVALID), (dict(cu=None), fa.FA_ERR_INVALID),
-    (dict(det=1), fa.FA_ERR_UNSUPPORTED), (dict(det=3), fa.FA_ERR_INVALID),
+    (dict(det=-1), fa.FA_ERR_INVALID), (dict(det=3), fa.FA_ERR_INVALID),
+    (dict(det=1, total=1 << 22, max_seqlen=32768), fa.FA_ERR_TOO_LARGE),
     (dict(B=0), fa.FA_ERR_INVALID), (dict(max_seqlen=1 << 30), fa.FA_ERR_INVALID),
     (dict(D=32), fa.FA_ERR_UNSUPPORTED), (dict(dq=DQ + 4), fa.FA_ERR_ALIGN),
     (dict(wsb=64), fa.FA_ERR_WORKSPACE), (dict(dk=DQ), fa.FA_ERR_INVALID),
@@ -272,10 +273,18 @@ def test_bwd_varlen_rejects(kw, code):
 def test_bwd_varlen_sizes_and_empty_batch():
     assert bwdv(total=0, max_seqlen=1) == fa.FA_OK
     assert bwdv(total=0, max_seqlen=1, det=0) == fa.FA_OK
-    assert fa.fa_bwd_varlen_workspace_size(3, 2, 1, 500, 128, 1) == 0
-    s0 = fa.fa_bwd_varlen_workspace_size(3, 2, 1, 500, 128, 0)
-    s2 = fa.fa_bwd_varlen_workspace_size(3, 2, 1, 500, 128, 2)
+    assert bwdv(total=0, max_seqlen=1, det=1) == fa.FA_OK
+    assert fa.fa_bwd_varlen_workspace_size(3, 2, 1, 500, 300, 128, 3) == 0
+    assert fa.fa_bwd_varlen_workspace_size(3, 2, 1, 500, 0, 128, 2) == 0
+    s0 = fa.fa_bwd_varlen_workspace_size(3, 2, 1, 500, 300, 128, 0)
+    s1 = fa.fa_bwd_varlen_workspace_size(3, 2, 1, 500, 300, 128, 1)
+    s2 = fa.fa_bwd_varlen_workspace_size(3, 2, 1, 500, 300, 128, 2)
     assert s0 >= 2 * 500 * 128 * 4 and s2 < s0
+    # Mode 1 adds, per query head, (ceil(total/32) + B) * ceil(max_seqlen/32)
+    # dS blocks of 32 x 32 bf16.
+    assert s1 >= s2 + 2 * (16 + 3) * 10 * 2048
+    assert fa.fa_bwd_varlen_workspace_size(3, 2, 1, 1 << 22, 32768, 128, 1) == 0
+    assert fa.fa_bwd_varlen_workspace_size(3, 2, 1, 1 << 22, 32768, 128, 2) > 0
 
 
 def test_exp2_poly_eval_argument_checks():

@@ -1,6 +1,6 @@
 """Variable-length backward (packed sequences, device-side work lists) against
-the fp64 oracle applied to each sequence on its own, in dQ modes 0 (atomic)
-and 2 (fixed order, recomputing dS)."""
+the fp64 oracle applied to each sequence on its own, in dQ modes 0 (atomic),
+1 (fixed order from stored dS blocks) and 2 (fixed order, recomputing dS)."""
 import hashlib
 import math
 
@@ -36,7 +36,7 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("mode", [0, 2])
+@pytest.mark.parametrize("mode", [0, 1, 2])
 @pytest.mark.parametrize("lens,Hq,Hkv,D,causal", CASES)
 def test_varlen_bwd_matches_per_sequence_oracle(lens, Hq, Hkv, D, causal, mode):
     say(f"varlen bwd lens={lens} Hq{Hq} Hkv{Hkv} D{D} causal={causal} mode={mode}")
@@ -52,23 +52,24 @@ def test_varlen_bwd_matches_per_sequence_oracle(lens, Hq, Hkv, D, causal, mode):
         check_grad(dv[None, :, sl], rv, f"seq {b} dV")
 
 
+@pytest.mark.parametrize("mode", [1, 2])
 @pytest.mark.parametrize("D", [64, 128])
-def test_varlen_bwd_fixed_order_is_deterministic_and_equals_dense(D):
+def test_varlen_bwd_fixed_order_is_deterministic_and_equals_dense(D, mode):
     dev = require_gpu()
     B, H, N = 3, 4, 384
-    say(f"varlen bwd mode 2 vs dense mode 2, B{B} H{H} N{N} D{D} causal, x5 reruns")
+    say(f"varlen bwd mode {mode} vs dense mode {mode}, B{B} H{H} N{N} D{D} causal, x5 reruns")
     q, k, v, do = synth.generate(B, H, H, N, D, seed=4, with_dout=True)
     scale = 1.0 / math.sqrt(D)
     qd, kd, vd, dod = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
     o, lse = fa.forward(qd, kd, vd, True, scale)
-    dense = fa.backward(qd, kd, vd, o, lse, dod, True, scale, deterministic=2)
+    dense = fa.backward(qd, kd, vd, o, lse, dod, True, scale, deterministic=mode)
     pack = lambda t: t.permute(1, 0, 2, 3).reshape(t.shape[1], B * N, D).contiguous()
     cu = torch.arange(0, (B + 1) * N, N, dtype=torch.int32, device=dev)
     lse_p = lse.permute(1, 0, 2).reshape(H, B * N).contiguous()
     digests = set()
     for _ in range(5):
         got = fa.backward_varlen(pack(qd), pack(kd), pack(vd), pack(o), lse_p, pack(dod), cu, N,
-                                 True, scale, deterministic=2)
+                                 True, scale, deterministic=mode)
         h = hashlib.sha256()
         for t in got:
             h.update(t.cpu().view(torch.int16).numpy().tobytes())
@@ -77,3 +78,42 @@ def test_varlen_bwd_fixed_order_is_deterministic_and_equals_dense(D):
     assert len(digests) == 1
     for a, b in zip(dense, got):
         assert torch.equal(pack(a).cpu(), b.cpu())
+
+
+@pytest.mark.parametrize("lens,max_seqlen", [([640, 17, 0, 300], 640), ([640, 17, 0, 300], 64)])
+def test_varlen_bwd_stored_ds_region_bounds(lens, max_seqlen):
+    # Mode 1 sizes each head's dS region from max_seqlen.  The call must stay
+    # inside the workspace it asked for (a guard tail after the requested
+    # bytes comes back unchanged), and dK, dV, which the fixed-order modes
+    # form in the same main kernel in the same order, equal mode 2's bit for
+    # bit.  With the true bound dQ matches the oracle; with a bound far below
+    # the longest sequence (640 > 64) the region is too small and dQ is
+    # unspecified.
+    dev = require_gpu()
+    Hq, Hkv, D = 4, 2, 128
+    say(f"varlen bwd mode 1 region bounds lens={lens} max_seqlen={max_seqlen}")
+    q, k, v, do, cu = synth.generate_varlen(lens, Hq, Hkv, D, seed=11, with_dout=True)
+    qd, kd, vd, dod, cud = q.to(dev), k.to(dev), v.to(dev), do.to(dev), cu.to(dev)
+    scale = 1.0 / math.sqrt(D)
+    total = sum(lens)
+    o, lse = fa.forward_varlen(qd, kd, vd, cud, max(lens), True, scale)
+    ref = fa.backward_varlen(qd, kd, vd, o, lse, dod, cud, max(lens), True, scale, deterministic=2)
+    ws_bytes = fa.fa_bwd_varlen_workspace_size(len(lens), Hq, Hkv, total, max_seqlen, D, 1)
+    assert ws_bytes > 0
+    guard = 4096
+    buf = torch.full((ws_bytes + guard,), 0x5A, dtype=torch.uint8, device=dev)
+    dq, dk, dv = fa.backward_varlen(qd, kd, vd, o, lse, dod, cud, max_seqlen, True, scale,
+                                    deterministic=1, workspace=buf[:ws_bytes])
+    torch.cuda.synchronize()
+    assert bool((buf[ws_bytes:] == 0x5A).all()), "dS blocks written past the workspace"
+    assert torch.equal(ref[1].cpu(), dk.cpu()) and torch.equal(ref[2].cpu(), dv.cpu())
+    if max_seqlen < max(lens):
+        return
+    dq = dq.cpu()
+    for b, n in enumerate(lens):
+        if n == 0:
+            continue
+        sl = slice(int(cu[b]), int(cu[b]) + n)
+        rq, _, _ = oracle.attention_bwd(q[None, :, sl], k[None, :, sl], v[None, :, sl],
+                                        do[None, :, sl], True, scale)
+        check_grad(dq[None, :, sl], rq, f"seq {b} (len {n}) dQ")

@@ -90,7 +90,7 @@ def test_varlen_workload_sampled_rows():
     check_lse(torch.cat(got_l), torch.cat(ref_l), "sampled LSE")
 
 
-@pytest.mark.parametrize("direction", ["fwd", "bwd0", "bwd2"])
+@pytest.mark.parametrize("direction", ["fwd", "bwd0", "bwd1", "bwd2"])
 def test_overlapping_sequences_stay_inside_the_workspace(direction):
     # cu_seqlens = [0, T, 0, T]: sequences 0 and 2 both cover rows 0..T-1
     # (clamping keeps each inside the tensors but not apart), which lists 20
@@ -113,7 +113,7 @@ def test_overlapping_sequences_stay_inside_the_workspace(direction):
     if direction == "fwd":
         ws_bytes = fa.fa_fwd_varlen_workspace_size(3, T)
     else:
-        ws_bytes = fa.fa_bwd_varlen_workspace_size(3, Hq, Hkv, T, D, int(direction[-1]))
+        ws_bytes = fa.fa_bwd_varlen_workspace_size(3, Hq, Hkv, T, T, D, int(direction[-1]))
     assert ws_bytes > 0
     buf = torch.full((ws_bytes + guard,), 0xA5, dtype=torch.uint8, device=dev)
     ws = buf[:ws_bytes]
