@@ -993,6 +993,14 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
     }
   } else {
     // ======================= gradient waves =======================
+    // Gradient wave g takes d-block db = g % ND of the keys of score waves
+    // kbw0 .. kbw0 + ND - 1 (kbw0 = (g / ND) ND): all 128 keys at D = 128,
+    // one half of them at D = 64.  Each transposing read of dO^T or Q^T then
+    // feeds ND products (one per key block) instead of one; the A operands
+    // P^T and dS^T are plain 16-byte reads of the score waves' slots.
+    // Accumulator j covers keys kw_j = k0 + 32 (kbw0 + j), d = 32 db + n.
+    const int gdb = kwave % ND;
+    const int kbw0 = (kwave / ND) * ND;
     f32x16 dk_acc[ND], dv_acc[ND];
 #pragma unroll
     for (int i = 0; i < ND; ++i)
@@ -1005,15 +1013,12 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
     // of column d = 32 db + n): lane j of 16-lane group gq points at row
     // 8 rd + 4 h + j/4 and d = 32 db + 16 (gq & 1) + 4 (j & 3).
     const int tj = lane & 15, gq = lane >> 4;
-    uint32_t tr_off[ND][2];
+    uint32_t tr_off[2];
 #pragma unroll
     for (int rd = 0; rd < 2; ++rd) {
       const int row = 8 * rd + 4 * h + (tj >> 2);
-#pragma unroll
-      for (int db = 0; db < ND; ++db) {
-        const int c = 4 * db + 2 * (gq & 1) + ((tj & 3) >> 1);
-        tr_off[db][rd] = (uint32_t)(row * RB + ((c ^ tile_swz<D>(row)) * 16) + (tj & 1) * 8);
-      }
+      const int c = 4 * gdb + 2 * (gq & 1) + ((tj & 3) >> 1);
+      tr_off[rd] = (uint32_t)(row * RB + ((c ^ tile_swz<D>(row)) * 16) + (tj & 1) * 8);
     }
     // Iteration i: dV, dK of step i-1 (tile `prv`, P and dS in `pbr`).
     auto body = [&](int i, const char* prv, const char* pbr, char* ld) __attribute__((always_inline)) {
@@ -1021,26 +1026,24 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
       lds_barrier();
       if (i + 4 < nsteps) issue_next(ld);
       if (i == 0 || i > nsteps) return;
-      const char* pr = pbr + kwave * 4096 + lane * 16;
-      bf16x8 pa[2], dsa[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        pa[u] = as_bf16x8(*(const u32x4*)(pr + u * 1024));
-        dsa[u] = as_bf16x8(*(const u32x4*)(pr + (2 + u) * 1024));
-      }
-      constexpr int NB = 2 * ND;  // MFMA pairs: (u, db), db fastest
+      const char* pr = pbr + kbw0 * 4096 + lane * 16;
+      constexpr int NB = 2 * ND;  // MFMA pairs: (u, key block j), j fastest
       constexpr int PD = 2;
-      bf16x8 opA[NB], opB[NB];
+      bf16x8 pa[NB], dsa[NB], ob[2], qb[2];
       auto fetch = [&](int jb) {
         if (jb < NB) {
-          const int u = jb / ND, db = jb % ND;
-          const int roff = 16 * u * RB;
-          const u32x2 olo = lds_read_tr16((const lds_void*)(prv + TB + roff + tr_off[db][0]));
-          const u32x2 ohi = lds_read_tr16((const lds_void*)(prv + TB + roff + tr_off[db][1]));
-          const u32x2 qlo = lds_read_tr16((const lds_void*)(prv + roff + tr_off[db][0]));
-          const u32x2 qhi = lds_read_tr16((const lds_void*)(prv + roff + tr_off[db][1]));
-          opA[jb] = as_bf16x8(u32x4{olo[0], olo[1], ohi[0], ohi[1]});
-          opB[jb] = as_bf16x8(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]});
+          const int u = jb / ND, j = jb % ND;
+          if (j == 0) {
+            const int roff = 16 * u * RB;
+            const u32x2 olo = lds_read_tr16((const lds_void*)(prv + TB + roff + tr_off[0]));
+            const u32x2 ohi = lds_read_tr16((const lds_void*)(prv + TB + roff + tr_off[1]));
+            const u32x2 qlo = lds_read_tr16((const lds_void*)(prv + roff + tr_off[0]));
+            const u32x2 qhi = lds_read_tr16((const lds_void*)(prv + roff + tr_off[1]));
+            ob[u] = as_bf16x8(u32x4{olo[0], olo[1], ohi[0], ohi[1]});
+            qb[u] = as_bf16x8(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]});
+          }
+          pa[jb] = as_bf16x8(*(const u32x4*)(pr + j * 4096 + u * 1024));
+          dsa[jb] = as_bf16x8(*(const u32x4*)(pr + j * 4096 + (2 + u) * 1024));
         }
       };
 #pragma unroll
@@ -1048,10 +1051,10 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int jb = 0; jb < NB; ++jb) {
-        const int u = jb / ND, db = jb % ND;
+        const int u = jb / ND, j = jb % ND;
         fetch(jb + PD);
-        dv_acc[db] = mfma32(pa[u], opA[jb], dv_acc[db]);
-        dk_acc[db] = mfma32(dsa[u], opB[jb], dk_acc[db]);
+        dv_acc[j] = mfma32(pa[jb], ob[u], dv_acc[j]);
+        dk_acc[j] = mfma32(dsa[jb], qb[u], dk_acc[j]);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
@@ -1065,37 +1068,37 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
       body(i + 4, st3, pb1, st2);
       body(i + 5, st4, pb0, st3);
     }
-    // dK (scaled) and dV of this wave's 32 keys.  Register r of d-block db:
-    // key kw + 8(r/4) + 4h + r%4, d = 32 db + n.  With the query heads cut
-    // into parts, each part writes fp32 partials that bwd_kv_reduce_kernel
-    // sums in part order.
+    // dK (scaled) and dV: register r of accumulator j holds key
+    // k0 + 32 (kbw0 + j) + 8(r/4) + 4h + r%4, d = 32 gdb + n.  With the query
+    // heads cut into parts, each part writes fp32 partials that
+    // bwd_kv_reduce_kernel sums in part order.
     if (!VARLEN && p.hsplit > 1) {
       const size_t plane = (size_t)BHkv * N * D;
       float* pk = p.kv_part + (size_t)hs * 2 * plane + (size_t)bhk * N * D;
       float* pv = pk + plane;
 #pragma unroll
-      for (int db = 0; db < ND; ++db)
+      for (int j = 0; j < ND; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int krow = kw + 8 * (r >> 2) + 4 * h + (r & 3);
+          const int krow = k0 + 32 * (kbw0 + j) + 8 * (r >> 2) + 4 * h + (r & 3);
           if (krow < N) {
-            const size_t off = (size_t)krow * D + 32 * db + n;
-            pk[off] = dk_acc[db][r] * p.scale;
-            pv[off] = dv_acc[db][r];
+            const size_t off = (size_t)krow * D + 32 * gdb + n;
+            pk[off] = dk_acc[j][r] * p.scale;
+            pv[off] = dv_acc[j][r];
           }
         }
     } else {
       uint16_t* dKh = dK + kv_head;
       uint16_t* dVh = dV + kv_head;
 #pragma unroll
-      for (int db = 0; db < ND; ++db)
+      for (int j = 0; j < ND; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int krow = kw + 8 * (r >> 2) + 4 * h + (r & 3);
+          const int krow = k0 + 32 * (kbw0 + j) + 8 * (r >> 2) + 4 * h + (r & 3);
           if (krow < N) {
-            const size_t off = (size_t)krow * D + 32 * db + n;
-            dKh[off] = (uint16_t)(pack_bf16x2(dk_acc[db][r] * p.scale, 0.f) & 0xffffu);
-            dVh[off] = (uint16_t)(pack_bf16x2(dv_acc[db][r], 0.f) & 0xffffu);
+            const size_t off = (size_t)krow * D + 32 * gdb + n;
+            dKh[off] = (uint16_t)(pack_bf16x2(dk_acc[j][r] * p.scale, 0.f) & 0xffffu);
+            dVh[off] = (uint16_t)(pack_bf16x2(dv_acc[j][r], 0.f) & 0xffffu);
           }
         }
     }
