@@ -135,13 +135,15 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
 
 namespace {
 
-// dQ mode of the variable-length backward: 0, 1 or 2; in mode 1 one head's
+// dQ mode of the variable-length backward: 0, 1 or 2.  In mode 1 one head's
 // region of dS blocks (bounded by total, B and max_seqlen) is addressed with
-// 32-bit offsets, as in the dense stored-dS mode.
-int check_varlen_mode(int B, int total, int max_seqlen, int deterministic) {
+// 32-bit offsets, as in the dense stored-dS mode; in mode 0 one head's fp32
+// accumulator rows (all total of them) with 32-bit signed offsets.
+int check_varlen_mode(int B, int total, int max_seqlen, int D, int deterministic) {
   if (deterministic < 0 || deterministic > 2) return FA_ERR_INVALID;
   if (deterministic == 1 && fa::varlen_ds_head_bytes(B, total, max_seqlen) > 0xFFFFF000ull - 4096)
     return FA_ERR_TOO_LARGE;
+  if (deterministic == 0) return check_mode(total, D, 0);
   return FA_OK;
 }
 
@@ -178,7 +180,7 @@ size_t fa_bwd_varlen_workspace_size(int B, int Hq, int Hkv, int total, int max_s
   if (B < 1 || total < 0) return 0;
   if (max_seqlen < 1 || max_seqlen > fa::varlen_max_seqlen_limit() / 2) return 0;
   if (check_shape(1, Hq, Hkv, total > 0 ? total : 1, D, 1.0f) != FA_OK) return 0;
-  if (check_varlen_mode(B, total, max_seqlen, deterministic) != FA_OK) return 0;
+  if (check_varlen_mode(B, total, max_seqlen, D, deterministic) != FA_OK) return 0;
   return fa::bwd_varlen_workspace_bytes(B, Hq, total, D, deterministic, max_seqlen);
 }
 
@@ -193,7 +195,7 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, co
     return FA_ERR_INVALID;
   int rc = check_shape(1, Hq, Hkv, total > 0 ? total : 1, D, scale);
   if (rc != FA_OK) return rc;
-  rc = check_varlen_mode(B, total, max_seqlen, deterministic);
+  rc = check_varlen_mode(B, total, max_seqlen, D, deterministic);
   if (rc != FA_OK) return rc;
   const void* all[11] = {q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens, workspace};
   for (int i = 0; i < 10; ++i)

@@ -232,7 +232,8 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
  *     (a longer one stays memory-safe: blocks beyond the region are neither
  *     written nor read, and that dQ is unspecified).  Mode 1 returns
  *     FA_ERR_TOO_LARGE when one head's region would exceed 4 GiB
- *     ((ceil(total/32) + B) * ceil(max_seqlen/32) blocks of 2 KiB).
+ *     ((ceil(total/32) + B) * ceil(max_seqlen/32) blocks of 2 KiB); mode 0
+ *     when one head's fp32 accumulator, total * D * 4 bytes, reaches 2 GiB.
  *   workspace: fa_bwd_varlen_workspace_size(B, Hq, Hkv, total, max_seqlen, D,
  *     deterministic) bytes, 256-byte aligned (0 for an invalid argument).
  * Work lists are built on the device as for the forward: the dK/dV pass takes

@@ -261,6 +261,9 @@ def bwdv(**kw):
     (dict(dout=None), fa.FA_ERR_INVALID), (dict(cu=None), fa.FA_ERR_INVALID),
     (dict(det=-1), fa.FA_ERR_INVALID), (dict(det=3), fa.FA_ERR_INVALID),
     (dict(det=1, total=1 << 22, max_seqlen=32768), fa.FA_ERR_TOO_LARGE),
+    # Mode 0: one head's fp32 dQ accumulator, total * D * 4 bytes, must stay
+    # below 2^31 (32-bit signed offsets).
+    (dict(det=0, total=1 << 22, max_seqlen=32768), fa.FA_ERR_TOO_LARGE),
     (dict(B=0), fa.FA_ERR_INVALID), (dict(max_seqlen=1 << 30), fa.FA_ERR_INVALID),
     (dict(D=32), fa.FA_ERR_UNSUPPORTED), (dict(dq=DQ + 4), fa.FA_ERR_ALIGN),
     (dict(wsb=64), fa.FA_ERR_WORKSPACE), (dict(dk=DQ), fa.FA_ERR_INVALID),
@@ -285,6 +288,8 @@ def test_bwd_varlen_sizes_and_empty_batch():
     assert s1 >= s2 + 2 * (16 + 3) * 10 * 2048
     assert fa.fa_bwd_varlen_workspace_size(3, 2, 1, 1 << 22, 32768, 128, 1) == 0
     assert fa.fa_bwd_varlen_workspace_size(3, 2, 1, 1 << 22, 32768, 128, 2) > 0
+    assert fa.fa_bwd_varlen_workspace_size(3, 2, 1, 1 << 22, 32768, 128, 0) == 0
+    assert fa.fa_bwd_varlen_workspace_size(3, 2, 1, (1 << 22) - 1, 32768, 128, 0) > 0
 
 
 def test_exp2_poly_eval_argument_checks():
