@@ -888,13 +888,18 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
     // complete), so the first products of an iteration start right after it.
     constexpr int PD = 2;  // operand read distance, in MFMA pairs
     bf16x8 opA[T], opB[T];
-    f32x4 lc[4], dc[4];
+    // Row constants of register r (query 8(r/4) + 4h + r%4 of the step):
+    // LSE log2 e as lc[r/4][r%4]; Delta held once per 16-lane row, lane j of
+    // the row holding register j's value, and broadcast by DPP where it is
+    // used (one LDS read instead of four).
+    f32x4 lc[4];
+    float dcl;
+    const int dc_pos = 8 * ((lane & 15) >> 2) + 4 * h + (lane & 3);
     auto prefetch = [&](const char* rows, const char* ops) __attribute__((always_inline)) {
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
+      for (int r4 = 0; r4 < 4; ++r4)
         lc[r4] = *(const f32x4*)((const float*)(rows + 2 * TB) + 8 * r4 + 4 * h);
-        dc[r4] = *(const f32x4*)((const float*)(rows + 2 * TB + 256) + 8 * r4 + 4 * h);
-      }
+      dcl = *((const float*)(rows + 2 * TB + 256) + dc_pos);
 #pragma unroll
       for (int c = 0; c < PD; ++c) {
         opA[c] = as_bf16x8(*(const u32x4*)(ops + a_off[c]));
@@ -952,7 +957,7 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
         for (int r = EPJ * j; r < EPJ * (j + 1); ++r) {
           const float pv = exp2_hw(__builtin_fmaf(sv[r], p.c, -lc[r >> 2][r & 3]));
           sv[r] = pv;
-          dv[r] = pv * (dv[r] - dc[r >> 2][r & 3]);
+          dv[r] = pv * (dv[r] - row_bcast(dcl, r));
           if ((r & 7) == 7) {
             const int u = r >> 3;
             u32x4 w1, w2;

@@ -51,6 +51,38 @@ __device__ __forceinline__ float xhalf_max(float v) { return __builtin_fmaxf(v, 
 __device__ __forceinline__ float xhalf_sum(float v) { return v + __shfl_xor(v, 32, 64); }
 __device__ __forceinline__ float xhalf(float v) { return __shfl_xor(v, 32, 64); }
 
+// Value of lane R of the caller's 16-lane row, in every lane of that row
+// (DPP row_newbcast, CDNA3 and later).  Used as the first operand of a VOP2
+// instruction the compiler folds the broadcast into it (v_sub_f32_dpp and
+// the like), so it costs no instruction of its own there.  R must be a
+// constant; row_bcast() maps an index known after unrolling onto it.
+template <int R>
+__device__ __forceinline__ float row_bcast_c(float v) {
+  static_assert(R >= 0 && R < 16, "lane of a 16-lane row");
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + R, 0xf,
+                                                               0xf, false));
+}
+__device__ __forceinline__ float row_bcast(float v, int r) {
+  switch (r) {
+    case 0: return row_bcast_c<0>(v);
+    case 1: return row_bcast_c<1>(v);
+    case 2: return row_bcast_c<2>(v);
+    case 3: return row_bcast_c<3>(v);
+    case 4: return row_bcast_c<4>(v);
+    case 5: return row_bcast_c<5>(v);
+    case 6: return row_bcast_c<6>(v);
+    case 7: return row_bcast_c<7>(v);
+    case 8: return row_bcast_c<8>(v);
+    case 9: return row_bcast_c<9>(v);
+    case 10: return row_bcast_c<10>(v);
+    case 11: return row_bcast_c<11>(v);
+    case 12: return row_bcast_c<12>(v);
+    case 13: return row_bcast_c<13>(v);
+    case 14: return row_bcast_c<14>(v);
+    default: return row_bcast_c<15>(v);
+  }
+}
+
 // Index of the calling wave in its workgroup, as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
