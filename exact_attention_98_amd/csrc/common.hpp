@@ -60,7 +60,7 @@ template <int R>
 __device__ __forceinline__ float row_bcast_c(float v) {
   static_assert(R >= 0 && R < 16, "lane of a 16-lane row");
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + R, 0xf,
-                                                               0xf, false));
+                                                               0xf, true));
 }
 __device__ __forceinline__ float row_bcast(float v, int r) {
   switch (r) {
