@@ -859,8 +859,10 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
       if constexpr (STORE_DS) {
         const size_t hidx = (VARLEN ? 0 : (size_t)b * p.Hq) + hq0 + cur_g;
         const rsrc_t r = make_rsrc_uniform(p.ds + hidx * p.ds_head + ds_seq, ds_range);
-        const bool ok = cur_qs < nb32s && kb32 < nb32s && (!CAUSAL || kb32 <= cur_qs);
-        const uint32_t off = ok ? (uint32_t)(cur_qs * nb32s + kb32) * 2048u : 0xFFFFF000u;
+        const uint64_t boff = ((uint64_t)cur_qs * (uint64_t)nb32s + (uint64_t)kb32) * 2048u;
+        const bool ok = cur_qs < nb32s && kb32 < nb32s && (!CAUSAL || kb32 <= cur_qs) &&
+                        boff + 2048u <= (uint64_t)ds_range;
+        const uint32_t off = ok ? (uint32_t)boff : 0xFFFFF000u;
         // Non-temporal (NT): dS is read once, by the dQ pass, so the caches
         // keep K, V and the step tiles instead, and the dQ pass does not first
         // write back lines left dirty here.
@@ -1409,10 +1411,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_kernel(const uint16_t* __res
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int kb32 = 2 * kt + j;
-      const uint32_t blk = (uint32_t)(qb32 * nb32 + kb32);
+      // Byte offset in 64 bits: with packed sequences a sequence longer than
+      // max_seqlen can index past 2^32 bytes, and only blocks inside the
+      // sequence's range are read.
+      const uint64_t boff = ((uint64_t)qb32 * (uint64_t)nb32 + (uint64_t)kb32) * 2048u;
       const bool ok = qb32 < nb32 && kb32 < nb32 && (!CAUSAL || kb32 <= qb32) &&
-                      (blk + 1) * 2048u <= ds_range;
-      const uint32_t off = ok ? blk * 2048u : 0u;
+                      boff + 2048u <= (uint64_t)ds_range;
+      const uint32_t off = ok ? (uint32_t)boff : 0u;
       const rsrc_t dr = make_rsrc_uniform(dsh + off, ok ? 2048u : 0u);
 #pragma unroll
       for (int s = 0; s < 2; ++s)

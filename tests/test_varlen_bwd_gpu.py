@@ -151,3 +151,31 @@ def test_varlen_bwd_many_short_sequences_all_modes():
             check_grad(dq[None, :, sl], rq, f"mode {m} seq {b} (len {n}) dQ")
             check_grad(dk[None, :, sl], rk, f"mode {m} seq {b} dK")
             check_grad(dv[None, :, sl], rv, f"mode {m} seq {b} dV")
+
+
+def test_varlen_bwd_stored_ds_sequence_far_beyond_max_seqlen():
+    # One 50000-token sequence with max_seqlen = 64 in mode 1: the dS region is
+    # sized for 64-token sequences, and the sequence's block indices reach
+    # past 2^32 bytes (ceil(50000/32)^2 blocks of 2 KiB).  Block offsets are
+    # formed in 64 bits, so every block outside the region is neither written
+    # nor read: the call completes, the guard tail after the workspace comes
+    # back unchanged, and dK, dV (which do not use the stored blocks) equal
+    # mode 2's.  dQ is unspecified here.
+    dev = require_gpu()
+    lens, Hq, Hkv, D = [50000], 1, 1, 64
+    say(f"varlen bwd mode 1, one sequence of {lens[0]} tokens, max_seqlen 64")
+    q, k, v, do, cu = synth.generate_varlen(lens, Hq, Hkv, D, seed=21, with_dout=True)
+    qd, kd, vd, dod, cud = q.to(dev), k.to(dev), v.to(dev), do.to(dev), cu.to(dev)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = fa.forward_varlen(qd, kd, vd, cud, lens[0], True, scale)
+    ref = fa.backward_varlen(qd, kd, vd, o, lse, dod, cud, lens[0], True, scale, deterministic=2)
+    ws_bytes = fa.fa_bwd_varlen_workspace_size(1, Hq, Hkv, lens[0], 64, D, 1)
+    assert ws_bytes > 0
+    guard = 4096
+    buf = torch.full((ws_bytes + guard,), 0x3C, dtype=torch.uint8, device=dev)
+    dq, dk, dv = fa.backward_varlen(qd, kd, vd, o, lse, dod, cud, 64, True, scale, deterministic=1,
+                                    workspace=buf[:ws_bytes])
+    torch.cuda.synchronize()
+    assert bool((buf[ws_bytes:] == 0x3C).all()), "written past the workspace"
+    assert torch.equal(ref[1].cpu(), dk.cpu()) and torch.equal(ref[2].cpu(), dv.cpu())
+    assert bool(torch.isfinite(dq.float()).all())
