@@ -49,7 +49,6 @@ __device__ __forceinline__ float bf16_bits_to_float(uint32_t b16) {
 // second result (r[0] + r[1] compiles to r[0] + r[0]).
 __device__ __forceinline__ float xhalf_max(float v) { return __builtin_fmaxf(v, __shfl_xor(v, 32, 64)); }
 __device__ __forceinline__ float xhalf_sum(float v) { return v + __shfl_xor(v, 32, 64); }
-__device__ __forceinline__ float xhalf(float v) { return __shfl_xor(v, 32, 64); }
 
 // Value of lane R of the caller's 16-lane row, in every lane of that row
 // (DPP row_newbcast, CDNA3 and later).  Used as the first operand of a VOP2
@@ -119,9 +118,6 @@ __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t voff) {
 }
 __device__ __forceinline__ void buf_store8(rsrc_t r, uint32_t voff, u32x2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, voff, 0, 0);
-}
-__device__ __forceinline__ void buf_store4(rsrc_t r, uint32_t voff, float v) {
-  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, 0, 0);
 }
 // 16 bytes per lane from global memory straight into LDS
 // (buffer_load_dwordx4 ... lds): lane l's bytes land at lds + 16 l, where lds
