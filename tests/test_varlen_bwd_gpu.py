@@ -179,3 +179,42 @@ def test_varlen_bwd_stored_ds_sequence_far_beyond_max_seqlen():
     assert bool((buf[ws_bytes:] == 0x3C).all()), "written past the workspace"
     assert torch.equal(ref[1].cpu(), dk.cpu()) and torch.equal(ref[2].cpu(), dv.cpu())
     assert bool(torch.isfinite(dq.float()).all())
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_varlen_bwd_workload_sampled(mode):
+    # The benchmark's length mix (64 sequences, 65536 tokens, 16 heads, D=128,
+    # causal) in the launch configuration the benchmark times: dQ rows (first,
+    # middle, last of heads 0 and 15) of every sequence one by one, and the
+    # full dQ, dK, dV of heads 0 and 15 for the shortest and the longest
+    # sequence, against the oracle.
+    dev = require_gpu()
+    w = synth.VARLEN
+    lens = synth.varlen_lengths(w["n_seqs"], w["total"], w["lo"], w["hi"])
+    H, D = w["Hq"], w["D"]
+    say(f"varlen bwd workload mode {mode}: {len(lens)} sequences, {sum(lens)} tokens, max {max(lens)}")
+    q, k, v, do, cu = synth.generate_varlen(lens, H, H, D, seed=0, with_dout=True)
+    scale = 1.0 / math.sqrt(D)
+    qd, kd, vd, dod, cud = q.to(dev), k.to(dev), v.to(dev), do.to(dev), cu.to(dev)
+    o, lse = fa.forward_varlen(qd, kd, vd, cud, max(lens), True, scale)
+    dq, dk, dv = (t.cpu() for t in fa.backward_varlen(qd, kd, vd, o, lse, dod, cud, max(lens), True,
+                                                      scale, deterministic=mode))
+    torch.cuda.synchronize()
+    got, ref = [], []
+    for b, n in enumerate(lens):
+        s0 = int(cu[b])
+        sl = slice(s0, s0 + n)
+        rows = [(0, h, i) for h in (0, H - 1) for i in sorted({0, n // 2, n - 1})]
+        ref.append(oracle.attention_bwd_dq_rows(q[None, :, sl], k[None, :, sl], v[None, :, sl],
+                                                do[None, :, sl], True, scale, rows))
+        got.append(torch.stack([dq[h, s0 + i] for (_, h, i) in rows]))
+    check_grad(torch.cat(got), torch.cat(ref), f"sampled dQ rows of all {len(lens)} sequences")
+    for b in (min(range(len(lens)), key=lambda i: lens[i]), max(range(len(lens)), key=lambda i: lens[i])):
+        s0, n = int(cu[b]), lens[b]
+        sl = slice(s0, s0 + n)
+        for h in (0, H - 1):
+            one = lambda t: t[None, h:h + 1, sl]
+            rq, rk, rv = oracle.attention_bwd(one(q), one(k), one(v), one(do), True, scale)
+            check_grad(one(dq), rq, f"seq {b} (len {n}) head {h} dQ")
+            check_grad(one(dk), rk, f"seq {b} head {h} dK")
+            check_grad(one(dv), rv, f"seq {b} head {h} dV")
