@@ -206,3 +206,25 @@ def test_sharp_softmax_scale(D, scale, deterministic):
     check_grad(dq.cpu(), rq, "dQ")
     check_grad(dk.cpu(), rk, "dK")
     check_grad(dv.cpu(), rv, "dV")
+
+
+def test_grouped_heads_headline_size():
+    # The benchmark's grouped-head workload, B2 Hq16 Hkv2 N8192 D128 causal,
+    # stored-dS mode: K/V head 1 of batch 1 (query heads 8..15) in full
+    # against the oracle, and dQ rows of every query head sampled one by one.
+    B, Hq, Hkv, N, D = 2, 16, 2, 8192, 128
+    say(f"bwd grouped heads B{B} Hq{Hq} Hkv{Hkv} N{N} D{D} causal, stored dS")
+    q, k, v, do = synth.generate(B, Hq, Hkv, N, D, seed=2, with_dout=True)
+    scale = 1.0 / math.sqrt(D)
+    [(dq, dk, dv)] = run_bwd(q, k, v, do, True, scale, 1)
+    G = Hq // Hkv
+    rq, rk, rv = oracle.attention_bwd(q[1:2, G:], k[1:2, 1:], v[1:2, 1:], do[1:2, G:], True, scale)
+    check_grad(dq[1:2, G:], rq, "dQ of query heads 8..15, batch 1")
+    check_grad(dk[1:2, 1:], rk, "dK of K/V head 1, batch 1")
+    check_grad(dv[1:2, 1:], rv, "dV of K/V head 1, batch 1")
+    g = torch.Generator().manual_seed(5)
+    rows = [(b, h, i) for b in range(B) for h in range(Hq)
+            for i in (0, N - 1, int(torch.randint(N, (1,), generator=g)))]
+    ref = oracle.attention_bwd_dq_rows(q, k, v, do, True, scale, rows)
+    got = torch.stack([dq[b, h, i] for (b, h, i) in rows])
+    check_grad(got, ref, f"sampled dQ rows ({len(rows)} over all heads)")
