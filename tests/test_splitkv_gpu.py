@@ -73,3 +73,23 @@ def test_split_count_does_not_change_the_result_beyond_rounding():
     for o, l in res:
         check_o(o, ro, "O")
         check_lse(l, rl, "LSE")
+
+
+def test_decode_workload_full():
+    # The benchmark's decode workload, B16 Hq32 Hkv1 Nq1 Nk32768 D128 causal,
+    # with the split count the library picks (as the benchmark runs it): every
+    # output row against the oracle.
+    dev = require_gpu()
+    B, Hq, Hkv, Nq, Nk, D = 16, 32, 1, 1, 32768, 128
+    splits = fa.fa_fwd_splitkv_num_splits(B, Hq, Hkv, Nq, Nk, D)
+    say(f"split-KV decode workload B{B} Hq{Hq} Hkv{Hkv} Nq{Nq} Nk{Nk} D{D}, {splits} key ranges")
+    g = torch.Generator().manual_seed(1)
+    q = torch.randn((B, Hq, Nq, D), generator=g).to(torch.bfloat16)
+    k = torch.randn((B, Hkv, Nk, D), generator=g).to(torch.bfloat16)
+    v = torch.randn((B, Hkv, Nk, D), generator=g).to(torch.bfloat16)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = fa.forward_splitkv(q.to(dev), k.to(dev), v.to(dev), True, scale, num_splits=splits)
+    torch.cuda.synchronize()
+    ro, rl = reference(q, k, v, True, scale)
+    check_o(o.cpu(), ro, "O")
+    check_lse(lse.cpu(), rl, "LSE")
