@@ -635,9 +635,10 @@ __global__ __launch_bounds__(256, 1) void bwd_atomic_kernel(
 //     the VALU forms P(i) = exp2(S c - LSE log2 e) and dS(i) = P (dP - Delta);
 //     P(i) and dS(i) go to LDS in MFMA operand order (and, stored mode, dS(i)
 //     to the workspace);
-//   gradient waves 4..7 (keys 32 (w - 4)): dV += P^T dO and dK += dS^T Q of
-//     step i-1, P and dS from that LDS copy, dO^T and Q^T by transposing reads
-//     of the step tile.
+//   gradient waves 4..7 (one 32-wide d-block each, over all 128 keys at
+//     D = 128, over half of them at D = 64): dV += P^T dO and dK += dS^T Q of
+//     step i-1, P and dS from the score waves' LDS slots, dO^T and Q^T by
+//     transposing reads of the step tile.
 // Waves are dealt to the 4 SIMDs round-robin, so waves w and w + 4 share one:
 // the exp2-heavy score stream and the MFMA-only gradient stream run side by
 // side, and each role needs about half the registers of the single-role
