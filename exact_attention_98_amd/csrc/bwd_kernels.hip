@@ -55,7 +55,7 @@ struct BwdParams {
   float* dq_acc;   // fp32 [B][Hq][N][D] (atomic mode)
   float* delta;    // fp32 [B][Hq][N]
   float* lse2;     // fp32 [B][Hq][N]
-  char* ds;        // dS^T blocks (stored-dS mode), ds_head bytes per (b, hq)
+  char* ds;        // dS^T blocks (stored-dS mode), ds_head bytes per (b, hq) (packed: per hq)
   uint32_t ds_head;
   // Stored-dS mode with packed sequences: sequence b's blocks start at block
   // blk_off[b] of each head's region (B + 1 entries, clamped to its size).
@@ -628,7 +628,7 @@ __global__ __launch_bounds__(256, 1) void bwd_atomic_kernel(
 
 // ---------------------------------------------------------------------------
 // Warp-specialized main backward kernel, D = 64 or 128 (dQ modes stored and
-// recompute; dense, or packed sequences in the recompute mode).  Same work item as bwd_atomic_kernel -- (batch, K/V head, 128-key
+// recompute; dense or packed sequences).  Same work item as bwd_atomic_kernel -- (batch, K/V head, 128-key
 // tile), every query step of every query head of the group -- with 8 waves in
 // two roles over the same step tiles:
 //   score waves 0..3 (keys 32 w): the MFMA unit forms S, dP of step i+1 while
