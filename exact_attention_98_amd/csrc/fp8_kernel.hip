@@ -19,10 +19,13 @@
 // Attention kernel: the pipelined structure of the bf16 forward with
 // v_mfma_scale_f32_32x32x64_f8f6f4 for S^T = K Q^T (k = 64 channels per
 // instruction) and O^T += V^T P^T (k = the 64 keys of a tile).  The Q and K
-// factors scale S in fp32; the V factor is the A-operand block scale.  P is
-// kept <= 1 by rescaling whenever a row maximum grows (tau = 0), then stored
-// as e4m3(256 P) with block scale 2^-8, so P down to 2^-14 stays a normal
-// e4m3 value.  The row sum l adds the fp32 P.
+// factors scale S in fp32; the V factor is the A-operand block scale.  The
+// rescale is the bf16 forward's lazy one (tau = 8, a rescale only when a row's
+// maximum grows by more than 2^8).  Each row's P of a tile is stored as
+// e4m3(2^k P), k the integer that puts the row's largest value of the tile in
+// (2^7, 2^8], with block scale 2^-k (the matrix instruction's per-lane scale
+// of the B operand), so every row uses the top of the e4m3 range whatever its
+// distance from the reference maximum.  The row sum l adds the fp32 P.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -300,10 +303,12 @@ __global__ __launch_bounds__(64 * f8_waves<D>(), 8 / f8_waves<D>()) void fwd_fp8
           if (32 * sb + 8 * (r >> 2) + (r & 3) > lim) sv[sb][r] = -__builtin_inff();
     }
   };
-  // Rescale whenever any row's maximum grows (tau = 0 keeps P <= 1, so 256 P
-  // fits e4m3).
-  auto rescale = [&](float m_new) {
-    if (__builtin_amdgcn_ballot_w64(m_new > m_ref) != 0) {
+  // Lazy rescale: taken by the whole wave when some row's tile maximum exceeds
+  // its reference by more than tau; each row then moves to the larger of the
+  // two.
+  auto rescale = [&](float m_tile) {
+    if (__builtin_amdgcn_ballot_w64(m_tile > m_ref + kTau) != 0) {
+      const float m_new = fmaxf(m_ref, m_tile);
       const float alpha = (m_new == -__builtin_inff()) ? 1.f : exp2_hw(m_ref - m_new);
       l_part *= alpha;
 #pragma unroll
@@ -315,15 +320,22 @@ __global__ __launch_bounds__(64 * f8_waves<D>(), 8 / f8_waves<D>()) void fwd_fp8
   };
 
   // Phase A(kt): S^T(kt+1) on the MFMA unit while the VALU forms
-  // e4m3(256 P(kt)) into pb; phase B(kt): O^T += V^T P^T(kt) with the row max
-  // of S^T(kt+1).  The row sum l_part accumulates 256 P (exact power-of-two
-  // scale, undone at the end), so 256 is folded into the exp2 argument.
+  // e4m3(2^k P(kt)) into pb (k in pbk, per row); phase B(kt): O^T += V^T P^T(kt)
+  // with the row max of S^T(kt+1).  2^k is folded into the exp2 argument; the
+  // tile's sum of 2^k P is scaled by 2^-k into the row sum.
   v8i pb;
+  int pbk = 0;
   auto phase_a = [&](int kt, const char* kn, f32x16 (&sv)[2], f32x16 (&sn)[2],
-                     float m_new) __attribute__((always_inline)) {
-    rescale(m_new);
-    const float msub8 = 8.f - ((m_ref == -__builtin_inff()) ? 0.f : m_ref);
+                     float m_tile) __attribute__((always_inline)) {
+    rescale(m_tile);
+    const float mu = (m_ref == -__builtin_inff()) ? 0.f : m_ref;
+    // m_tile - mu <= tau after the rescale, so k >= 0; a row with no key in
+    // the tile (m_tile = -inf) gets the cap, and its P are 0 anyway.
+    const float kf = fminf(floorf(8.f - (m_tile - mu)), 64.f);
+    const float xoff = kf - mu;
+    pbk = (int)kf;
     const float ct = cq * ksc[kt];
+    float ts = 0.f;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
@@ -343,37 +355,39 @@ __global__ __launch_bounds__(64 * f8_waves<D>(), 8 / f8_waves<D>()) void fwd_fp8
         float pv[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          pv[q] = exp2_hw(__builtin_fmaf(sv[esb][r + q], ct, msub8));
-          l_part += pv[q];
+          pv[q] = exp2_hw(__builtin_fmaf(sv[esb][r + q], ct, xoff));
+          ts += pv[q];
         }
         pb[e >> 2] = (int)cvt_fp8x4(pv[0], pv[1], pv[2], pv[3]);
       }
-      pin(l_part);
+      pin(ts);
       __builtin_amdgcn_sched_barrier(0);
     }
+    l_part = __builtin_fmaf(ts, __builtin_amdgcn_ldexpf(1.f, -pbk), l_part);
     mask(kt + 1, sn);
   };
   auto phase_b = [&](int kt, const char* vc, const f32x16 (&sn)[2],
-                     float& m_new) __attribute__((always_inline)) {
-    // V block scale 2^e, P block scale 2^-8.
+                     float& m_tile) __attribute__((always_inline)) {
+    // V block scale 2^e, P block scale 2^-k (per row: each lane's scale
+    // covers the 32 keys of P it holds).
     const int sa = 127 + vex[kt];
+    const int sbp = 127 - pbk;
     const float cn = cq * ksc[min(kt + 1, ntiles - 1)];
     float mx = -__builtin_inff();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int db = 0; db < ND; ++db) {
-      oacc[db] = mfma_f8(vread(vc, db), pb, oacc[db], sa, 127 - 8);
+      oacc[db] = mfma_f8(vread(vc, db), pb, oacc[db], sa, sbp);
 #pragma unroll
       for (int e = db * (32 / ND); e < (db + 1) * (32 / ND); ++e) mx = fmaxf(mx, sn[e >> 4][e & 15]);
       pin(mx);
       __builtin_amdgcn_sched_barrier(0);
     }
-    mx = xhalf_max(mx);
-    m_new = fmaxf(m_ref, mx * cn);
+    m_tile = xhalf_max(mx) * cn;
   };
 
   f32x16 sA[2], sB[2];
-  float m_new = -__builtin_inff();
+  float m_nxt = -__builtin_inff();  // row maximum of the next tile's S c (log2 units)
   if (ntiles > 0) {
     issue_k(0, kbuf0);
     issue_v(0, vbuf0);
@@ -393,7 +407,7 @@ __global__ __launch_bounds__(64 * f8_waves<D>(), 8 / f8_waves<D>()) void fwd_fp8
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sA[sb][r]);
-    m_new = fmaxf(m_ref, xhalf_max(mx) * cq * ksc[0]);
+    m_nxt = xhalf_max(mx) * cq * ksc[0];
   }
   // Tile kt between barrier kt and barrier kt+1: at barrier kt, K(kt+1) and
   // V(kt) are in LDS and the copies of K(kt+2), V(kt+1) are issued.  Leading
@@ -409,11 +423,11 @@ __global__ __launch_bounds__(64 * f8_waves<D>(), 8 / f8_waves<D>()) void fwd_fp8
       if (kt + 2 < ntiles) issue_k(kt + 2, kld);
       if (kt + 1 < ntiles) issue_v(kt + 1, vld);
       if constexpr (LAG) {
-        if (kt > 0) phase_b(kt - 1, vp, sv, m_new);
-        phase_a(kt, kn, sv, sn, m_new);
+        if (kt > 0) phase_b(kt - 1, vp, sv, m_nxt);
+        phase_a(kt, kn, sv, sn, m_nxt);
       } else {
-        phase_a(kt, kn, sv, sn, m_new);
-        phase_b(kt, vc, sn, m_new);
+        phase_a(kt, kn, sv, sn, m_nxt);
+        phase_b(kt, vc, sn, m_nxt);
       }
     };
     // K(j) in kbuf[j % 2], V(j) in vbuf[j % 4] (vbuf2, vbuf3 alias vbuf0,
@@ -432,7 +446,7 @@ __global__ __launch_bounds__(64 * f8_waves<D>(), 8 / f8_waves<D>()) void fwd_fp8
     if constexpr (LAG) {
       if (ntiles > 0) {
         const int r = (ntiles - 1) & 3;
-        phase_b(ntiles - 1, r == 0 ? vbuf0 : r == 1 ? vbuf1 : r == 2 ? vbuf2 : vbuf3, sA, m_new);
+        phase_b(ntiles - 1, r == 0 ? vbuf0 : r == 1 ? vbuf1 : r == 2 ? vbuf2 : vbuf3, sA, m_nxt);
       }
     }
   };
@@ -441,9 +455,9 @@ __global__ __launch_bounds__(64 * f8_waves<D>(), 8 / f8_waves<D>()) void fwd_fp8
   else
     run(Flag<false>{});
 
-  // O = O / l (bf16), LSE = (m_ref + log2 l) ln 2, with l = l_part / 256.
+  // O = O / l (bf16), LSE = (m_ref + log2 l) ln 2.
   const float l_tot = xhalf_sum(l_part);
-  const float inv = 256.f / l_tot;
+  const float inv = 1.f / l_tot;
   const uint32_t head_bytes = (uint32_t)((size_t)N * D * 2);
   const rsrc_t orr = make_rsrc_uniform(O + (size_t)bh * N * D, head_bytes);
 #pragma unroll
@@ -455,7 +469,7 @@ __global__ __launch_bounds__(64 * f8_waves<D>(), 8 / f8_waves<D>()) void fwd_fp8
       w[1] = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
       buf_store8(orr, (uint32_t)(qi * D * 2 + (32 * db + 8 * g + 4 * h) * 2), w);
     }
-  if (h == 0 && qi < N) LSE[(size_t)bh * N + qi] = (m_ref + __builtin_amdgcn_logf(l_tot) - 8.f) * kLn2;
+  if (h == 0 && qi < N) LSE[(size_t)bh * N + qi] = (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2;
 }
 
 template <int D, bool CAUSAL>
