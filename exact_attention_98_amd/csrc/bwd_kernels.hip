@@ -635,10 +635,10 @@ __global__ __launch_bounds__(256, 1) void bwd_atomic_kernel(
 //     the VALU forms P(i) = exp2(S c - LSE log2 e) and dS(i) = P (dP - Delta);
 //     P(i) and dS(i) go to LDS in MFMA operand order (and, stored mode, dS(i)
 //     to the workspace);
-//   gradient waves 4..7 (one 32-wide d-block each, over all 128 keys at
-//     D = 128, over half of them at D = 64): dV += P^T dO and dK += dS^T Q of
-//     step i-1, P and dS from the score waves' LDS slots, dO^T and Q^T by
-//     transposing reads of the step tile.
+//   gradient waves 4..7 (one product each over all 128 keys, half of the d
+//     range: waves 4, 5 dV += P^T dO, waves 6, 7 dK += dS^T Q) of step i-1,
+//     P and dS from the score waves' LDS slots, dO^T and Q^T by transposing
+//     reads of the step tile.
 // Waves are dealt to the 4 SIMDs round-robin, so waves w and w + 4 share one:
 // the exp2-heavy score stream and the MFMA-only gradient stream run side by
 // side, and each role needs about half the registers of the single-role
@@ -1001,57 +1001,63 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
     }
   } else {
     // ======================= gradient waves =======================
-    // Gradient wave g takes d-block db = g % ND of the keys of score waves
-    // kbw0 .. kbw0 + ND - 1 (kbw0 = (g / ND) ND): all 128 keys at D = 128,
-    // one half of them at D = 64.  Each transposing read of dO^T or Q^T then
-    // feeds ND products (one per key block) instead of one; the A operands
-    // P^T and dS^T are plain 16-byte reads of the score waves' slots.
-    // Accumulator j covers keys kw_j = k0 + 32 (kbw0 + j), d = 32 db + n.
-    const int gdb = kwave % ND;
-    const int kbw0 = (kwave / ND) * ND;
-    f32x16 dk_acc[ND], dv_acc[ND];
+    // Gradient wave g computes one product over all 128 keys: waves 4, 5 dV
+    // += P^T dO, waves 6, 7 dK += dS^T Q, each for ND / 2 of the 32-wide d
+    // blocks (d-blocks db0 .. db0 + ND/2 - 1, db0 = (g & 1) ND / 2).  Per
+    // 16-query k-step the wave reads the four key blocks' A operands (plain
+    // 16-byte reads of the score waves' slots) and, by transposing reads of
+    // the step tile, one B operand per d-block, each A read feeding ND / 2
+    // products and each B read four.  Accumulator [e][j] covers keys
+    // k0 + 32 j + 8(r/4) + 4h + r%4 of register r, d = 32 (db0 + e) + n.
+    constexpr int NDW = ND / 2;
+    const bool gk = kwave >= 2;  // dK (dS^T Q) rather than dV (P^T dO)
+    const int db0 = (kwave & 1) * NDW;
+    f32x16 acc[NDW][4];
 #pragma unroll
-    for (int i = 0; i < ND; ++i)
+    for (int e = 0; e < NDW; ++e)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        dk_acc[i][r] = 0.f;
-        dv_acc[i][r] = 0.f;
-      }
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[e][j][r] = 0.f;
     // Transposing B-operand reads of dO / Q (queries 16 u + 8 rd + 4 h + 0..3
     // of column d = 32 db + n): lane j of 16-lane group gq points at row
     // 8 rd + 4 h + j/4 and d = 32 db + 16 (gq & 1) + 4 (j & 3).
     const int tj = lane & 15, gq = lane >> 4;
-    uint32_t tr_off[2];
+    uint32_t tr_off[NDW][2];
 #pragma unroll
-    for (int rd = 0; rd < 2; ++rd) {
-      const int row = 8 * rd + 4 * h + (tj >> 2);
-      const int c = 4 * gdb + 2 * (gq & 1) + ((tj & 3) >> 1);
-      tr_off[rd] = (uint32_t)(row * RB + ((c ^ tile_swz<D>(row)) * 16) + (tj & 1) * 8);
-    }
-    // Iteration i: dV, dK of step i-1 (tile `prv`, P and dS in `pbr`).
+    for (int e = 0; e < NDW; ++e)
+#pragma unroll
+      for (int rd = 0; rd < 2; ++rd) {
+        const int row = 8 * rd + 4 * h + (tj >> 2);
+        const int c = 4 * (db0 + e) + 2 * (gq & 1) + ((tj & 3) >> 1);
+        tr_off[e][rd] = (uint32_t)(row * RB + ((c ^ tile_swz<D>(row)) * 16) + (tj & 1) * 8);
+      }
+    const int tile_off = gk ? 0 : TB;      // Q or dO half of the step tile
+    const int slot_off = gk ? 2048 : 0;    // dS or P half of each score wave's slot
+    // Iteration i: the product of step i-1 (tile `prv`, P and dS in `pbr`).
     auto body = [&](int i, const char* prv, const char* pbr, char* ld) __attribute__((always_inline)) {
       wait_step(i);
       lds_barrier();
       if (i + 4 < nsteps) issue_next(ld);
       if (i == 0 || i > nsteps) return;
-      const char* pr = pbr + kbw0 * 4096 + lane * 16;
-      constexpr int NB = 2 * ND;  // MFMA pairs: (u, key block j), j fastest
+      const char* pr = pbr + slot_off + lane * 16;
+      const char* tile = prv + tile_off;
+      constexpr int NB = 2 * 4;  // (u, key block j), j fastest
       constexpr int PD = 2;
-      bf16x8 pa[NB], dsa[NB], ob[2], qb[2];
+      bf16x8 pa[NB], ob[2][NDW];
       auto fetch = [&](int jb) {
         if (jb < NB) {
-          const int u = jb / ND, j = jb % ND;
+          const int u = jb / 4, j = jb % 4;
           if (j == 0) {
             const int roff = 16 * u * RB;
-            const u32x2 olo = lds_read_tr16((const lds_void*)(prv + TB + roff + tr_off[0]));
-            const u32x2 ohi = lds_read_tr16((const lds_void*)(prv + TB + roff + tr_off[1]));
-            const u32x2 qlo = lds_read_tr16((const lds_void*)(prv + roff + tr_off[0]));
-            const u32x2 qhi = lds_read_tr16((const lds_void*)(prv + roff + tr_off[1]));
-            ob[u] = as_bf16x8(u32x4{olo[0], olo[1], ohi[0], ohi[1]});
-            qb[u] = as_bf16x8(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]});
+#pragma unroll
+            for (int e = 0; e < NDW; ++e) {
+              const u32x2 lo = lds_read_tr16((const lds_void*)(tile + roff + tr_off[e][0]));
+              const u32x2 hi = lds_read_tr16((const lds_void*)(tile + roff + tr_off[e][1]));
+              ob[u][e] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+            }
           }
           pa[jb] = as_bf16x8(*(const u32x4*)(pr + j * 4096 + u * 1024));
-          dsa[jb] = as_bf16x8(*(const u32x4*)(pr + j * 4096 + (2 + u) * 1024));
         }
       };
 #pragma unroll
@@ -1059,10 +1065,10 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int jb = 0; jb < NB; ++jb) {
-        const int u = jb / ND, j = jb % ND;
+        const int u = jb / 4, j = jb % 4;
         fetch(jb + PD);
-        dv_acc[j] = mfma32(pa[jb], ob[u], dv_acc[j]);
-        dk_acc[j] = mfma32(dsa[jb], qb[u], dk_acc[j]);
+#pragma unroll
+        for (int e = 0; e < NDW; ++e) acc[e][j] = mfma32(pa[jb], ob[u][e], acc[e][j]);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
@@ -1076,39 +1082,38 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
       body(i + 4, st3, pb1, st2);
       body(i + 5, st4, pb0, st3);
     }
-    // dK (scaled) and dV: register r of accumulator j holds key
-    // k0 + 32 (kbw0 + j) + 8(r/4) + 4h + r%4, d = 32 gdb + n.  With the query
-    // heads cut into parts, each part writes fp32 partials that
-    // bwd_kv_reduce_kernel sums in part order.
+    // dK (scaled) or dV, through a buffer range that starts at the tile's
+    // first key and ends at the sequence's last, so stores of padding keys are
+    // dropped.  With the query heads cut into parts, each part writes fp32
+    // partials that bwd_kv_reduce_kernel sums in part order.
+    const float osc = gk ? p.scale : 1.f;
+    const uint32_t rows = (uint32_t)min(N - k0, BN);
     if (!VARLEN && p.hsplit > 1) {
       const size_t plane = (size_t)BHkv * N * D;
-      float* pk = p.kv_part + (size_t)hs * 2 * plane + (size_t)bhk * N * D;
-      float* pv = pk + plane;
+      const float* po = p.kv_part + (size_t)hs * 2 * plane + (gk ? 0 : plane) + ((size_t)bhk * N + k0) * D;
+      const rsrc_t orr = make_rsrc_uniform(po, rows * (uint32_t)(D * 4));
 #pragma unroll
-      for (int j = 0; j < ND; ++j)
+      for (int e = 0; e < NDW; ++e)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int krow = k0 + 32 * (kbw0 + j) + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (krow < N) {
-            const size_t off = (size_t)krow * D + 32 * gdb + n;
-            pk[off] = dk_acc[j][r] * p.scale;
-            pv[off] = dv_acc[j][r];
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = 32 * j + 8 * (r >> 2) + 4 * h + (r & 3);
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, acc[e][j][r] * osc), orr,
+                                                  (uint32_t)((row * D + 32 * (db0 + e) + n) * 4), 0, 0);
           }
-        }
     } else {
-      uint16_t* dKh = dK + kv_head;
-      uint16_t* dVh = dV + kv_head;
+      const rsrc_t orr = make_rsrc_uniform((gk ? dK : dV) + kv_head + (size_t)k0 * D, rows * (uint32_t)RB);
 #pragma unroll
-      for (int j = 0; j < ND; ++j)
+      for (int e = 0; e < NDW; ++e)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int krow = k0 + 32 * (kbw0 + j) + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (krow < N) {
-            const size_t off = (size_t)krow * D + 32 * gdb + n;
-            dKh[off] = (uint16_t)(pack_bf16x2(dk_acc[j][r] * p.scale, 0.f) & 0xffffu);
-            dVh[off] = (uint16_t)(pack_bf16x2(dv_acc[j][r], 0.f) & 0xffffu);
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = 32 * j + 8 * (r >> 2) + 4 * h + (r & 3);
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pack_bf16x2(acc[e][j][r] * osc, 0.f) & 0xffffu), orr,
+                                                  (uint32_t)((row * D + 32 * (db0 + e) + n) * 2), 0, 0);
           }
-        }
     }
   }
 }
