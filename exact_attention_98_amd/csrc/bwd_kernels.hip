@@ -1043,7 +1043,9 @@ __global__ __launch_bounds__(512, 1) void bwd_ws_kernel(
       const char* pr = pbr + slot_off + lane * 16;
       const char* tile = prv + tile_off;
       constexpr int NB = 2 * 4;  // (u, key block j), j fastest
-      constexpr int PD = 2;
+      // Operands are read PD key blocks ahead of their products (3 measured
+      // 0.2-0.9% faster than 2).
+      constexpr int PD = 3;
       bf16x8 pa[NB], ob[2][NDW];
       auto fetch = [&](int jb) {
         if (jb < NB) {
