@@ -278,19 +278,35 @@ __global__ __launch_bounds__(256, 1) void bwd_atomic_kernel(
       tr_off[db][rd] = (uint32_t)(row * RB + ((c ^ tile_swz<D>(row)) * 16) + (tj & 1) * 8);
     }
   }
-  // dS^T [key][query] (rows of DSRB bytes).  Chunk swizzle for 4 consecutive
-  // rows read at two adjacent chunks: fd(r) keeps those 8 chunks on distinct
-  // banks for both 64-byte and 128-byte rows.
-  auto fd = [](int r) { return QS == 32 ? (((r >> 1) & 1) << 1) : (((r & 3) << 1) | ((r >> 2) & 1)); };
+  // dS^T [key][query] (rows of DSRB bytes): 16-byte chunk c of row r sits at
+  // chunk c ^ fd(r), its two 8-byte halves swapped when fh(r) = 1.  Both
+  // are XORs of row bits chosen so that the writer (16 or 32 consecutive
+  // rows, one 8-byte half each) and the transposing reader (4 consecutive
+  // rows, 2 or 4 chunks each) touch every bank equally, whether the LDS
+  // serves 16 or 32 lanes at a time from 32 or 64 banks: the writer's row
+  // bits map one to one onto the 8-byte positions of each 128- or 256-byte
+  // bank window, and rows sharing a window on the reader's side get
+  // disjoint chunk groups.
+  auto fd = [](int r) {
+    return QS == 32 ? (((((r >> 1) ^ (r >> 3)) & 1) << 1) | ((r >> 2) & 1))
+                    : ((((r >> 1) & 1) << 2) | (((r ^ (r >> 2)) & 1) << 1) | ((r >> 3) & 1));
+  };
+  auto fh = [](int r) { return QS == 32 ? (((r >> 3) ^ (r >> 4)) & 1) : (((r >> 2) ^ (r >> 4)) & 1); };
   // Writer: lane (key 32 wave + n) stores 4 consecutive queries 32 qb + 8 g + 4 h.
   // Reader (A operand of dQ): lane j of group gq points at key row
-  // 16 t + 8 rd + 4 h + j/4 and query 32 dq_qb + 16 (gq & 1) + 4 (j & 3).
-  uint32_t dsr_off;
-  {
-    const int row = 4 * h + (tj >> 2);
-    const int col = 32 * dq_qb + 16 * (gq & 1) + 4 * (tj & 3);
-    dsr_off = (uint32_t)(row * DSRB + (((col >> 3) ^ fd(row)) * 16) + ((col >> 2) & 1) * 8);
-  }
+  // 16 t + 8 rd + 4 h + j/4 and query 32 dq_qb + 16 (gq & 1) + 4 (j & 3);
+  // the swizzle depends on the row's bits 3 and 4, so the offsets are kept
+  // per (t & 1, rd).
+  uint32_t dsr_off[2][2];
+#pragma unroll
+  for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) {
+      const int row = 16 * tp + 8 * rd + 4 * h + (tj >> 2);
+      const int col = 32 * dq_qb + 16 * (gq & 1) + 4 * (tj & 3);
+      dsr_off[tp][rd] =
+          (uint32_t)(row * DSRB + (((col >> 3) ^ fd(row)) * 16) + ((((col >> 2) & 1) ^ fh(row)) * 8));
+    }
   const int ds_wrow = 32 * wave + n;
 
   // ---- step schedule -------------------------------------------------------
@@ -362,9 +378,9 @@ __global__ __launch_bounds__(256, 1) void bwd_atomic_kernel(
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
     for (int t = 0; t < BN / 16; ++t) {
-      const char* base = dsb + (16 * t) * DSRB + dsr_off;
-      const u32x2 lo = lds_read_tr16((const lds_void*)base);
-      const u32x2 hi = lds_read_tr16((const lds_void*)(base + 8 * DSRB));
+      const char* base = dsb + (16 * (t & ~1)) * DSRB;
+      const u32x2 lo = lds_read_tr16((const lds_void*)(base + dsr_off[t & 1][0]));
+      const u32x2 hi = lds_read_tr16((const lds_void*)(base + dsr_off[t & 1][1]));
       const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
       acc = mfma32(as_bf16x8(a), kT[t], acc);
     }
@@ -555,7 +571,8 @@ __global__ __launch_bounds__(256, 1) void bwd_atomic_kernel(
           u32x2 w;
           w[0] = dsw4[(g4 & 1) * 2];
           w[1] = dsw4[(g4 & 1) * 2 + 1];
-          *(u32x2*)(dsw + ds_wrow * DSRB + (((col >> 3) ^ fd(ds_wrow)) * 16) + ((col >> 2) & 1) * 8) = w;
+          *(u32x2*)(dsw + ds_wrow * DSRB + (((col >> 3) ^ fd(ds_wrow)) * 16) +
+                    ((((col >> 2) & 1) ^ fh(ds_wrow)) * 8)) = w;
         }
       }
       __builtin_amdgcn_sched_barrier(0);
